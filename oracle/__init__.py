@@ -1,0 +1,239 @@
+"""fp64 CPU reference ("oracle") for the selective state-space scan (S6).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The GPU library never imports, links or calls it,
+and the two share no code.
+
+The arithmetic lives in ``ss_oracle.c`` (plain C, IEEE double, sequential in time); this module
+only builds it with gcc and marshals numpy arrays into it.  ``numpy_twin`` holds an independent
+pure-numpy transcription used on tiny inputs to cross-check the C build.
+
+Sources: the Mamba reading guide (xyznot.com), sections "Método" and "O Mecanismo de Seleção
+(S6)"; the IBM explainer "O que é um modelo Mamba?" (state/output equations, Mamba block); the
+aivaro.ru answer "Как работает Mamba", section 3 "Selective Scan".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ss_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libss_oracle.so")
+
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ss_oracle.c into libss_oracle.so next to it (gcc, -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", "-Werror",
+             "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def use_library(path):
+    """Point this module at another build of ss_oracle.c (used by the mutation tests, which
+    compile deliberately broken copies and check that the pins catch them).  Returns the previous
+    handle so that it can be restored with restore_library()."""
+    global _lib
+    prev = _lib
+    _lib = _bind(ctypes.CDLL(path))
+    return prev
+
+
+def restore_library(prev):
+    global _lib
+    _lib = prev
+
+
+def _bind(lib):
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.oracle_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                    i64, i64, i64, i64, vp, i64, vp, vp, i32]
+    lib.oracle_scan_fwd.restype = i32
+    lib.oracle_scan_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+                                            i64, i64, i64, i64, i64, vp, vp]
+    lib.oracle_scan_fwd_chunked.restype = i32
+    lib.oracle_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                        i64, i64, i64, vp, i64, vp, i32]
+    lib.oracle_state_update.restype = i32
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _io(x, name):
+    """Accept float32 arrays, or bf16 given as raw uint16 bit patterns."""
+    if x is None:
+        return None, None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16:
+        return x, BF16
+    raise TypeError(f"{name}: expected float32 or uint16 (bf16 bits), got {x.dtype}")
+
+
+def _f32(x, shape, name):
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.shape != shape:
+        raise ValueError(f"{name}: shape {x.shape}, expected {shape}")
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data
+
+
+def _check_io(arrs, shapes, dtype_ref):
+    for (name, a), shp in zip(arrs, shapes):
+        if a is None:
+            continue
+        if a.shape != shp:
+            raise ValueError(f"{name}: shape {a.shape}, expected {shp}")
+        if (a.dtype == np.uint16) != (dtype_ref == BF16):
+            raise TypeError(f"{name}: io dtype differs from u's")
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, zoh_exact=False, rows=None, nthreads=None):
+    """Sequential fp64 prefill.
+
+    u, delta, z: (batch, L, d_inner); B, C: (batch, L, d_state) -- float32, or uint16 holding
+    bf16 bits (all five in the same io dtype).  A: (d_inner, d_state); D, delta_bias: (d_inner,).
+    h0: (batch, d_inner, d_state) float64 or None.  rows: optional 1-D array of row ids
+    b*d_inner + d.
+
+    Returns (out, h_last): without rows, out is (batch, L, d_inner) and h_last is
+    (batch, d_inner, d_state); with rows, out is (len(rows), L) and h_last (len(rows), d_state).
+    """
+    u, dt = _io(u, "u")
+    delta, _ = _io(delta, "delta")
+    B, _ = _io(B, "B")
+    C, _ = _io(C, "C")
+    z, _ = _io(z, "z")
+    batch, L, d_inner = u.shape
+    d_state = B.shape[2]
+    _check_io([("delta", delta), ("z", z), ("B", B), ("C", C)],
+              [(batch, L, d_inner), (batch, L, d_inner), (batch, L, d_state),
+               (batch, L, d_state)], dt)
+    A = _f32(A, (d_inner, d_state), "A")
+    D = _f32(D, (d_inner,), "D")
+    delta_bias = _f32(delta_bias, (d_inner,), "delta_bias")
+    if h0 is not None:
+        h0 = np.ascontiguousarray(h0, dtype=np.float64).reshape(batch, d_inner, d_state)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows.shape[0]
+    else:
+        nrows = batch * d_inner
+    out = np.empty((nrows, L), dtype=np.float64)
+    h_last = np.empty((nrows, d_state), dtype=np.float64)
+    if nthreads is None:
+        nthreads = max(1, len(os.sched_getaffinity(0)))
+    rc = _load().oracle_scan_fwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt,
+        batch, L, d_inner, d_state, _ptr(rows), nrows, _ptr(out), _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_scan_fwd rejected its arguments")
+    if rows is None:
+        out = out.reshape(batch, d_inner, L).transpose(0, 2, 1)
+        h_last = h_last.reshape(batch, d_inner, d_state)
+    return out, h_last
+
+
+def scan_fwd_chunked(u, delta, A, B, C, chunk, D=None, z=None, delta_bias=None,
+                     delta_softplus=True, h0=None, zoh_exact=False):
+    """Same result as scan_fwd via the blockwise associative decomposition (block = chunk)."""
+    u, dt = _io(u, "u")
+    delta, _ = _io(delta, "delta")
+    B, _ = _io(B, "B")
+    C, _ = _io(C, "C")
+    z, _ = _io(z, "z")
+    batch, L, d_inner = u.shape
+    d_state = B.shape[2]
+    _check_io([("delta", delta), ("z", z), ("B", B), ("C", C)],
+              [(batch, L, d_inner), (batch, L, d_inner), (batch, L, d_state),
+               (batch, L, d_state)], dt)
+    A = _f32(A, (d_inner, d_state), "A")
+    D = _f32(D, (d_inner,), "D")
+    delta_bias = _f32(delta_bias, (d_inner,), "delta_bias")
+    if h0 is not None:
+        h0 = np.ascontiguousarray(h0, dtype=np.float64).reshape(batch, d_inner, d_state)
+    out = np.empty((batch * d_inner, L), dtype=np.float64)
+    h_last = np.empty((batch * d_inner, d_state), dtype=np.float64)
+    rc = _load().oracle_scan_fwd_chunked(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt,
+        batch, L, d_inner, d_state, int(chunk), _ptr(out), _ptr(h_last))
+    if rc != 0:
+        raise ValueError("oracle_scan_fwd_chunked rejected its arguments")
+    return (out.reshape(batch, d_inner, L).transpose(0, 2, 1),
+            h_last.reshape(batch, d_inner, d_state))
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=True, zoh_exact=False, rows=None, nthreads=None):
+    """One fp64 decode step.  state: (batch, d_inner, d_state) float64, updated IN PLACE (only
+    the selected rows when rows is given).  u, delta, z: (batch, d_inner); B, C:
+    (batch, d_state).  Returns out: (batch, d_inner), or (len(rows),) with rows."""
+    if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+            and state.flags.c_contiguous):
+        raise TypeError("state must be a C-contiguous float64 array (updated in place)")
+    u, dt = _io(u, "u")
+    delta, _ = _io(delta, "delta")
+    B, _ = _io(B, "B")
+    C, _ = _io(C, "C")
+    z, _ = _io(z, "z")
+    batch, d_inner = u.shape
+    d_state = B.shape[1]
+    if state.shape != (batch, d_inner, d_state):
+        raise ValueError(f"state: shape {state.shape}, expected {(batch, d_inner, d_state)}")
+    _check_io([("delta", delta), ("z", z), ("B", B), ("C", C)],
+              [(batch, d_inner), (batch, d_inner), (batch, d_state), (batch, d_state)], dt)
+    A = _f32(A, (d_inner, d_state), "A")
+    D = _f32(D, (d_inner,), "D")
+    delta_bias = _f32(delta_bias, (d_inner,), "delta_bias")
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows.shape[0]
+    else:
+        nrows = batch * d_inner
+    out = np.empty((nrows,), dtype=np.float64)
+    if nthreads is None:
+        nthreads = max(1, len(os.sched_getaffinity(0)))
+    rc = _load().oracle_state_update(
+        _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh_exact)), dt,
+        batch, d_inner, d_state, _ptr(rows), nrows, _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_state_update rejected its arguments")
+    return out.reshape(batch, d_inner) if rows is None else out

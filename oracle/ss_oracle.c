@@ -1,0 +1,233 @@
+/*
+ * ss_oracle.c -- fp64 CPU reference ("oracle") for the selective state-space scan (S6).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct definition that the GPU
+ * library is checked against.  Only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark load it.  The GPU library neither links nor calls it, and it shares no code,
+ * header, table or helper with the GPU library.
+ *
+ * Sources (web pages; section names as printed on each page):
+ *   [P1] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces" reading guide
+ *        (xyznot.com), sections "Método", "O Mecanismo de Seleção (S6)",
+ *        "Expansão de Estado Ciente de Hardware", "Perguntas".
+ *   [P2] "O que é um modelo Mamba?" (ibm.com), the state and output equations, the
+ *        discretisation paragraphs and the Mamba-block walk-through.
+ *   [P5] "Как работает Mamba (State Space Model) и чем она лучше трансформера?" (aivaro.ru),
+ *        section 3 "Selective Scan" and its simplified selective_scan sketch.
+ *
+ * What is computed, for every independent row (b, d) of the (batch, d_inner) grid:
+ *   s_t     = delta[b,t,d] + delta_bias[d]                     [P1 S6: tau(Parameter + s(x))]
+ *   dt_t    = softplus(s_t)  (or s_t when softplus is off)     [P1 S6; P5 section 3]
+ *   Abar    = exp(dt_t * A[d,n])                               [P1 Method: ZOH Abar = exp(dA)]
+ *   Bbar    = dt_t * B[b,t,n]                                  [P5 sketch: B_bar = delta * B]
+ *             or, with zoh_exact, (exp(dt A) - 1)/A * B        [P1 Method: exact ZOH Bbar]
+ *   h_t[n]  = Abar * h_{t-1}[n] + Bbar * u[b,t,d]              [P1 Method recurrence]
+ *   y_t     = sum_n C[b,t,n] h_t[n] + D[d] u[b,t,d]            [P1 Method y_t = C h_t; P2 output
+ *                                                               equation with D; P5 D*u skip]
+ *   out     = y_t * silu(z[b,t,d]) when z is given             [P2 Mamba block: SSM output
+ *                                                               multiplied by the activated gate]
+ * with h_{-1} = h0 (zeros when absent, as in the P5 sketch).  The state is diagonal: each
+ * channel d carries its own N-vector, and A is stored (d_inner, d_state) [P2: diagonal A].
+ * B and C have shape (batch, seqlen, d_state) and are shared by all channels [P1 S6; P5].
+ *
+ * Everything is evaluated in IEEE double with libm exp/log1p/expm1, sequentially in t.  Inputs
+ * are read exactly: fp32 as is, bf16 by placing its 16 bits in the top half of a float.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC ss_oracle.c -lm   (no -ffast-math).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+
+/* Read element i of an io-dtype array exactly (bf16 -> fp32 is a 16-bit shift). */
+static double rd(const void* p, int64_t i, int dtype) {
+  if (dtype == OR_BF16) {
+    uint32_t bits = ((uint32_t)((const uint16_t*)p)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)p)[i];
+}
+
+/* softplus(s) = log(1 + e^s), written without overflow or cancellation [P1 S6, tau = softplus]. */
+static double softplus(double s) { return (s > 0.0 ? s : 0.0) + log1p(exp(-fabs(s))); }
+
+/* silu(z) = z * sigmoid(z) [P2 Mamba block: the gate's activation; SiLU is the one the block uses]. */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Step size dt for one (b, t, d) element [P1 S6]. */
+static double step_size(double raw, const float* delta_bias, int64_t d, int delta_softplus) {
+  double s = raw + (delta_bias ? (double)delta_bias[d] : 0.0);
+  return delta_softplus ? softplus(s) : s;
+}
+
+/* Input coefficient Bbar / B for one state: dt (first-order form, [P5 sketch]) or the exact ZOH
+ * factor (exp(dt a) - 1) / a, which tends to dt as a -> 0 [P1 Method]. */
+static double bbar_factor(double dt, double a, int zoh_exact) {
+  if (!zoh_exact) return dt;
+  if (a == 0.0) return dt;
+  return expm1(dt * a) / a;
+}
+
+/*
+ * Whole-sequence prefill, sequential in t (RNN mode [P1 Method; P2 discretised recurrence]).
+ *
+ * Layouts (row-major, contiguous):
+ *   u, delta, z : (batch, seqlen, d_inner)   io dtype
+ *   B, C        : (batch, seqlen, d_state)   io dtype
+ *   A           : (d_inner, d_state) f32;  D, delta_bias : (d_inner) f32, NULL = 0
+ *   h0          : (batch, d_inner, d_state) f64, NULL = zeros
+ *   rows        : row ids r = b*d_inner + d to evaluate; NULL = all rows in order
+ *   out         : (nrows, seqlen) f64, out[i*seqlen + t] for rows[i]
+ *   h_last      : (nrows, d_state) f64 or NULL
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int delta_softplus, const double* h0, int zoh_exact, int io_dtype,
+                    int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                    const int64_t* rows, int64_t nrows, double* out, double* h_last,
+                    int nthreads) {
+  if (!u || !delta || !A || !B || !C || !out) return -1;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > 256) return -1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  if (!rows) nrows = batch * d_inner;
+  if (nthreads < 1) nthreads = 1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t r = rows ? rows[i] : i;
+    if (r < 0 || r >= batch * d_inner) { bad = 1; continue; }
+    int64_t b = r / d_inner, d = r % d_inner;
+    double h[256];
+    for (int64_t n = 0; n < d_state; ++n) h[n] = h0 ? h0[r * d_state + n] : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      int64_t e = (b * seqlen + t) * d_inner + d;      /* (b, t, d) element */
+      int64_t bc = (b * seqlen + t) * d_state;         /* (b, t, 0) of B and C */
+      double x = rd(u, e, io_dtype);
+      double dt = step_size(rd(delta, e, io_dtype), delta_bias, d, delta_softplus);
+      double y = 0.0;
+      for (int64_t n = 0; n < d_state; ++n) {
+        double a = (double)A[d * d_state + n];
+        double abar = exp(dt * a);
+        double bbar = bbar_factor(dt, a, zoh_exact) * rd(B, bc + n, io_dtype);
+        h[n] = abar * h[n] + bbar * x;
+        y += rd(C, bc + n, io_dtype) * h[n];
+      }
+      if (D) y += (double)D[d] * x;
+      if (z) y *= silu(rd(z, e, io_dtype));
+      out[i * seqlen + t] = y;
+    }
+    if (h_last)
+      for (int64_t n = 0; n < d_state; ++n) h_last[i * d_state + n] = h[n];
+  }
+  return bad ? -1 : 0;
+}
+
+/*
+ * The same prefill through the associative decomposition over time blocks of `chunk` steps
+ * [P1 "Parallel Associative Scan"; P2: the recurrence split into small independent blocks that
+ * are combined hierarchically].  Inside a block each state is run from zero while the running
+ * product of Abar is kept; the true state is then
+ *     h_t = hloc_t + (prod_{s<=t in block} Abar_s) * h_in,
+ * and h_in for the next block is the true state at the block's end.  Arguments and layouts are
+ * those of oracle_scan_fwd.  Used to pin that decomposition against the sequential form.
+ */
+int oracle_scan_fwd_chunked(const void* u, const void* delta, const float* A, const void* B,
+                            const void* C, const float* D, const void* z,
+                            const float* delta_bias, int delta_softplus, const double* h0,
+                            int zoh_exact, int io_dtype, int64_t batch, int64_t seqlen,
+                            int64_t d_inner, int64_t d_state, int64_t chunk, double* out,
+                            double* h_last) {
+  if (!u || !delta || !A || !B || !C || !out) return -1;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > 256 || chunk < 1)
+    return -1;
+  for (int64_t r = 0; r < batch * d_inner; ++r) {
+    int64_t b = r / d_inner, d = r % d_inner;
+    double h_in[256], hloc[256], prod[256];
+    for (int64_t n = 0; n < d_state; ++n) h_in[n] = h0 ? h0[r * d_state + n] : 0.0;
+    for (int64_t t0 = 0; t0 < seqlen; t0 += chunk) {
+      int64_t t1 = t0 + chunk < seqlen ? t0 + chunk : seqlen;
+      for (int64_t n = 0; n < d_state; ++n) { hloc[n] = 0.0; prod[n] = 1.0; }
+      for (int64_t t = t0; t < t1; ++t) {
+        int64_t e = (b * seqlen + t) * d_inner + d;
+        int64_t bc = (b * seqlen + t) * d_state;
+        double x = rd(u, e, io_dtype);
+        double dt = step_size(rd(delta, e, io_dtype), delta_bias, d, delta_softplus);
+        double y = 0.0;
+        for (int64_t n = 0; n < d_state; ++n) {
+          double a = (double)A[d * d_state + n];
+          double abar = exp(dt * a);
+          hloc[n] = abar * hloc[n] + bbar_factor(dt, a, zoh_exact) * rd(B, bc + n, io_dtype) * x;
+          prod[n] *= abar;
+          y += rd(C, bc + n, io_dtype) * (hloc[n] + prod[n] * h_in[n]);
+        }
+        if (D) y += (double)D[d] * x;
+        if (z) y *= silu(rd(z, e, io_dtype));
+        out[r * seqlen + t] = y;
+      }
+      for (int64_t n = 0; n < d_state; ++n) h_in[n] = hloc[n] + prod[n] * h_in[n];
+    }
+    if (h_last)
+      for (int64_t n = 0; n < d_state; ++n) h_last[r * d_state + n] = h_in[n];
+  }
+  return 0;
+}
+
+/*
+ * One decode step (single token) on a resident state [P1 Perguntas: a fixed-size D x N state
+ * per layer, advanced once per generated token; P2: constant memory at inference].
+ * Exactly one t-iteration of oracle_scan_fwd with h read from and written back to `state`.
+ *
+ *   state            : (batch, d_inner, d_state) f64, updated in place for the selected rows
+ *   u, delta, z      : (batch, d_inner) io dtype;  B, C : (batch, d_state) io dtype
+ *   rows / nrows     : as in oracle_scan_fwd;  out : (nrows) f64
+ */
+int oracle_state_update(double* state, const void* u, const void* delta, const float* A,
+                        const void* B, const void* C, const float* D, const void* z,
+                        const float* delta_bias, int delta_softplus, int zoh_exact,
+                        int io_dtype, int64_t batch, int64_t d_inner, int64_t d_state,
+                        const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (!state || !u || !delta || !A || !B || !C || !out) return -1;
+  if (batch < 0 || d_inner < 0 || d_state < 1 || d_state > 256) return -1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  if (!rows) nrows = batch * d_inner;
+  if (nthreads < 1) nthreads = 1;
+  int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : bad)
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t r = rows ? rows[i] : i;
+    if (r < 0 || r >= batch * d_inner) { bad = 1; continue; }
+    int64_t b = r / d_inner, d = r % d_inner;
+    double x = rd(u, r, io_dtype);
+    double dt = step_size(rd(delta, r, io_dtype), delta_bias, d, delta_softplus);
+    double y = 0.0;
+    for (int64_t n = 0; n < d_state; ++n) {
+      double a = (double)A[d * d_state + n];
+      double* h = &state[r * d_state + n];
+      *h = exp(dt * a) * (*h) + bbar_factor(dt, a, zoh_exact) * rd(B, b * d_state + n, io_dtype) * x;
+      y += rd(C, b * d_state + n, io_dtype) * (*h);
+    }
+    if (D) y += (double)D[d] * x;
+    if (z) y *= silu(rd(z, r, io_dtype));
+    out[i] = y;
+  }
+  return bad ? -1 : 0;
+}
+
+/* Number of threads OpenMP would use by default (for reporting the CPU baseline). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
