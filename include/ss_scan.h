@@ -1,0 +1,130 @@
+/*
+ * ss_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library (libssscan.so).
+ *
+ * The operation (Mamba's selective SSM, "S6"), for every batch row b and channel d:
+ *
+ *     dt_t    = softplus(delta[b,t,d] + delta_bias[d])      (or the raw sum, softplus off)
+ *     h_t[n]  = exp(dt_t * A[d,n]) * h_{t-1}[n] + dt_t * B[b,t,n] * u[b,t,d]
+ *     y_t     = sum_n C[b,t,n] * h_t[n] + D[d] * u[b,t,d]
+ *     out     = y_t * silu(z[b,t,d])                        (when z is given)
+ *
+ * Sources (web pages; cited by title and section):
+ *   - "Mamba: Linear-Time Sequence Modeling with Selective State Spaces" reading guide
+ *     (xyznot.com): "Método" (continuous SSM, ZOH discretisation Abar = exp(dt A), the
+ *     recurrence and y_t = C h_t), "O Mecanismo de Seleção (S6)" (B_t, C_t and dt_t depend on the
+ *     input; dt = softplus(Parameter + s(x))), "Expansão de Estado Ciente de Hardware" (the
+ *     (batch, L, d_inner, d_state) state is never written to HBM; the output is contracted with C
+ *     first), "Perguntas" (decode keeps a fixed d_inner x d_state state per layer, O(1) per token).
+ *   - "O que é um modelo Mamba?" (ibm.com): the output equation with the D term, the diagonal A,
+ *     and the Mamba block in which the SSM output is multiplied by the activated gate z.
+ *   - "Как работает Mamba" (aivaro.ru), section 3 "Selective Scan": the function shape
+ *     selective_scan(u, delta, A, B, C, D) with u, delta [batch, length, d_in] and B, C
+ *     [batch, length, d_state], and the first-order input term B_bar = delta * B.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller; arrays are contiguous and row-major.
+ *     The library allocates no device memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
+ *     work and return; they never synchronise, print or throw.
+ *   - Argument errors are detected before anything is launched and leave all outputs untouched.
+ *     A launch failure is reported as SS_ERR_HIP.  ss_last_error() gives a thread-local message.
+ *   - All index arithmetic is 64-bit.  Calls are thread-safe.
+ *   - Element types: SS_F32 (float) or SS_BF16 (bfloat16 bits) for u, delta, z, B, C and out;
+ *     A, D, delta_bias, the state, h0 and h_last are always float32.  Arithmetic and the state
+ *     are float32; out is rounded to its dtype with round-to-nearest-even.
+ */
+#ifndef SS_SCAN_H
+#define SS_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_INVALID_ARG = 1, /* NULL required pointer, negative or inconsistent size, aliasing */
+  SS_ERR_UNSUPPORTED = 2, /* d_state outside 1..64, unknown dtype, misaligned element type */
+  SS_ERR_HIP = 3          /* the HIP runtime reported an error while launching */
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/*
+ * Prefill: the whole sequence in one call.
+ *
+ *   u, delta, z, out : (batch, seqlen, d_inner), io dtype.  z == NULL: no gate.
+ *   B, C             : (batch, seqlen, d_state), io dtype, shared by all channels.
+ *   A                : (d_inner, d_state) float32, the diagonal of each channel's A.
+ *   D                : (d_inner) float32, skip weight; NULL means 0.
+ *   delta_bias       : (d_inner) float32, added to delta before softplus; NULL means 0.
+ *   delta_softplus   : nonzero -> dt = softplus(delta + bias); zero -> dt = delta + bias.
+ *   h0               : (batch, d_inner, d_state) float32 initial state; NULL means zeros.
+ *   h_last           : (batch, d_inner, d_state) float32 final state, written if non-NULL.
+ *   workspace        : optional device scratch for splitting long sequences in time.  Size it
+ *                      with ss_scan_fwd_workspace_bytes(); with less (or NULL/0) the library
+ *                      splits less (or not at all): the result is the same up to rounding,
+ *                      only slower on shapes with few channels.
+ * out and h_last must not overlap any input or each other (SS_ERR_INVALID_ARG).
+ * batch == 0, seqlen == 0 or d_inner == 0 is a no-op returning SS_OK (with seqlen == 0 and
+ * h_last given, h_last receives h0, or zeros).
+ */
+ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int delta_softplus, const float* h0, float* h_last, void* out,
+                      int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      ss_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ss_scan_fwd can use for this shape (0 when it would not split in time). */
+size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                   int64_t d_state, ss_dtype dtype);
+
+/*
+ * Prefill with an explicit time split.  nseg > 0 forces the sequence to be cut into that many
+ * segments (each scanned from a carried state; the carries come from a first summary pass over
+ * the segments, the blockwise associative decomposition of the recurrence); nseg == 0 chooses
+ * automatically.  Used to check that the result does not depend on the split.  The workspace
+ * must hold ss_scan_fwd_ex_workspace_bytes(..., nseg) bytes.
+ */
+ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* delta_bias,
+                         int delta_softplus, const float* h0, float* h_last, void* out,
+                         int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                         ss_dtype dtype, void* workspace, size_t workspace_bytes, int32_t nseg,
+                         void* stream);
+
+size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                      int64_t d_state, ss_dtype dtype, int32_t nseg);
+
+/*
+ * Decode: advance a resident state by ONE token (the recurrence above for a single t).
+ *
+ *   state        : (batch, d_inner, d_state) float32, read and overwritten IN PLACE.
+ *   u, delta, z  : (batch, d_inner), io dtype; z == NULL: no gate.
+ *   B, C         : (batch, d_state), io dtype.
+ *   out          : (batch, d_inner), io dtype.
+ *   A, D, delta_bias, delta_softplus, dtype, stream: as for ss_scan_fwd.
+ * out must not overlap state or the inputs.
+ */
+ss_status ss_state_update(float* state, const void* u, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D, const void* z,
+                          const float* delta_bias, int delta_softplus, void* out,
+                          int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                          void* stream);
+
+/* Static description of a status code. */
+const char* ss_status_string(ss_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* ss_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int ss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SCAN_H */

@@ -1,0 +1,328 @@
+// ss_api.hip -- the C ABI of libssscan.so (declared in include/ss_scan.h): argument checking,
+// choice of the time split, workspace layout and kernel dispatch.  No allocation, no
+// synchronisation, no printing: errors come back as status codes with a thread-local message.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/ss_scan.h"
+#include "ss_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ss_status fail(ss_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ss_status fail(ss_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ss_status ok() {
+  g_err[0] = '\0';
+  return SS_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* p, int64_t elems, int64_t esize) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + static_cast<uintptr_t>(elems * esize) : lo};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Automatic time split: enough waves for ~3 per SIMD (4 SIMDs per CU), segments of >= 256 steps.
+int32_t auto_nseg(int64_t batch, int64_t seqlen, int64_t d_inner) {
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0) return 1;
+  const int64_t waves_per_seg = batch * ((d_inner + ss::kChanPerWG - 1) / ss::kChanPerWG) * 4;
+  const int64_t target = 12ll * cu_count();
+  int64_t nseg = (target + waves_per_seg - 1) / waves_per_seg;
+  nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, seqlen / 256));
+  nseg = std::min<int64_t>(nseg, 4096);
+  return static_cast<int32_t>(std::max<int64_t>(nseg, 1));
+}
+
+// Segment length (a multiple of the B/C tile) and the effective segment count for a request.
+void segments(int64_t seqlen, int32_t want, int64_t* seg_len, int32_t* nseg) {
+  if (want <= 1 || seqlen <= ss::kChunk) {
+    *seg_len = std::max<int64_t>(seqlen, 1);
+    *seg_len = (*seg_len + ss::kChunk - 1) / ss::kChunk * ss::kChunk;
+    *nseg = 1;
+    return;
+  }
+  int64_t len = (seqlen + want - 1) / want;
+  len = (len + ss::kChunk - 1) / ss::kChunk * ss::kChunk;
+  *seg_len = len;
+  *nseg = static_cast<int32_t>((seqlen + len - 1) / len);
+}
+
+size_t ws_bytes(int64_t batch, int64_t d_inner, int64_t d_state, int32_t nseg) {
+  if (nseg <= 1) return 0;
+  const int64_t rows = batch * d_inner;
+  const int64_t per = rows * d_state + rows;  // floats per summarised segment
+  return static_cast<size_t>((nseg - 1) * per) * sizeof(float) + 256;
+}
+
+ss_status check_dtype(ss_dtype dt, int64_t* esize) {
+  if (dt == SS_F32) { *esize = 4; return SS_OK; }
+  if (dt == SS_BF16) { *esize = 2; return SS_OK; }
+  return fail(SS_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
+}
+
+ss_status scan_impl(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int delta_softplus, const float* h0, float* h_last, void* out, int64_t batch,
+                    int64_t seqlen, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                    void* workspace, size_t workspace_bytes, int32_t nseg_req, bool forced,
+                    void* stream) {
+  int64_t es = 0;
+  if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
+    return fail(SS_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld d_inner=%lld "
+                "d_state=%lld)", (long long)batch, (long long)seqlen, (long long)d_inner,
+                (long long)d_state);
+  if (d_state < 1 || d_state > 64)
+    return fail(SS_ERR_UNSUPPORTED, "d_state=%lld outside 1..64", (long long)d_state);
+  if (nseg_req < 0) return fail(SS_ERR_INVALID_ARG, "nseg=%d is negative", nseg_req);
+  int64_t rows, elems, bc_elems, st_elems;
+  if (!mul_ok(batch, d_inner, &rows) || !mul_ok(rows, seqlen, &elems) ||
+      !mul_ok(batch * seqlen, d_state, &bc_elems) || !mul_ok(rows, d_state, &st_elems) ||
+      !mul_ok(elems, 8, &elems) || !mul_ok(bc_elems, 8, &bc_elems))
+    return fail(SS_ERR_INVALID_ARG, "sizes overflow 64-bit byte offsets");
+  elems /= 8;
+  bc_elems /= 8;
+  if (batch == 0 || d_inner == 0) return ok();
+  if (seqlen == 0) {
+    if (h_last) {
+      if (h0 && overlap(range("h0", h0, st_elems, 4), range("h_last", h_last, st_elems, 4)) &&
+          h0 != h_last)
+        return fail(SS_ERR_INVALID_ARG, "h_last overlaps h0");
+      if (h0 != h_last) {
+        const hipError_t e = ss::launch_copy_state(h_last, h0, st_elems,
+                                                   static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+      }
+    }
+    return ok();
+  }
+  if (!u || !delta || !A || !B || !C || !out)
+    return fail(SS_ERR_INVALID_ARG, "required pointer is NULL (u, delta, A, B, C and out are "
+                "required)");
+  const void* io_ptrs[] = {u, delta, B, C, z, out};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es))
+      return fail(SS_ERR_UNSUPPORTED, "io pointer %p not aligned to its %lld-byte element", p,
+                  (long long)es);
+  const void* f_ptrs[] = {A, D, delta_bias, h0, h_last};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
+  if (int64_t(d_inner) * d_state > (int64_t(1) << 40))
+    return fail(SS_ERR_INVALID_ARG, "A too large");
+
+  const Range ins[] = {range("u", u, elems, es), range("delta", delta, elems, es),
+                       range("z", z, elems, es), range("B", B, bc_elems, es),
+                       range("C", C, bc_elems, es), range("A", A, d_inner * d_state, 4),
+                       range("D", D, d_inner, 4), range("delta_bias", delta_bias, d_inner, 4),
+                       range("h0", h0, st_elems, 4)};
+  const Range ro = range("out", out, elems, es);
+  const Range rh = range("h_last", h_last, st_elems, 4);
+  for (const Range& in : ins) {
+    if (overlap(ro, in)) return fail(SS_ERR_INVALID_ARG, "out overlaps %s", in.name);
+    if (overlap(rh, in)) return fail(SS_ERR_INVALID_ARG, "h_last overlaps %s", in.name);
+  }
+  if (overlap(ro, rh)) return fail(SS_ERR_INVALID_ARG, "out overlaps h_last");
+
+  // time split
+  int32_t want = forced && nseg_req > 0 ? nseg_req : auto_nseg(batch, seqlen, d_inner);
+  int64_t seg_len = 0;
+  int32_t nseg = 1;
+  segments(seqlen, want, &seg_len, &nseg);
+  if (forced && nseg_req > 0) {
+    if (ws_bytes(batch, d_inner, d_state, nseg) > workspace_bytes || (nseg > 1 && !workspace))
+      return fail(SS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes "
+                  "needed for nseg=%d", workspace_bytes, ws_bytes(batch, d_inner, d_state, nseg),
+                  nseg);
+  } else {
+    // split only as far as the workspace allows
+    while (nseg > 1 && (!workspace || ws_bytes(batch, d_inner, d_state, nseg) > workspace_bytes)) {
+      want = std::max<int32_t>(1, want / 2);
+      segments(seqlen, want, &seg_len, &nseg);
+      if (want == 1) break;
+    }
+    if (nseg > 1 && (!workspace || ws_bytes(batch, d_inner, d_state, nseg) > workspace_bytes))
+      segments(seqlen, 1, &seg_len, &nseg);
+  }
+
+  ss::ScanArgs a{};
+  a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.D = D;
+  a.delta_bias = delta_bias; a.h0 = h0; a.h_last = h_last; a.out = out;
+  a.batch = batch; a.seqlen = seqlen; a.d_inner = d_inner;
+  a.seg_len = seg_len;
+  a.n_cblk = (d_inner + ss::kChanPerWG - 1) / ss::kChanPerWG;
+  a.d_state = static_cast<int32_t>(d_state);
+  a.nseg = nseg;
+  a.softplus = delta_softplus ? 1 : 0;
+  if (nseg > 1) {
+    uintptr_t base = (reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255);
+    a.seg_h = reinterpret_cast<float*>(base);
+    a.seg_dt = a.seg_h + (nseg - 1) * rows * d_state;
+    const Range rw = range("workspace", workspace, static_cast<int64_t>(workspace_bytes), 1);
+    for (const Range& in : ins)
+      if (overlap(rw, in)) return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", in.name);
+    if (overlap(rw, ro) || overlap(rw, rh))
+      return fail(SS_ERR_INVALID_ARG, "workspace overlaps an output");
+  }
+  const int64_t ncb = batch * a.n_cblk;
+  if (ncb * nseg > int64_t(0x7fffffff))
+    return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == SS_BF16;
+  if (nseg > 1) {
+    a.n_wg = ncb * (nseg - 1);
+    const hipError_t e = ss::launch_scan(a, bf16, /*summary=*/true, st);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "summary launch failed: %s", hipGetErrorString(e));
+  }
+  a.n_wg = ncb * nseg;
+  const hipError_t e = ss::launch_scan(a, bf16, /*summary=*/false, st);
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int delta_softplus, const float* h0, float* h_last, void* out,
+                      int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      ss_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, 0, false, stream);
+}
+
+size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                   int64_t d_state, ss_dtype dtype) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
+  int64_t seg_len;
+  int32_t nseg;
+  segments(seqlen, auto_nseg(batch, seqlen, d_inner), &seg_len, &nseg);
+  return ws_bytes(batch, d_inner, d_state, nseg);
+}
+
+ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* delta_bias,
+                         int delta_softplus, const float* h0, float* h_last, void* out,
+                         int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                         ss_dtype dtype, void* workspace, size_t workspace_bytes, int32_t nseg,
+                         void* stream) {
+  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, nseg, true,
+                   stream);
+}
+
+size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                      int64_t d_state, ss_dtype dtype, int32_t nseg) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
+  int64_t seg_len;
+  int32_t n;
+  segments(seqlen, nseg > 0 ? nseg : auto_nseg(batch, seqlen, d_inner), &seg_len, &n);
+  return ws_bytes(batch, d_inner, d_state, n);
+}
+
+ss_status ss_state_update(float* state, const void* u, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D, const void* z,
+                          const float* delta_bias, int delta_softplus, void* out,
+                          int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                          void* stream) {
+  int64_t es = 0;
+  if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (batch < 0 || d_inner < 0 || d_state < 0)
+    return fail(SS_ERR_INVALID_ARG, "negative size");
+  if (d_state < 1 || d_state > 64)
+    return fail(SS_ERR_UNSUPPORTED, "d_state=%lld outside 1..64", (long long)d_state);
+  int64_t rows, st_elems;
+  if (!mul_ok(batch, d_inner, &rows) || !mul_ok(rows, d_state, &st_elems) ||
+      !mul_ok(st_elems, 64, &st_elems))
+    return fail(SS_ERR_INVALID_ARG, "sizes overflow");
+  st_elems /= 64;
+  if (rows == 0) return ok();
+  if (!state || !u || !delta || !A || !B || !C || !out)
+    return fail(SS_ERR_INVALID_ARG, "required pointer is NULL (state, u, delta, A, B, C, out)");
+  const void* io_ptrs[] = {u, delta, B, C, z, out};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es)) return fail(SS_ERR_UNSUPPORTED, "io pointer %p misaligned", p);
+  const void* f_ptrs[] = {state, A, D, delta_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
+  const Range ins[] = {range("u", u, rows, es), range("delta", delta, rows, es),
+                       range("z", z, rows, es), range("B", B, batch * d_state, es),
+                       range("C", C, batch * d_state, es), range("A", A, d_inner * d_state, 4),
+                       range("D", D, d_inner, 4), range("delta_bias", delta_bias, d_inner, 4)};
+  const Range rs = range("state", state, st_elems, 4);
+  const Range ro = range("out", out, rows, es);
+  for (const Range& in : ins) {
+    if (overlap(rs, in)) return fail(SS_ERR_INVALID_ARG, "state overlaps %s", in.name);
+    if (overlap(ro, in)) return fail(SS_ERR_INVALID_ARG, "out overlaps %s", in.name);
+  }
+  if (overlap(ro, rs)) return fail(SS_ERR_INVALID_ARG, "out overlaps state");
+
+  ss::DecodeArgs a{};
+  a.state = state; a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.D = D;
+  a.delta_bias = delta_bias; a.out = out;
+  a.batch = batch; a.d_inner = d_inner; a.d_state = static_cast<int32_t>(d_state);
+  int g = 1;
+  while (g * 4 < d_state) g <<= 1;
+  a.lanes_per_chan = g;
+  a.softplus = delta_softplus ? 1 : 0;
+  a.vec4 = (d_state % 4 == 0 && aligned(state, 16) && aligned(A, 16)) ? 1 : 0;
+  if ((rows * g + 255) / 256 > int64_t(0x7fffffff))
+    return fail(SS_ERR_INVALID_ARG, "too many rows");
+  const hipError_t e = ss::launch_decode(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* ss_status_string(ss_status s) {
+  switch (s) {
+    case SS_OK: return "ok";
+    case SS_ERR_INVALID_ARG: return "invalid argument";
+    case SS_ERR_UNSUPPORTED: return "unsupported argument";
+    case SS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ss_last_error(void) { return g_err; }
+
+int ss_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// ss_device.h -- device-side helpers shared by the gfx950 prefill and decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element access for the two io dtypes.  bf16 is carried as raw 16-bit patterns: widening is a
+// 16-bit shift (exact); narrowing uses the hardware round-to-nearest-even conversion.
+struct F32 {
+  using elem = float;
+  static __device__ __forceinline__ float load(const elem* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ elem from_float(float f) { return f; }
+};
+struct BF16 {
+  using elem = uint16_t;
+  static __device__ __forceinline__ float load(const elem* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+  static __device__ __forceinline__ elem from_float(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+  }
+};
+
+// 2^x and log2(x) on the hardware transcendental unit (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(s) = max(s, 0) + log1p(e^{-|s|}).  log1p(e) for e in (0, 1] is evaluated as
+// log(w) + (e - (w - 1)) with w = fl(1 + e): the second term restores the part of e lost when
+// forming w, so the result keeps full relative precision when e is tiny (small step sizes).
+__device__ __forceinline__ float softplus_f(float s) {
+  const float e = exp2_hw(-fabsf(s) * kLog2e);
+  const float w = 1.0f + e;
+  const float l = log2_hw(w) * kLn2;
+  const float c = e - (w - 1.0f);
+  return fmaxf(s, 0.0f) + (l + c);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z}).
+__device__ __forceinline__ float silu_f(float z) {
+  return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+}
+
+// Value of `x` held by lane SRC of this lane's 16-lane row (DPP row_newbcast).  When the result
+// feeds a multiply the compiler folds the broadcast into the multiply itself.
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(SRC >= 0 && SRC < 16, "row lane");
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + SRC, 0xf, 0xf, false));
+}
+
+// Make this wavefront's LDS writes visible to all of its lanes (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Remap the hardware
+// workgroup index so that each XCD receives one contiguous range of logical indices: logical
+// neighbours (which share cache lines of the inputs) then meet in the same L2.  A bijection on
+// [0, n) for any n.
+__device__ __forceinline__ int64_t xcd_remap(int64_t hw, int64_t n) {
+  const int64_t q = n >> 3, rem = n & 7;
+  const int64_t x = hw & 7, j = hw >> 3;
+  return x < rem ? x * (q + 1) + j : rem * (q + 1) + (x - rem) * q + j;
+}
+
+}  // namespace ss

@@ -1,0 +1,67 @@
+// ss_launch.h -- host-side launch interface between the C-ABI layer (ss_api.hip) and the kernel
+// translation units.  Argument validation happens before these are called; they only pick the
+// kernel instance and enqueue it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+// Geometry of the prefill kernels: 16 lanes (one DPP row) per channel, 4 channels per wave,
+// 4 waves (16 channels) per workgroup, time processed in 16-step sub-chunks and 32-step B/C tiles.
+constexpr int kPrefillThreads = 256;
+constexpr int kChanPerWG = 16;
+constexpr int kChunk = 32;
+
+struct ScanArgs {
+  const void* u;
+  const void* delta;
+  const void* z;       // nullptr: no gate
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;      // nullptr: 0
+  const float* delta_bias;  // nullptr: 0
+  const float* h0;     // nullptr: zeros
+  float* h_last;       // nullptr: not written
+  void* out;
+  float* seg_h;        // (nseg-1, batch, d_inner, d_state): local end state of each segment
+  float* seg_dt;       // (nseg-1, batch, d_inner): sum of dt over each segment
+  int64_t batch, seqlen, d_inner;
+  int64_t seg_len;     // multiple of kChunk
+  int64_t n_cblk;      // channel blocks per batch row = ceil(d_inner / kChanPerWG)
+  int64_t n_wg;        // workgroups of the launch
+  int32_t d_state;
+  int32_t nseg;
+  int32_t softplus;
+};
+
+struct DecodeArgs {
+  float* state;
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;
+  const float* delta_bias;
+  void* out;
+  int64_t batch, d_inner;
+  int32_t d_state;
+  int32_t lanes_per_chan;  // power of two >= ceil(d_state / 4)
+  int32_t softplus;
+  int32_t vec4;            // d_state % 4 == 0 and 16-byte aligned state/A
+};
+
+// Prefill passes.  `summary` selects the first pass of a time-split scan (segments 0..nseg-2,
+// local end states and dt sums into seg_h/seg_dt); otherwise the output pass over all segments.
+hipError_t launch_scan(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
+
+// Fill h_last with h0 (or zeros) when the sequence is empty.
+hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
+}  // namespace ss

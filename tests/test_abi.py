@@ -1,0 +1,98 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol include/ss_scan.h declares,
+and rejects bad arguments before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_36_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss_scan.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from selective_state_space_36_amd import build
+        build.build()
+    return ops.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ss_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("ss_scan_fwd", "ss_state_update", "ss_scan_fwd_workspace_bytes",
+                     "ss_scan_fwd_ex", "ss_status_string", "ss_last_error"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in ops.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.ss_status_string(0) == b"ok"
+    assert lib.ss_status_string(1) == b"invalid argument"
+    assert lib.ss_status_string(3) == b"HIP runtime error"
+    assert lib.ss_version() >= 100
+
+
+FAKE = 1 << 20  # a non-NULL, aligned address that is never dereferenced
+
+
+def _scan(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None,
+             bias=None, sp=1, h0=None, hl=None, out=FAKE * 6, batch=1, L=4, d=8, N=16,
+             dtype=ops.SS_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.ss_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                           a["sp"], a["h0"], a["hl"], a["out"], a["batch"], a["L"], a["d"], a["N"],
+                           a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_scan_argument_errors_before_launch(lib):
+    assert _scan(lib, N=0) == ops.SS_ERR_UNSUPPORTED
+    assert _scan(lib, N=65) == ops.SS_ERR_UNSUPPORTED
+    assert _scan(lib, dtype=7) == ops.SS_ERR_UNSUPPORTED
+    assert _scan(lib, batch=-1) == ops.SS_ERR_INVALID_ARG
+    assert _scan(lib, u=None) == ops.SS_ERR_INVALID_ARG
+    assert b"NULL" in lib.ss_last_error()
+    assert _scan(lib, out=FAKE) == ops.SS_ERR_INVALID_ARG          # out aliases u
+    assert b"overlaps" in lib.ss_last_error()
+    assert _scan(lib, u=FAKE + 1) == ops.SS_ERR_UNSUPPORTED         # misaligned bf16
+    assert _scan(lib, L=1 << 62, d=1 << 10) == ops.SS_ERR_INVALID_ARG  # overflow
+    # empty problems are no-ops that succeed without any launch
+    assert _scan(lib, batch=0) == ops.SS_OK
+    assert _scan(lib, d=0) == ops.SS_OK
+    assert lib.ss_last_error() == b""
+
+
+def test_forced_split_needs_workspace(lib):
+    rc = lib.ss_scan_fwd_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
+                            None, None, FAKE * 6, 2, 4096, 64, 16, ops.SS_BF16, None, 0, 4, None)
+    assert rc == ops.SS_ERR_INVALID_ARG and b"workspace" in lib.ss_last_error()
+    assert lib.ss_scan_fwd_ex_workspace_bytes(2, 4096, 64, 16, ops.SS_BF16, 1) == 0
+    nb = lib.ss_scan_fwd_ex_workspace_bytes(2, 4096, 64, 16, ops.SS_BF16, 4)
+    assert nb >= 3 * (2 * 64 * 16 + 2 * 64) * 4
+
+
+def test_decode_argument_errors(lib):
+    f = lib.ss_state_update
+    assert f(None, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1, FAKE * 6,
+             2, 8, 16, ops.SS_BF16, None) == ops.SS_ERR_INVALID_ARG
+    assert f(FAKE * 8, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
+             FAKE * 6, 2, 8, 0, ops.SS_BF16, None) == ops.SS_ERR_UNSUPPORTED
+    assert f(FAKE * 8, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
+             FAKE * 8, 2, 8, 16, ops.SS_BF16, None) == ops.SS_ERR_INVALID_ARG  # out == state
+    assert f(FAKE * 8, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
+             FAKE * 6, 0, 8, 16, ops.SS_BF16, None) == ops.SS_OK

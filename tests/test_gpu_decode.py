@@ -1,0 +1,129 @@
+"""GPU parity of the decode entry point (ss_state_update) against the fp64 oracle, and the
+decode/prefill contract: L single-token steps reproduce the prefill outputs and final state."""
+import numpy as np
+import pytest
+
+import oracle
+from selective_state_space_36_amd import workloads as wl
+from tests.helpers import TOL, check_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_36_amd import ops
+    ops.lib()
+    yield
+
+
+def ops():
+    from selective_state_space_36_amd import ops as o
+    return o
+
+
+def _decode_steps(d, steps, rows=None, gate=True, skip=True):
+    """Run `steps` GPU decode steps and the oracle's; compare every step's output (optionally on
+    a row subset) and the final state."""
+    batch, d_inner, N = d["state"].shape
+    st_gpu = dev(d["state"])
+    st_ref = d["state"].astype(np.float64)
+    A, D, db = dev(d["A"]), dev(d["D"]) if skip else None, dev(d["delta_bias"])
+    u_all, dl_all, B_all, C_all = (dev(d[k]) for k in ("u", "delta", "B", "C"))
+    z_all = dev(d["z"]) if gate else None
+    tol = TOL["bf16"] if d["u"].dtype == np.uint16 else TOL["f32"]
+    for s in range(steps):
+        out = ops().state_update(st_gpu, u_all[s], dl_all[s], A, B_all[s], C_all[s], D=D,
+                                 z=None if z_all is None else z_all[s], delta_bias=db)
+        ref = oracle.state_update(st_ref, d["u"][s], d["delta"][s], d["A"], d["B"][s], d["C"][s],
+                                  D=d["D"] if skip else None, z=d["z"][s] if gate else None,
+                                  delta_bias=d["delta_bias"], rows=rows)
+        g = host(out).reshape(-1)
+        if rows is not None:
+            g = g[rows]
+        check_close(g, ref.reshape(-1), tol, f"decode step {s}")
+    torch.cuda.synchronize()
+    gs = host(st_gpu).reshape(-1, N)
+    rs = st_ref.reshape(-1, N)
+    if rows is not None:
+        gs, rs = gs[rows], rs[rows]
+    check_close(gs, rs, 1e-4, "final state")
+
+
+@pytest.mark.parametrize("d_state", [16, 1, 3, 8, 24, 64])
+def test_decode_small(d_state):
+    w = wl.WORKLOADS[4]
+    d = wl.make_decode(w, steps=6, batch=3, d_inner=40)
+    if d_state != 16:
+        rng = np.random.default_rng(d_state)
+        d["state"] = rng.standard_normal((3, 40, d_state)).astype(np.float32)
+        d["A"] = np.ascontiguousarray(np.tile(-np.arange(1, d_state + 1, dtype=np.float32), (40, 1)))
+        d["B"] = wl.f32_to_bf16_bits(rng.standard_normal((6, 3, d_state)).astype(np.float32))
+        d["C"] = wl.f32_to_bf16_bits(rng.standard_normal((6, 3, d_state)).astype(np.float32))
+    print(f"  decode small N={d_state}", flush=True)
+    _decode_steps(d, 6)
+
+
+def test_decode_fp32_no_gate():
+    rng = np.random.default_rng(5)
+    batch, d_inner, N, steps = 4, 33, 16, 5
+    d = dict(state=rng.standard_normal((batch, d_inner, N)).astype(np.float32),
+             u=rng.standard_normal((steps, batch, d_inner)).astype(np.float32),
+             delta=(0.5 * rng.standard_normal((steps, batch, d_inner))).astype(np.float32),
+             z=None,
+             B=rng.standard_normal((steps, batch, N)).astype(np.float32),
+             C=rng.standard_normal((steps, batch, N)).astype(np.float32),
+             A=-rng.uniform(0.5, 4, size=(d_inner, N)).astype(np.float32),
+             D=rng.standard_normal(d_inner).astype(np.float32),
+             delta_bias=rng.uniform(-4, -1, size=d_inner).astype(np.float32))
+    _decode_steps(d, steps, gate=False)
+
+
+def test_decode_reproduces_prefill():
+    """L decode steps from h0 == one prefill of length L (outputs per step and final state)."""
+    w = wl.WORKLOADS[1]
+    p = wl.make_prefill(w, batch=2, seqlen=40, d_inner=64, seed=3)
+    h0 = np.random.default_rng(9).standard_normal((2, 64, 16)).astype(np.float32)
+    out, h_last = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]),
+                                 dev(p["C"]), D=dev(p["D"]), z=dev(p["z"]),
+                                 delta_bias=dev(p["delta_bias"]), h0=dev(h0),
+                                 return_last_state=True)
+    st = dev(h0)
+    outs = []
+    for t in range(40):
+        sl = lambda k: dev(np.ascontiguousarray(p[k][:, t]))
+        outs.append(ops().state_update(st, sl("u"), sl("delta"), dev(p["A"]), sl("B"), sl("C"),
+                                       D=dev(p["D"]), z=sl("z"), delta_bias=dev(p["delta_bias"])))
+    torch.cuda.synchronize()
+    dec = host(torch.stack(outs, dim=1))
+    check_close(dec, host(out), 1e-2, "decode vs prefill outputs")
+    check_close(host(st), host(h_last), 1e-5, "decode vs prefill state")
+
+
+def test_decode_invalid_arguments():
+    o = ops()
+    st = torch.zeros((2, 8, 16), device="cuda")
+    u = torch.zeros((2, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((2, 16), dtype=torch.bfloat16, device="cuda")
+    A = -torch.ones((8, 16), device="cuda")
+    with pytest.raises(o.SSError) as e:
+        o.state_update(st, u, u.clone(), A, B, B.clone(), out=u)
+    assert e.value.status == o.SS_ERR_INVALID_ARG
+
+
+def test_decode_full_size_sampled():
+    """The batch-128 decode workload at full size for 50 consecutive steps (the bench times
+    1000): every step's output checked on sampled rows, and the final state on them."""
+    w = wl.WORKLOADS[4]
+    d = wl.make_decode(w, steps=50)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 16), np.arange(w.d_inner - 16, w.d_inner + 16),
+        (w.batch - 1) * w.d_inner + np.arange(w.d_inner - 16, w.d_inner),
+        rng.integers(0, w.batch * w.d_inner, size=2000)])).astype(np.int64)
+    print(f"  decode full size, {len(rows)} sampled rows", flush=True)
+    _decode_steps(d, 50, rows=rows)

@@ -1,0 +1,244 @@
+"""GPU parity of the prefill entry point (ss_scan_fwd / ss_scan_fwd_ex) against the fp64 oracle.
+
+Every case draws seeded inputs from selective_state_space_36_amd.workloads, runs the HIP kernels
+through the C ABI, and compares elementwise with oracle.scan_fwd on the same bytes:
+|gpu - oracle| <= tol + tol * |oracle|, tol = 1e-4 (float32 io) or 2e-2 (bfloat16 io).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from selective_state_space_36_amd import workloads as wl
+from tests.helpers import TOL, check_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_36_amd import ops
+    ops.lib()  # raises if the HIP library is missing: no silent fallback
+    yield
+
+
+def ops():
+    from selective_state_space_36_amd import ops as o
+    return o
+
+
+def run_case(p, *, gate=True, skip=True, h0=None, nseg=None, softplus=True, bias=True):
+    """Run GPU and oracle on generator arrays p; returns (gpu_out, gpu_h, ref_out, ref_h)."""
+    z = p["z"] if gate else None
+    D = p["D"] if skip else None
+    db = p["delta_bias"] if bias else None
+    print(f"  gpu case: shape={p['u'].shape} N={p['B'].shape[-1]} dtype={p['u'].dtype} "
+          f"gate={gate} skip={skip} h0={h0 is not None} nseg={nseg}", flush=True)
+    out, h_last = ops().scan_fwd(
+        dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"]), D=dev(D), z=dev(z),
+        delta_bias=dev(db), delta_softplus=softplus,
+        h0=None if h0 is None else dev(h0.astype(np.float32)), return_last_state=True, nseg=nseg)
+    torch.cuda.synchronize()
+    ref_out, ref_h = oracle.scan_fwd(
+        p["u"], p["delta"], p["A"], p["B"], p["C"], D=D, z=z, delta_bias=db,
+        delta_softplus=softplus, h0=None if h0 is None else h0.astype(np.float32).astype(np.float64))
+    return host(out), host(h_last), ref_out, ref_h
+
+
+def small(index, batch, seqlen, d_inner, seed=None, d_state=None):
+    w = wl.WORKLOADS[index]
+    p = wl.make_prefill(w, batch=batch, seqlen=seqlen, d_inner=d_inner, seed=seed)
+    if d_state is not None and d_state != w.d_state:
+        rng = np.random.default_rng(seed or 0)
+        shape = (batch, seqlen, d_state)
+        mk = (lambda x: wl.f32_to_bf16_bits(x)) if w.io_dtype == "bf16" else (lambda x: x)
+        p["B"] = mk(rng.standard_normal(shape).astype(np.float32))
+        p["C"] = mk(rng.standard_normal(shape).astype(np.float32))
+        p["A"] = np.ascontiguousarray(
+            np.tile(-np.arange(1, d_state + 1, dtype=np.float32), (d_inner, 1)))
+    return p, w
+
+
+# ------------------------------------------------------------------------------------------
+# the tiny fp32 workload at its full size, and scan-isolated
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("skip", [True, False])
+def test_tiny_fp32_full(skip):
+    w = wl.WORKLOADS[0]
+    p = wl.make_prefill(w)
+    g, gh, r, rh = run_case(p, gate=False, skip=skip)
+    check_close(g, r, TOL["f32"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+@pytest.mark.parametrize("gate,skip", [(True, True), (False, False), (True, False)])
+def test_tiny_fp32_with_gate_and_h0(gate, skip):
+    p, _ = small(0, 2, 200, 40, seed=5)
+    p["z"] = np.random.default_rng(1).standard_normal(p["u"].shape).astype(np.float32)
+    h0 = np.random.default_rng(2).standard_normal((2, 40, 16))
+    g, gh, r, rh = run_case(p, gate=gate, skip=skip, h0=h0)
+    check_close(g, r, TOL["f32"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 cases spanning several tiles, ragged channel blocks and ragged time tails
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("batch,seqlen,d_inner", [(1, 1, 16), (2, 33, 17), (3, 300, 50),
+                                                  (2, 1000, 64), (1, 64, 1)])
+def test_bf16_ragged_shapes(batch, seqlen, d_inner):
+    p, _ = small(1, batch, seqlen, d_inner, seed=7)
+    g, gh, r, rh = run_case(p)
+    check_close(g, r, TOL["bf16"], "out")
+    check_close(gh, rh, TOL["bf16"], "h_last")
+    # scan isolated: no skip term, no gate
+    g, gh, r, rh = run_case(p, gate=False, skip=False)
+    check_close(g, r, TOL["bf16"], "out (scan only)")
+
+
+@pytest.mark.parametrize("d_state", [1, 2, 5, 15, 16, 17, 31, 32, 48, 64])
+def test_state_sizes(d_state):
+    p, _ = small(0, 2, 130, 24, seed=11, d_state=d_state)
+    h0 = np.random.default_rng(3).standard_normal((2, 24, d_state))
+    g, gh, r, rh = run_case(p, h0=h0, gate=False)
+    check_close(g, r, TOL["f32"], f"out N={d_state}")
+    check_close(gh, rh, TOL["f32"], f"h_last N={d_state}")
+
+
+# ------------------------------------------------------------------------------------------
+# time split: forced segment counts agree with the oracle and with each other
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("nseg", [1, 2, 3, 7, 16])
+def test_time_split_matches_oracle(nseg):
+    p, _ = small(0, 2, 700, 32, seed=13)
+    h0 = np.random.default_rng(4).standard_normal((2, 32, 16))
+    g, gh, r, rh = run_case(p, gate=False, h0=h0, nseg=nseg)
+    check_close(g, r, TOL["f32"], f"out nseg={nseg}")
+    check_close(gh, rh, TOL["f32"], f"h_last nseg={nseg}")
+
+
+def test_time_split_long_bf16():
+    p, _ = small(3, 1, 20000, 48, seed=17)
+    g1, gh1, r, rh = run_case(p, nseg=1)
+    g8, gh8, _, _ = run_case(p, nseg=8)
+    check_close(g1, r, TOL["bf16"], "out nseg=1")
+    check_close(g8, r, TOL["bf16"], "out nseg=8")
+    check_close(gh8, rh, 1e-3, "h_last nseg=8")
+    check_close(gh1, rh, 1e-3, "h_last nseg=1")
+
+
+# ------------------------------------------------------------------------------------------
+# pins on the GPU: dt == 0, softplus off, determinism, split resume
+# ------------------------------------------------------------------------------------------
+def test_zero_step_is_exact_skip():
+    p, _ = small(0, 1, 100, 20, seed=19)
+    p["delta"] = np.zeros_like(p["delta"])
+    g, gh, r, rh = run_case(p, gate=False, softplus=False, bias=False)
+    want = (p["D"].astype(np.float64)[None, None, :] * p["u"].astype(np.float64)).astype(np.float32)
+    assert np.array_equal(g.astype(np.float32), want)
+    assert np.array_equal(gh, np.zeros_like(gh))
+
+
+def test_softplus_off():
+    p, _ = small(0, 2, 90, 20, seed=23)
+    p["delta"] = np.abs(p["delta"]) * np.float32(0.1)
+    g, gh, r, rh = run_case(p, gate=False, softplus=False)
+    check_close(g, r, TOL["f32"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+def test_bitwise_deterministic():
+    p, _ = small(1, 2, 500, 96, seed=29)
+    outs = []
+    for _ in range(3):
+        o, h = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"]),
+                              D=dev(p["D"]), z=dev(p["z"]), delta_bias=dev(p["delta_bias"]),
+                              return_last_state=True, nseg=3)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy(), h.cpu().numpy()))
+    for o, h in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(h, outs[0][1])
+
+
+def test_split_sequence_resume():
+    p, _ = small(1, 2, 640, 48, seed=31)
+    args = lambda sl: [dev(np.ascontiguousarray(p[k][:, sl])) for k in ("u", "delta")] + [dev(p["A"])] + \
+        [dev(np.ascontiguousarray(p[k][:, sl])) for k in ("B", "C")]
+    kw = lambda sl: dict(D=dev(p["D"]), z=dev(np.ascontiguousarray(p["z"][:, sl])),
+                         delta_bias=dev(p["delta_bias"]))
+    whole, hw = ops().scan_fwd(*args(slice(0, 640)), **kw(slice(0, 640)), return_last_state=True)
+    o1, h1 = ops().scan_fwd(*args(slice(0, 250)), **kw(slice(0, 250)), return_last_state=True)
+    o2, h2 = ops().scan_fwd(*args(slice(250, 640)), **kw(slice(250, 640)), h0=h1,
+                            return_last_state=True)
+    torch.cuda.synchronize()
+    check_close(host(torch.cat([o1, o2], dim=1)), host(whole), 1e-2, "resumed out")
+    check_close(host(h2), host(hw), 1e-5, "resumed state")
+
+
+def test_empty_and_degenerate_sizes():
+    o = ops()
+    u = torch.zeros((2, 0, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((2, 0, 16), dtype=torch.bfloat16, device="cuda")
+    A = -torch.ones((8, 16), device="cuda")
+    h0 = torch.randn((2, 8, 16), device="cuda")
+    out, hl = o.scan_fwd(u, u.clone(), A, B, B.clone(), h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 0, 8) and torch.equal(hl, h0)
+    u0 = torch.zeros((0, 5, 8), dtype=torch.bfloat16, device="cuda")
+    B0 = torch.zeros((0, 5, 16), dtype=torch.bfloat16, device="cuda")
+    out0 = o.scan_fwd(u0, u0.clone(), A, B0, B0.clone())
+    assert out0.shape == (0, 5, 8)
+
+
+def test_invalid_arguments_raise():
+    o = ops()
+    p, _ = small(1, 1, 8, 16, seed=37)
+    u, d, A, B, C = dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"])
+    with pytest.raises(o.SSError) as e:
+        o.scan_fwd(u, d, A, B, C, out=u)            # out aliases u
+    assert e.value.status == o.SS_ERR_INVALID_ARG
+    with pytest.raises(o.SSError) as e:
+        o.scan_fwd(u, d, A, B, C, nseg=4, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                  device="cuda"))
+    assert e.value.status == o.SS_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times; sampled rows
+# ------------------------------------------------------------------------------------------
+def _sample_rows(batch, d_inner, k, seed):
+    """Rows covering every batch index, both ends of the channel range and random interior
+    channels (each row is one independent recurrence, so the check on it is exact)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(batch):
+        for d in (0, 1, 15, 16, d_inner // 2, d_inner - 17, d_inner - 1):
+            rows.add(b * d_inner + d)
+    rows.update(rng.integers(0, batch * d_inner, size=k).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_full_size_workload_sampled(index):
+    w = wl.WORKLOADS[index]
+    print(f"  generating {w.name} ...", flush=True)
+    p = wl.make_prefill(w)
+    print(f"  running {w.name} on the GPU ...", flush=True)
+    out, h_last = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]),
+                                 dev(p["C"]), D=dev(p["D"]), z=dev(p["z"]),
+                                 delta_bias=dev(p["delta_bias"]), return_last_state=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.batch, w.d_inner, 24 if index < 3 else 6, seed=index)
+    b_idx, d_idx = rows // w.d_inner, rows % w.d_inner
+    g = out[torch.from_numpy(b_idx).cuda(), :, torch.from_numpy(d_idx).cuda()]
+    g = host(g)
+    gh = host(h_last.reshape(-1, w.d_state)[torch.from_numpy(rows).cuda()])
+    del out, h_last
+    print(f"  oracle on {len(rows)} rows x {w.seqlen} steps ...", flush=True)
+    r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                            delta_bias=p["delta_bias"], rows=rows)
+    check_close(g, r, TOL["bf16"], f"{w.name} out")
+    check_close(gh, rh, TOL["bf16"], f"{w.name} h_last")
