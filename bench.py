@@ -1,0 +1,298 @@
+"""Benchmark of the selective scan (S6) on one MI355X.
+
+Prints ONE JSON line.  A step is one prefill call (ss_scan_fwd) on the Mamba-2.8B-shaped layer
+(batch 4, L 4096, d_inner 5120, d_state 16, bf16 io, silu gate, fp32 state) with inputs resident
+in HBM; `value` is B*L*D elements per second over K timed steps.  The same line carries:
+  * roofline: the prefill kernel against the VALU issue rate (it is arithmetic-bound on gfx950,
+    see the design doc), with the HBM view alongside;
+  * decode: the batch-128 single-token step (ss_state_update) run 1000 times back to back over
+    pre-generated inputs: end-to-end us/step, kernel-only us/step and state GB/s;
+  * cpu_baseline: the fp64 C oracle timed on this host's cores on a bounded sample of rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--decode-steps 1000]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+# VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one 64-lane wave op
+# every 4 cycles per SIMD).  Non-packed fp32 ops take one slot; v_exp_f32 takes two on gfx950.
+PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
+SLOTS_PER_UPDATE = 6          # 1 exp (2 slots) + dt*A, (dt*u)*B, state FMA, C.h FMA
+SLOTS_PER_ELEMENT_GATED = 19  # bias add, softplus (exp 2 + log 4 + add), dt*u, skip FMA,
+                              # silu (exp 2 + add + rcp 4 + mul), gate mul
+SLOTS_PER_ELEMENT_PLAIN = 10
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3])
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def calibrate_copy(torch):
+    """A plain copy of known size: reads and writes exactly 1 GiB.  Its FETCH_SIZE/WRITE_SIZE
+    under rocprofv3 --pmc give the factor that converts those counters into HBM bytes."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_36_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def prefill_bytes(w) -> int:
+    s = 2 if w.io_dtype == "bf16" else 4
+    per_elem = (4 if w.gate else 3) * s          # u, delta, (z), out
+    return (w.elements * per_elem + 2 * w.batch * w.seqlen * w.d_state * s
+            + w.d_inner * w.d_state * 4 + 2 * w.d_inner * 4)
+
+
+def decode_bytes_per_step(w) -> int:
+    s = 2
+    return (8 * w.batch * w.d_inner * w.d_state + w.batch * w.d_inner * 4 * s
+            + 2 * w.batch * w.d_state * s + w.d_inner * w.d_state * 4 + 2 * w.d_inner * 4)
+
+
+def dev(x, torch, np):
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def bench_prefill(args, torch, np, ops, wl):
+    w = wl.WORKLOADS[args.workload]
+    log(f"generating {w.name} inputs")
+    p = wl.make_prefill(w)
+    u, dl, A, B, C = (dev(p[k], torch, np) for k in ("u", "delta", "A", "B", "C"))
+    D, z, db = dev(p["D"], torch, np), dev(p["z"], torch, np), dev(p["delta_bias"], torch, np)
+    out = torch.empty_like(u)
+    nbytes = ops.workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state, u.dtype)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ops.scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=db, out=out, workspace=ws,
+                     stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch events over the timed region give the kernel's average duration
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0, t_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_all0.elapsed_time(t_all1)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms_step = ms_total / args.steps
+    ms_kernel = sum(per) / len(per)
+    log(f"prefill {ms_step * 1e3:.1f} us/step (kernel avg {ms_kernel * 1e3:.1f} us, "
+        f"min {per[0] * 1e3:.1f})")
+
+    # spot parity check of the benchmarked output on a few rows
+    import oracle
+    rows = np.array([0, 1, w.d_inner - 1, (w.batch - 1) * w.d_inner + w.d_inner // 2],
+                    dtype=np.int64)
+    g = out.float()[torch.from_numpy(rows // w.d_inner).cuda(), :,
+                    torch.from_numpy(rows % w.d_inner).cuda()].cpu().numpy().astype(np.float64)
+    r, _ = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                           delta_bias=p["delta_bias"], rows=rows)
+    err = np.abs(g - r)
+    ok = bool(np.all(err <= 2e-2 + 2e-2 * np.abs(r)))
+    return w, p, ms_step, ms_kernel, ok, float(err.max())
+
+
+def bench_decode(args, torch, np, ops, wl):
+    w = wl.WORKLOADS[4]
+    steps = args.decode_steps
+    log(f"generating {steps} decode steps")
+    d = wl.make_decode(w, steps=steps)
+    st = dev(d["state"], torch, np)
+    u, dl, z, B, C = (dev(d[k], torch, np) for k in ("u", "delta", "z", "B", "C"))
+    A, D, db = dev(d["A"], torch, np), dev(d["D"], torch, np), dev(d["delta_bias"], torch, np)
+    out = torch.empty((steps, w.batch, w.d_inner), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one(s):
+        ops.state_update(st, u[s], dl[s], A, B[s], C[s], D=D, z=z[s], delta_bias=db, out=out[s],
+                         stream=stream)
+
+    for s in range(min(20, steps)):
+        one(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        one(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_e2e = e0.elapsed_time(e1) * 1e3 / steps
+    # kernel-only: events around each launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record(stream)
+        one(s)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    us_kernel = sum(per) / len(per)
+    log(f"decode {us_e2e:.2f} us/step end-to-end, kernel {us_kernel:.2f} us (median "
+        f"{per[len(per) // 2]:.2f})")
+    nb = decode_bytes_per_step(w)
+    return dict(
+        workload=w.name, batch=w.batch, d_inner=w.d_inner, d_state=w.d_state, steps=steps,
+        us_per_step_end_to_end=round(us_e2e, 3), us_per_step_kernel=round(us_kernel, 3),
+        us_per_step_kernel_median=round(per[len(per) // 2], 3),
+        state_GBps=round(8 * w.batch * w.d_inner * w.d_state / (us_kernel * 1e-6) / 1e9, 1),
+        roofline=dict(bound="hbm", achieved=round(nb / (us_kernel * 1e-6) / 1e9, 1),
+                      peak=PEAK_HBM_GBPS, unit="GB/s",
+                      frac=round(nb / (us_kernel * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                      traffic=measured_traffic(w.name)),
+        note="state (41.9 MB) is resident across steps and fits the 256 MB Infinity Cache")
+
+
+def cpu_baseline(args, np, w, p):
+    import oracle
+    threads = max(1, len(os.sched_getaffinity(0)))
+    # calibrate on a few rows, then size the sample to ~args.cpu_seconds of work
+    rows_all = w.batch * w.d_inner
+    rng = np.random.default_rng(0)
+    n = 32
+    while True:
+        rows = np.sort(rng.choice(rows_all, size=min(n, rows_all), replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                        delta_bias=p["delta_bias"], rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= args.cpu_seconds or n >= rows_all:
+            break
+        n = min(rows_all, max(n * 2, int(n * args.cpu_seconds / max(dt, 1e-3) * 1.05)))
+    elems = len(rows) * w.seqlen
+    log(f"cpu oracle: {len(rows)} rows x {w.seqlen} steps in {dt:.1f} s on {threads} threads")
+    return dict(value=round(elems / dt, 1), unit="elements/s", cores=threads, kind="oracle",
+                sample=f"{len(rows)} of {rows_all} (b,d) rows of {w.name}, all {w.seqlen} steps, "
+                       f"{dt:.1f} s wall")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (each box has "
+              "one MI355X; see DESIGN.md for how the scan would shard)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from selective_state_space_36_amd import ops
+    from selective_state_space_36_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    ops.lib()
+
+    w, p, ms_step, ms_kernel, ok, maxerr = bench_prefill(args, torch, np, ops, wl)
+    elems = w.elements
+    value = elems / (ms_step * 1e-3)
+    nbytes = prefill_bytes(w)
+    slots = elems * (w.d_state * SLOTS_PER_UPDATE +
+                     (SLOTS_PER_ELEMENT_GATED if w.gate else SLOTS_PER_ELEMENT_PLAIN))
+    achieved_slots = slots / (ms_kernel * 1e-3)
+    hbm_gbps = nbytes / (ms_kernel * 1e-3) / 1e9
+    result = {
+        "metric": "selective-scan fwd elements/s (B*L*D) + achieved HBM GB/s; decode step us",
+        "value": round(value, 1),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 io, f32 math and state" if w.io_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded, Mamba layer-shaped; no weights or datasets)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen,
+                   "d_inner": w.d_inner, "d_state": w.d_state, "gate": "silu(z)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": round(achieved_slots / 1e12, 3),
+                     "peak": round(PEAK_VALU_SLOTS / 1e12, 3), "unit": "T VALU-slot/s",
+                     "frac": round(achieved_slots / PEAK_VALU_SLOTS, 4),
+                     "traffic": measured_traffic(w.name),
+                     "kernel": "scan_kernel (prefill output pass)",
+                     "kernel_us": round(ms_kernel * 1e3, 2)},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(hbm_gbps, 1),
+                "peak_GBps": PEAK_HBM_GBPS, "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4)},
+        "parity_spot_check": {"ok": ok, "max_abs_err": maxerr},
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, torch, np, ops, wl)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, np, w, p)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

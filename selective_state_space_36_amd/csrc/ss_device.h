@@ -14,12 +14,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct F32 {
   using elem = float;
   static __device__ __forceinline__ float load(const elem* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ float widen(elem e) { return e; }
   static __device__ __forceinline__ elem from_float(float f) { return f; }
 };
 struct BF16 {
   using elem = uint16_t;
-  static __device__ __forceinline__ float load(const elem* p, int64_t i) {
-    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  static __device__ __forceinline__ float load(const elem* p, int64_t i) { return widen(p[i]); }
+  static __device__ __forceinline__ float widen(elem e) {
+    return __uint_as_float(static_cast<uint32_t>(e) << 16);
   }
   static __device__ __forceinline__ elem from_float(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));

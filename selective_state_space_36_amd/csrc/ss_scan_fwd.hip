@@ -105,48 +105,53 @@ struct ScanKernel {
       }
     }
 
-    // ---- B/C tile staging: NP states x kChunk steps, loaded as raw elements ----
+    // ---- B/C tile staging: NP states x kChunk steps ----
+    // Loads go to registers as raw elements at clamped (always valid) addresses and are only
+    // widened and masked when written to LDS, so that they stay in flight while the current tile
+    // is being processed.
     constexpr int kTilePairs = NP * kChunk;
     constexpr int kPerThread = (kTilePairs + kPrefillThreads - 1) / kPrefillThreads;
-    float tb[kPerThread], tc[kPerThread];
+    elem tb[kPerThread], tc[kPerThread];
     auto tile_load = [&](int64_t t0) {
 #pragma unroll
       for (int i = 0; i < kPerThread; ++i) {
         const int idx = threadIdx.x + i * kPrefillThreads;
         const int tau = idx / NP, n = idx - (idx / NP) * NP;
-        const int64_t t = t0 + tau;
-        const bool ok = idx < kTilePairs && t < t_end && n < a.d_state;
-        const int64_t off = (b * a.seqlen + t) * a.d_state + n;
-        tb[i] = ok ? IO::load(Bp, off) : 0.0f;
-        tc[i] = ok ? IO::load(Cp, off) : 0.0f;
+        const int64_t t = (t0 + tau < t_end) ? t0 + tau : t_end - 1;
+        const int nc = n < a.d_state ? n : a.d_state - 1;
+        const int64_t off = (b * a.seqlen + t) * a.d_state + nc;
+        tb[i] = Bp[off];
+        tc[i] = Cp[off];
       }
     };
-    auto tile_store = [&](int buf) {
+    auto tile_store = [&](int buf, int64_t t0) {
 #pragma unroll
       for (int i = 0; i < kPerThread; ++i) {
         const int idx = threadIdx.x + i * kPrefillThreads;
         if (idx < kTilePairs) {
           const int tau = idx / NP, n = idx - (idx / NP) * NP;
-          sm.bc[buf][n][tau] = make_float2(tb[i], tc[i]);
+          const bool ok = t0 + tau < t_end && n < a.d_state;
+          sm.bc[buf][n][tau] = ok ? make_float2(IO::widen(tb[i]), IO::widen(tc[i]))
+                                  : make_float2(0.0f, 0.0f);
         }
       }
     };
 
-    // ---- own-element inputs of a sub-chunk: step t0 + k of channel d ----
-    float own_u = 0.f, own_d = 0.f, own_z = 0.f;
-    auto own_load = [&](int64_t t0, float& ou, float& od, float& oz) {
-      const int64_t t = t0 + k;
-      const bool ok = chan_ok && t < t_end;
-      const int64_t off = (b * a.seqlen + t) * a.d_inner + d;
-      ou = ok ? IO::load(u, off) : 0.0f;
-      od = ok ? IO::load(dl, off) : 0.0f;
-      if (GATE && !SUMMARY) oz = ok ? IO::load(zz, off) : 0.0f;
+    // ---- own-element inputs of a sub-chunk: step t0 + k of channel d (raw, clamped) ----
+    const int64_t d_c = chan_ok ? d : a.d_inner - 1;
+    elem own_u, own_d, own_z{};
+    auto own_load = [&](int64_t t0, elem& ou, elem& od, elem& oz) {
+      const int64_t t = (t0 + k < t_end) ? t0 + k : t_end - 1;
+      const int64_t off = (b * a.seqlen + t) * a.d_inner + d_c;
+      ou = u[off];
+      od = dl[off];
+      if (GATE && !SUMMARY) oz = zz[off];
     };
 
     float dt_acc = 0.0f;  // summary pass: this lane's share of sum(dt) over the segment
 
     tile_load(t_begin);
-    tile_store(0);
+    tile_store(0, t_begin);
     own_load(t_begin, own_u, own_d, own_z);
     __syncthreads();
 
@@ -158,15 +163,16 @@ struct ScanKernel {
       for (int q = 0; q < kChunk / kSub; ++q) {
         const int64_t t0 = tcb + q * kSub;
         if (t0 < t_end) {
-          // prefetch the next sub-chunk's own inputs
-          float nu = 0.f, nd = 0.f, nz = 0.f;
-          if (t0 + kSub < t_end) own_load(t0 + kSub, nu, nd, nz);
+          // prefetch the next sub-chunk's own inputs (clamped: always a valid address)
+          elem nu, nd, nz{};
+          own_load(t0 + kSub, nu, nd, nz);
 
           const bool own_ok = chan_ok && (t0 + k) < t_end;
-          const float s = own_d + bias;
+          const float xu = IO::widen(own_u);
+          const float s = IO::widen(own_d) + bias;
           float dt = a.softplus ? softplus_f(s) : s;
-          dt = own_ok ? dt : 0.0f;  // steps past the end leave the state unchanged
-          const float du = dt * own_u;
+          dt = own_ok ? dt : 0.0f;                  // steps past the end leave h unchanged
+          const float du = own_ok ? dt * xu : 0.0f;
           if (SUMMARY) dt_acc += dt;
 
           sub_chunk(sm, buf, q * kSub, dt, du, A2, h, wave, r, k);
@@ -181,8 +187,8 @@ struct ScanKernel {
             wave_lds_sync();
             float y = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w))) +
                       (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
-            y = fmaf(dskip, own_u, y);
-            if (GATE) y *= silu_f(own_z);
+            y = fmaf(dskip, xu, y);
+            if (GATE) y *= silu_f(IO::widen(own_z));
             if (own_ok) outp[(b * a.seqlen + t0 + k) * a.d_inner + d] = IO::from_float(y);
           }
           own_u = nu;
@@ -190,7 +196,7 @@ struct ScanKernel {
           own_z = nz;
         }
       }
-      if (has_next) tile_store(buf ^ 1);
+      if (has_next) tile_store(buf ^ 1, tcb + kChunk);
       __syncthreads();
       buf ^= 1;
     }
@@ -220,36 +226,48 @@ struct ScanKernel {
     }
   }
 
-  // 16 recurrence steps of one sub-chunk.  toff: offset of the sub-chunk inside the B/C tile.
+  // One recurrence step (TAU of the sub-chunk) for this lane's states.  bcv holds the sub-chunk's
+  // (B, C) pairs for this lane's states, two steps per float4.
   template <int TAU>
-  static __device__ __forceinline__ void step(Smem& sm, int buf, int toff, float dt, float du,
-                                              const float (&A2)[NL], float (&h)[NL], int wave,
-                                              int r, int k) {
+  static __device__ __forceinline__ void step(Smem& sm, const float4 (&bcv)[NL][kSub / 2],
+                                              float dt, float du, const float (&A2)[NL],
+                                              float (&h)[NL], int wave, int r, int k) {
     const float dtb = row_bcast<TAU>(dt);
     const float dub = row_bcast<TAU>(du);
     float p = 0.0f;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const float2 bc = sm.bc[buf][k + 16 * j][toff + TAU];
+      const float4 v = bcv[j][TAU / 2];
+      const float bb = (TAU & 1) ? v.z : v.x;
+      const float cc = (TAU & 1) ? v.w : v.y;
       const float e = exp2_hw(dtb * A2[j]);
-      h[j] = fmaf(e, h[j], dub * bc.x);
-      p = (j == 0) ? bc.y * h[j] : fmaf(bc.y, h[j], p);
+      h[j] = fmaf(e, h[j], dub * bb);
+      p = (j == 0) ? cc * h[j] : fmaf(cc, h[j], p);
     }
     if (!SUMMARY) sm.p[wave][r * kPRow + TAU * kPTau + k] = p;
   }
 
   template <int... TAUS>
   static __device__ __forceinline__ void steps(std::integer_sequence<int, TAUS...>, Smem& sm,
-                                               int buf, int toff, float dt, float du,
-                                               const float (&A2)[NL], float (&h)[NL], int wave,
-                                               int r, int k) {
-    (step<TAUS>(sm, buf, toff, dt, du, A2, h, wave, r, k), ...);
+                                               const float4 (&bcv)[NL][kSub / 2], float dt,
+                                               float du, const float (&A2)[NL], float (&h)[NL],
+                                               int wave, int r, int k) {
+    (step<TAUS>(sm, bcv, dt, du, A2, h, wave, r, k), ...);
   }
 
+  // 16 recurrence steps of one sub-chunk.  toff: offset of the sub-chunk inside the B/C tile.
+  // The tile reads are issued together up front (16-byte reads, two steps each) so that the
+  // steps themselves are pure VALU work.
   static __device__ __forceinline__ void sub_chunk(Smem& sm, int buf, int toff, float dt,
                                                    float du, const float (&A2)[NL],
                                                    float (&h)[NL], int wave, int r, int k) {
-    steps(std::make_integer_sequence<int, kSub>{}, sm, buf, toff, dt, du, A2, h, wave, r, k);
+    float4 bcv[NL][kSub / 2];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+      for (int i = 0; i < kSub / 2; ++i)
+        bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k + 16 * j][toff + 2 * i]);
+    steps(std::make_integer_sequence<int, kSub>{}, sm, bcv, dt, du, A2, h, wave, r, k);
   }
 };
 

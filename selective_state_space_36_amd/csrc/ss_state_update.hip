@@ -6,11 +6,13 @@
 // (Mamba reading guide, "Perguntas": generation keeps only a fixed d_inner x d_state state per
 // layer and costs O(1) per token; "Método" for the recurrence.)
 //
-// The step is bound by HBM: every state element is read once and written once, and the arithmetic
-// per element is a handful of operations.  Layout: each channel's d_state floats are split over
-// a power-of-two group of lanes, 4 consecutive states per lane, so that one wave reads and writes
-// one contiguous run of the state with 16-byte accesses.  The group reduces C . h with
-// cross-lane shuffles; its first lane finishes the element (skip, gate, store).
+// The step is bound by memory: every state element is read once and written once, with a
+// handful of operations each.  Layout: each channel's d_state floats are split over a
+// power-of-two group of lanes, 4 consecutive states per lane, so that a wave reads and writes one
+// contiguous run of the state with 16-byte accesses.  Each thread handles several such 4-state
+// items and issues all their loads before any arithmetic, to keep enough bytes in flight to cover
+// the memory latency.  The group reduces C . h with cross-lane shuffles; its first lane finishes
+// the element (skip, gate, store).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,12 +24,106 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-template <class IO, bool GATE, bool VEC4>
-__global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeArgs a) {
+template <class IO>
+struct Vec4In;  // four consecutive io elements
+template <>
+struct Vec4In<F32> {
+  using raw = float4;
+  static __device__ __forceinline__ raw load(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  static __device__ __forceinline__ float get(const raw& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+  }
+};
+template <>
+struct Vec4In<BF16> {
+  using raw = uint2;
+  static __device__ __forceinline__ raw load(const uint16_t* p) {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+  static __device__ __forceinline__ float get(const raw& v, int i) {
+    const uint32_t w = (i < 2) ? v.x : v.y;
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+
+// Vector path: d_state % 4 == 0, 16-byte aligned state and A, ITEMS 4-state items per thread.
+template <class IO, bool GATE, int ITEMS>
+__global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs a) {
+  using elem = typename IO::elem;
+  using V = Vec4In<IO>;
+  const int G = a.lanes_per_chan;
+  const int N = a.d_state;
+  const int64_t nch = a.batch * a.d_inner;
+  const elem* up = static_cast<const elem*>(a.u);
+  const elem* dp = static_cast<const elem*>(a.delta);
+  const elem* zp = static_cast<const elem*>(a.z);
+  const elem* Bp = static_cast<const elem*>(a.B);
+  const elem* Cp = static_cast<const elem*>(a.C);
+
+  int64_t ch[ITEMS];
+  int q[ITEMS];
+  bool act[ITEMS];
+  float4 hv[ITEMS], av[ITEMS];
+  typename V::raw bv[ITEMS], cv[ITEMS];
+  elem xr[ITEMS], dr[ITEMS], zr[ITEMS];
+  float bias[ITEMS], dsk[ITEMS];
+  // issue every load first
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int64_t item = (static_cast<int64_t>(blockIdx.x) * ITEMS + i) * kDecodeThreads +
+                         threadIdx.x;
+    ch[i] = item / G;
+    q[i] = static_cast<int>(item - ch[i] * G);
+    act[i] = ch[i] < nch && q[i] * 4 < N;
+    const int64_t c = ch[i] < nch ? ch[i] : nch - 1;  // clamped: always a valid address
+    const int n0 = (q[i] * 4 < N) ? q[i] * 4 : 0;
+    const int64_t b = c / a.d_inner, d = c - b * a.d_inner;
+    hv[i] = *reinterpret_cast<const float4*>(a.state + c * N + n0);
+    av[i] = *reinterpret_cast<const float4*>(a.A + d * N + n0);
+    bv[i] = V::load(Bp + b * N + n0);
+    cv[i] = V::load(Cp + b * N + n0);
+    xr[i] = up[c];
+    dr[i] = dp[c];
+    if (GATE) zr[i] = zp[c];
+    bias[i] = a.delta_bias ? a.delta_bias[d] : 0.0f;
+    dsk[i] = a.D ? a.D[d] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const float x = IO::widen(xr[i]);
+    const float s = IO::widen(dr[i]) + bias[i];
+    const float dt = a.softplus ? softplus_f(s) : s;
+    const float du = dt * x;
+    float hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+    const float aa[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hh[j] = fmaf(exp2_hw(dt * (aa[j] * kLog2e)), hh[j], du * V::get(bv[i], j));
+      p = fmaf(V::get(cv[i], j), hh[j], p);
+    }
+    if (act[i])
+      *reinterpret_cast<float4*>(a.state + ch[i] * N + q[i] * 4) =
+          make_float4(hh[0], hh[1], hh[2], hh[3]);
+    p = act[i] ? p : 0.0f;
+    for (int m = G >> 1; m >= 1; m >>= 1) p += __shfl_xor(p, m, G);
+    if (ch[i] < nch && q[i] == 0) {
+      float y = fmaf(dsk[i], x, p);
+      if (GATE) y *= silu_f(IO::widen(zr[i]));
+      static_cast<elem*>(a.out)[ch[i]] = IO::from_float(y);
+    }
+  }
+}
+
+// Generic path: any d_state in 1..64 and any alignment; one 4-state item per thread.
+template <class IO, bool GATE>
+__global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeArgs a) {
   using elem = typename IO::elem;
   const int G = a.lanes_per_chan;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kDecodeThreads + threadIdx.x;
-  const int64_t ch = gid / G;              // (b, d) row
+  const int64_t ch = gid / G;  // (b, d) row
   const int q = static_cast<int>(gid - ch * G);
   const bool active = ch < a.batch * a.d_inner;
   const int64_t b = active ? ch / a.d_inner : 0;
@@ -46,33 +142,17 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeArgs a) {
   const float du = dt * x;
   const elem* Bp = static_cast<const elem*>(a.B);
   const elem* Cp = static_cast<const elem*>(a.C);
-
   if (active && n0 < N) {
     float* st = a.state + ch * N + n0;
     const float* Ar = a.A + d * N + n0;
     const int64_t bc = b * N + n0;
-    if (VEC4) {
-      float4 hv = *reinterpret_cast<const float4*>(st);
-      const float4 av = *reinterpret_cast<const float4*>(Ar);
-      float hh[4] = {hv.x, hv.y, hv.z, hv.w};
-      const float aa[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = exp2_hw(dt * (aa[i] * kLog2e));
-        hh[i] = fmaf(e, hh[i], du * IO::load(Bp, bc + i));
-        p = fmaf(IO::load(Cp, bc + i), hh[i], p);
-      }
-      *reinterpret_cast<float4*>(st) = make_float4(hh[0], hh[1], hh[2], hh[3]);
-    } else {
-      for (int i = 0; i < 4 && n0 + i < N; ++i) {
-        const float e = exp2_hw(dt * (Ar[i] * kLog2e));
-        const float hn = fmaf(e, st[i], du * IO::load(Bp, bc + i));
-        st[i] = hn;
-        p = fmaf(IO::load(Cp, bc + i), hn, p);
-      }
+    for (int i = 0; i < 4 && n0 + i < N; ++i) {
+      const float e = exp2_hw(dt * (Ar[i] * kLog2e));
+      const float hn = fmaf(e, st[i], du * IO::load(Bp, bc + i));
+      st[i] = hn;
+      p = fmaf(IO::load(Cp, bc + i), hn, p);
     }
   }
-  // reduce the partial dot products over the channel's lane group (G is a power of two <= 16)
   for (int m = G >> 1; m >= 1; m >>= 1) p += __shfl_xor(p, m, G);
   if (active && q == 0) {
     float y = p + (a.D ? a.D[d] : 0.0f) * x;
@@ -81,14 +161,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
+constexpr int kItems = 4;
+
 template <class IO, bool GATE>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t lanes = a.batch * a.d_inner * a.lanes_per_chan;
-  const dim3 grid(static_cast<unsigned>((lanes + kDecodeThreads - 1) / kDecodeThreads));
-  if (a.vec4)
-    hipLaunchKernelGGL((decode_kernel<IO, GATE, true>), grid, dim3(kDecodeThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<IO, GATE, false>), grid, dim3(kDecodeThreads), 0, stream, a);
+  if (a.vec4) {
+    const int64_t per_block = int64_t(kDecodeThreads) * kItems;
+    const dim3 grid(static_cast<unsigned>((lanes + per_block - 1) / per_block));
+    hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, kItems>), grid, dim3(kDecodeThreads), 0,
+                       stream, a);
+  } else {
+    const dim3 grid(static_cast<unsigned>((lanes + kDecodeThreads - 1) / kDecodeThreads));
+    hipLaunchKernelGGL((decode_generic_kernel<IO, GATE>), grid, dim3(kDecodeThreads), 0, stream,
+                       a);
+  }
   return hipGetLastError();
 }
 

@@ -68,6 +68,25 @@ def test_decode_small(d_state):
     _decode_steps(d, 6)
 
 
+def test_decode_unaligned_state_uses_generic_path():
+    """A state buffer that is only 4-byte aligned takes the scalar path; same results."""
+    w = wl.WORKLOADS[4]
+    d = wl.make_decode(w, steps=3, batch=2, d_inner=24)
+    flat = torch.empty(2 * 24 * 16 + 1, dtype=torch.float32, device="cuda")
+    st = flat[1:].view(2, 24, 16)
+    st.copy_(torch.from_numpy(d["state"]))
+    st_ref = d["state"].astype(np.float64)
+    for s in range(3):
+        out = ops().state_update(st, dev(d["u"][s]), dev(d["delta"][s]), dev(d["A"]),
+                                 dev(d["B"][s]), dev(d["C"][s]), D=dev(d["D"]), z=dev(d["z"][s]),
+                                 delta_bias=dev(d["delta_bias"]))
+        ref = oracle.state_update(st_ref, d["u"][s], d["delta"][s], d["A"], d["B"][s], d["C"][s],
+                                  D=d["D"], z=d["z"][s], delta_bias=d["delta_bias"])
+        check_close(host(out), ref, TOL["bf16"], f"step {s}")
+    torch.cuda.synchronize()
+    check_close(host(st), st_ref, 1e-4, "final state")
+
+
 def test_decode_fp32_no_gate():
     rng = np.random.default_rng(5)
     batch, d_inner, N, steps = 4, 33, 16, 5

@@ -144,8 +144,8 @@ def test_zero_step_is_exact_skip():
 
 def test_softplus_off():
     p, _ = small(0, 2, 90, 20, seed=23)
-    p["delta"] = np.abs(p["delta"]) * np.float32(0.1)
-    g, gh, r, rh = run_case(p, gate=False, softplus=False)
+    p["delta"] = np.abs(p["delta"]) * np.float32(0.1)   # dt used as given: non-negative
+    g, gh, r, rh = run_case(p, gate=False, softplus=False, bias=False)
     check_close(g, r, TOL["f32"], "out")
     check_close(gh, rh, TOL["f32"], "h_last")
 
@@ -195,7 +195,7 @@ def test_empty_and_degenerate_sizes():
 
 def test_invalid_arguments_raise():
     o = ops()
-    p, _ = small(1, 1, 8, 16, seed=37)
+    p, _ = small(1, 1, 512, 16, seed=37)   # long enough for a 4-way time split
     u, d, A, B, C = dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"])
     with pytest.raises(o.SSError) as e:
         o.scan_fwd(u, d, A, B, C, out=u)            # out aliases u
