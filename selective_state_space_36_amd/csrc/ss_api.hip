@@ -9,7 +9,7 @@
 
 #include <algorithm>
 
-#include "../../include/ss_scan.h"
+#include "ss_scan.h"
 #include "ss_launch.h"
 
 namespace {
@@ -188,6 +188,9 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
   a.d_state = static_cast<int32_t>(d_state);
   a.nseg = nseg;
   a.softplus = delta_softplus ? 1 : 0;
+  // 16-byte tile accesses need whole 16-channel blocks and 16-byte aligned rows
+  a.vec_io = (d_inner % ss::kChanPerWG == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
+              aligned(delta, 16) && (!z || aligned(z, 16)) && aligned(out, 16)) ? 1 : 0;
   if (nseg > 1) {
     uintptr_t base = (reinterpret_cast<uintptr_t>(workspace) + 255) & ~uintptr_t(255);
     a.seg_h = reinterpret_cast<float*>(base);

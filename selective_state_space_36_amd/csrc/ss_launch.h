@@ -9,10 +9,10 @@
 namespace ss {
 
 // Geometry of the prefill kernels: 16 lanes (one DPP row) per channel, 4 channels per wave,
-// 4 waves (16 channels) per workgroup, time processed in 16-step sub-chunks and 32-step B/C tiles.
+// 4 waves (16 channels) per workgroup, time processed in 16-step chunks.
 constexpr int kPrefillThreads = 256;
 constexpr int kChanPerWG = 16;
-constexpr int kChunk = 32;
+constexpr int kChunk = 16;
 
 struct ScanArgs {
   const void* u;
@@ -35,6 +35,7 @@ struct ScanArgs {
   int32_t d_state;
   int32_t nseg;
   int32_t softplus;
+  int32_t vec_io;      // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, out
 };
 
 struct DecodeArgs {
