@@ -68,6 +68,7 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
  *                      splits less (or not at all): the result is the same up to rounding,
  *                      only slower on shapes with few channels.
  * out and h_last must not overlap any input or each other (SS_ERR_INVALID_ARG).
+ * d_state outside 1..64, d_inner above 2^24 or seqlen above 2^31 - 1 -> SS_ERR_UNSUPPORTED.
  * batch == 0, seqlen == 0 or d_inner == 0 is a no-op returning SS_OK (with seqlen == 0 and
  * h_last given, h_last receives h0, or zeros).
  */

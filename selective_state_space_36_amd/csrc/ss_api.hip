@@ -117,6 +117,12 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
     return fail(SS_ERR_INVALID_ARG, "sizes overflow 64-bit byte offsets");
   elems /= 8;
   bc_elems /= 8;
+  // tiles of 16 steps are addressed with 32-bit byte offsets (16 * d_inner * 4 bytes < 2^31)
+  // and chunks are counted in 32 bits
+  if (d_inner > (int64_t(1) << 24))
+    return fail(SS_ERR_UNSUPPORTED, "d_inner=%lld above 16777216", (long long)d_inner);
+  if (seqlen > int64_t(0x7fffffff))
+    return fail(SS_ERR_UNSUPPORTED, "seqlen=%lld above 2147483647", (long long)seqlen);
   if (batch == 0 || d_inner == 0) return ok();
   if (seqlen == 0) {
     if (h_last) {

@@ -58,6 +58,40 @@ __device__ __forceinline__ float row_bcast(float x) {
       __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + SRC, 0xf, 0xf, false));
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (stride 0).  The hardware range check makes
+// loads at byte offsets >= bytes return 0 and drops stores there; offsets are per-lane bytes.
+// `base` must be uniform over the wavefront (the resource lives in scalar registers).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every range used here
+__device__ __forceinline__ rsrc_t make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+template <class T>
+__device__ __forceinline__ T buf_load(rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ uint4 buf_load<uint4>(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ uint16_t buf_load<uint16_t>(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ float buf_load<float>(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store(uint4 v, rsrc_t r, uint32_t off) {
+  using v4u = __attribute__((ext_vector_type(4))) unsigned int;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(uint16_t v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 // Make this wavefront's LDS writes visible to all of its lanes (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -17,7 +17,8 @@
 //   * Global memory is touched only by cooperative 16-byte loads and stores of whole tiles
 //     (u, delta, z and out as 16 steps x 16 channels; B and C as 16 steps x d_state), staged
 //     through LDS and double-buffered so that the next chunk's loads are in flight while the
-//     current chunk is computed.
+//     current chunk is computed.  The tiles are addressed as raw buffers sized to the valid
+//     steps, so the hardware range check handles the sequence tail.
 //   * The row's 16 partial sums C_t[n] h_t[n] go through a per-wave LDS tile; the owner lane of
 //     step t adds them up.  No atomics: results are bitwise reproducible.
 //   * Long sequences with few channels are cut into time segments.  A summary pass computes each
@@ -28,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "ss_device.h"
@@ -50,10 +52,9 @@ struct ScanKernel {
   static constexpr int ES = sizeof(elem);                    // io element bytes
   static constexpr int NTEN = SUMMARY ? 2 : (GATE ? 3 : 2);  // streamed inputs: u, delta, (z)
   static constexpr int PIECES = kChanPerWG * ES / 16;        // 16-byte pieces per tile row
-  static constexpr int IN_PIECES = NTEN * kT * PIECES;       // per chunk
-  static constexpr int OUT_PIECES = kT * PIECES;
-  static_assert(IN_PIECES <= kPrefillThreads, "one 16-byte input piece per thread");
-  static constexpr int BC_PER_THREAD = (kT * NP + kPrefillThreads - 1) / kPrefillThreads;
+  static_assert(kT * PIECES <= 64, "one 16-byte piece of a tile per lane of a wave");
+  static_assert(NTEN < kWaves, "a wave left over for the output tile");
+  static constexpr int BC_PER_THREAD = kT * NP / kPrefillThreads;
 
   struct alignas(16) Smem {
     float2 bc[2][NP][kTileStride];  // (B_t[n], C_t[n]) per chunk
@@ -64,12 +65,15 @@ struct ScanKernel {
 
   static __device__ __forceinline__ void run(const ScanArgs& a) {
     __shared__ Smem sm;
+    // Workgroup coordinates (all below 2^31: the host bounds the grid and d_inner); kept in
+    // scalar registers so that everything derived from them is scalar work.
     const int64_t ncb_total = a.batch * a.n_cblk;
     const int64_t lg = xcd_remap(blockIdx.x, a.n_wg);
-    const int64_t seg = lg / ncb_total;
+    const int64_t seg = __builtin_amdgcn_readfirstlane(static_cast<int>(lg / ncb_total));
     const int64_t cb = lg - seg * ncb_total;
-    const int64_t b = cb / a.n_cblk;
-    const int64_t d0 = (cb - b * a.n_cblk) * kChanPerWG;
+    const int64_t b = __builtin_amdgcn_readfirstlane(static_cast<int>(cb / a.n_cblk));
+    const int64_t d0 =
+        __builtin_amdgcn_readfirstlane(static_cast<int>((cb - b * a.n_cblk) * kChanPerWG));
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -81,13 +85,6 @@ struct ScanKernel {
     const int64_t row = b * a.d_inner + d;  // (b, d) row index
     const int64_t t_begin = seg * a.seg_len;
     const int64_t t_end = (t_begin + a.seg_len < a.seqlen) ? t_begin + a.seg_len : a.seqlen;
-
-    const elem* __restrict__ Bp = static_cast<const elem*>(a.B);
-    const elem* __restrict__ Cp = static_cast<const elem*>(a.C);
-    const elem* __restrict__ up = static_cast<const elem*>(a.u);
-    const elem* __restrict__ dp = static_cast<const elem*>(a.delta);
-    const elem* __restrict__ zp = static_cast<const elem*>(a.z);
-    elem* __restrict__ outp = static_cast<elem*>(a.out);
 
     // Per-lane constants: A scaled by log2(e) so that exp(dt A) = 2^(dt A2).
     float A2[NL], h[NL];
@@ -121,145 +118,107 @@ struct ScanKernel {
     }
 
     // ---- cooperative tile traffic ----
-    // Thread roles: B/C element(s) (tau, n) with consecutive threads on consecutive n (contiguous
-    // in memory); one 16-byte piece (tensor, step row, piece) of the u/delta/z tiles; one 16-byte
-    // piece (step row, piece) of the output tile.  Global loads for chunk i+1 are issued before
-    // chunk i is computed and written to LDS after it.  All loads are unconditional, at running
-    // pointers advanced by one chunk per call; only the last, partial chunk clamps its rows.
+    // Tiles are addressed through raw buffer resources whose base moves by one chunk per call and
+    // whose size covers only the chunk's valid steps: loads past the end of the sequence return 0
+    // and stores past it are dropped by the hardware range check.  Each thread's byte offset
+    // inside a tile is therefore fixed for the whole loop, and no load or store needs a mask or an
+    // address update of its own.
+    // Roles: every thread loads element(s) (tau, n) of the B and C tiles, consecutive threads on
+    // consecutive n (contiguous in memory); wave w < NTEN loads tile w of (u, delta, z), one
+    // 16-byte piece (step row, piece) per lane; wave NTEN stores the output tile.  Global loads for
+    // chunk i+1 are issued before chunk i is computed and written to LDS after it.
     const int64_t D = a.d_inner, N = a.d_state;
     const int64_t row0 = b * a.seqlen + t_begin;  // (b, t_begin) row of u/delta/z/out, B/C
-    const int in_ten_raw = tid / (kT * PIECES);
-    const int in_ten = in_ten_raw < NTEN ? in_ten_raw : NTEN - 1;
-    const int in_row = (tid / PIECES) % kT;
-    const int in_pc = tid % PIECES;
-    const int64_t in_col = d0 + in_pc * (16 / ES);  // first channel of this thread's piece
-    // a select, not an array of pointers: keeps the loads in the global address space
-    const elem* __restrict__ in_src = in_ten == 0 ? up : (in_ten == 1 ? dp : zp);
-    const elem* in_ld = in_src + (row0 + in_row) * D + in_col;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int tl_row = lane / PIECES, tl_pc = lane % PIECES;  // piece of a u/delta/z/out tile
+    const bool tl_on = lane < kT * PIECES;
+    const uint32_t tl_off =
+        tl_on ? static_cast<uint32_t>((tl_row * D + tl_pc * (16 / ES)) * ES) : kOffNone;
+    const char* in_base = static_cast<const char*>(wave_u == 0 ? a.u : (wave_u == 1 ? a.delta
+                                                                                     : a.z));
+    const int64_t io_chunk_bytes = kT * D * ES;
+    const int64_t io_off0 = (row0 * D + d0) * ES;  // byte offset of chunk 0's tiles
     int bc_tau[BC_PER_THREAD], bc_n[BC_PER_THREAD];
-    bool bc_ok[BC_PER_THREAD];
-    const elem* b_ld[BC_PER_THREAD];
-    const elem* c_ld[BC_PER_THREAD];
+    uint32_t bc_off[BC_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < BC_PER_THREAD; ++i) {
-      const int idx = tid + i * kPrefillThreads;
+      const int idx = tid + i * kPrefillThreads;  // < kT * NP
       bc_tau[i] = idx / NP;
       bc_n[i] = idx - bc_tau[i] * NP;
-      bc_ok[i] = idx < kT * NP && bc_n[i] < N;
-      const int64_t nc = bc_n[i] < N ? bc_n[i] : N - 1;
-      const int64_t tau = bc_tau[i] < kT ? bc_tau[i] : kT - 1;
-      b_ld[i] = Bp + (row0 + tau) * N + nc;
-      c_ld[i] = Cp + (row0 + tau) * N + nc;
+      bc_off[i] = bc_n[i] < N ? static_cast<uint32_t>((bc_tau[i] * N + bc_n[i]) * ES) : kOffNone;
     }
-    const int orow = tid / PIECES, opc = tid % PIECES;
-    const int64_t out_col = d0 + opc * (16 / ES);
-    elem* out_st = outp + (row0 + orow) * D + out_col;
-    const int64_t nchunks = (t_end - t_begin + kT - 1) / kT;
-    const bool partial = (t_end - t_begin) % kT != 0;  // the last chunk is cut short
+    static_assert(BC_PER_THREAD * kPrefillThreads == kT * NP, "B/C tile split over threads");
+    int ncols = static_cast<int>(D - (d0 + tl_pc * (16 / ES)));  // valid channels of the piece
+    ncols = ncols < 0 ? 0 : (ncols > 16 / ES ? 16 / ES : ncols);
+    // chunk counters are 32-bit (scalar compares; the host bounds seqlen below 2^31)
+    const int nchunks = static_cast<int>((t_end - t_begin + kT - 1) / kT);
 
     struct Pre {
       elem rb[BC_PER_THREAD], rc[BC_PER_THREAD];
       uint4 rin;
     } pre;
 
-    auto load_piece = [&](const elem* src) -> uint4 {
-      if (VEC) return *reinterpret_cast<const uint4*>(src);  // whole aligned block (host-checked)
-      elem tmp[16 / ES];
-#pragma unroll
-      for (int e = 0; e < 16 / ES; ++e) tmp[e] = src[in_col + e < D ? e : D - 1 - in_col];
-      return *reinterpret_cast<const uint4*>(tmp);
-    };
     // valid steps of chunk ci (kT except for a partial last chunk); uniform over the workgroup
-    const int last_valid = static_cast<int>(t_end - t_begin - (nchunks - 1) * kT);
-    auto nvalid_of = [&](int64_t ci) { return ci == nchunks - 1 ? last_valid : kT; };
-
-    auto load_chunk = [&](int64_t ci) {
-      // Rows past the end of the sequence re-read the last valid row (their values are masked
-      // when staged).  Only pointers are adjusted inside the (uniform) branch; the loads follow
-      // the join, so no wait is forced there.
-      const elem* pb[BC_PER_THREAD];
-      const elem* pc[BC_PER_THREAD];
-      const elem* pin = in_ld;
-#pragma unroll
-      for (int i = 0; i < BC_PER_THREAD; ++i) {
-        pb[i] = b_ld[i];
-        pc[i] = c_ld[i];
-      }
-      if (partial && ci == nchunks - 1) {
-        const int vr = last_valid - 1;
-#pragma unroll
-        for (int i = 0; i < BC_PER_THREAD; ++i) {
-          const int over = bc_tau[i] < kT ? max(bc_tau[i] - vr, 0) : 0;
-          pb[i] -= over * N;
-          pc[i] -= over * N;
-        }
-        pin -= static_cast<int64_t>(max(in_row - vr, 0)) * D;
-      }
-#pragma unroll
-      for (int i = 0; i < BC_PER_THREAD; ++i) {
-        pre.rb[i] = *pb[i];
-        pre.rc[i] = *pc[i];
-        b_ld[i] += kT * N;
-        c_ld[i] += kT * N;
-      }
-      pre.rin = load_piece(pin);
-      in_ld += kT * D;
+    const int last_valid = static_cast<int>(t_end - t_begin - int64_t(nchunks - 1) * kT);
+    auto nvalid_of = [&](int ci) { return ci == nchunks - 1 ? last_valid : kT; };
+    // The range ends with the last valid row: channels past d_inner in that row (reached only by
+    // the element path) read 0 and are not written.
+    auto io_buf = [&](const void* base, int ci) {
+      return make_buf(static_cast<const char*>(base) + io_off0 + int64_t(ci) * io_chunk_bytes,
+                      static_cast<uint32_t>((nvalid_of(ci) * D - d0) * ES));
     };
-    auto stage_chunk = [&](int buf, int64_t ci) {
-      const int nv = nvalid_of(ci);
+
+    auto load_chunk = [&](int ci) {
+      const int64_t bc_off0 = ((row0 + int64_t(ci) * kT) * N) * ES;
+      const uint32_t bc_bytes = static_cast<uint32_t>(nvalid_of(ci) * N * ES);
+      const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + bc_off0, bc_bytes);
+      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + bc_off0, bc_bytes);
 #pragma unroll
       for (int i = 0; i < BC_PER_THREAD; ++i) {
-        if (bc_tau[i] < kT) {
-          float2 v = make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
-          if (NL * 16 != 16 || nv != kT) {  // masks needed only for padded states / a cut chunk
-            if (!(bc_ok[i] && bc_tau[i] < nv)) v = make_float2(0.0f, 0.0f);
-          } else if (!bc_ok[i]) {
-            v = make_float2(0.0f, 0.0f);
-          }
-          sm.bc[buf][bc_n[i]][bc_tau[i]] = v;
+        pre.rb[i] = buf_load<elem>(rb, bc_off[i]);
+        pre.rc[i] = buf_load<elem>(rc, bc_off[i]);
+      }
+      if (wave_u < NTEN) {  // uniform
+        const rsrc_t ri = io_buf(in_base, ci);
+        if (VEC) {
+          pre.rin = buf_load<uint4>(ri, tl_off);
+        } else {
+          // element loads; channels past d_inner read the next row or 0 and are never used
+          elem tmp[16 / ES];
+#pragma unroll
+          for (int e = 0; e < 16 / ES; ++e) tmp[e] = buf_load<elem>(ri, tl_off + e * ES);
+          pre.rin = *reinterpret_cast<const uint4*>(tmp);
         }
       }
-      if (tid < IN_PIECES) {
-        uint4 v = pre.rin;
-        if (nv != kT && in_row >= nv) v = uint4{0, 0, 0, 0};
-        if (!VEC) {
+    };
+    auto stage_chunk = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < BC_PER_THREAD; ++i)
+        sm.bc[buf][bc_n[i]][bc_tau[i]] = make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
+      if (wave_u < NTEN && tl_on) sm.in[buf][wave_u][tl_row][tl_pc] = pre.rin;
+    };
+    // The data registers of the last output store are kept live (hold_store) until the next
+    // chunk's compute is done: otherwise the allocator reuses them at once and the write to them
+    // has to wait for the store to complete.
+    uint4 st_val{0, 0, 0, 0};
+    auto hold_store = [&]() {
+      if (VEC && !SUMMARY)
+        asm volatile("" ::"v"(st_val.x), "v"(st_val.y), "v"(st_val.z), "v"(st_val.w));
+    };
+    auto store_out = [&](int buf, int ci) {
+      if (!SUMMARY && wave_u == NTEN && tl_on) {
+        const rsrc_t ro = io_buf(a.out, ci);
+        const uint4 v = sm.out[buf][tl_row][tl_pc];
+        if (VEC) {
+          st_val = v;
+          buf_store(v, ro, tl_off);
+        } else {
           elem tmp[16 / ES];
           *reinterpret_cast<uint4*>(tmp) = v;
 #pragma unroll
           for (int e = 0; e < 16 / ES; ++e)
-            if (in_col + e >= D) tmp[e] = elem{};
-          v = *reinterpret_cast<const uint4*>(tmp);
+            if (e < ncols) buf_store(tmp[e], ro, tl_off + e * ES);
         }
-        sm.in[buf][in_ten][in_row][in_pc] = v;
-      }
-    };
-    // The registers of the last output store are kept live (hold_store) until the next chunk's
-    // compute is done: otherwise the allocator reuses them at once and the write to them has to
-    // wait for the store to complete.
-    uint4 st_val{0, 0, 0, 0};
-    uint64_t st_ptr = 0;
-    auto hold_store = [&]() {
-      if (VEC && !SUMMARY)
-        asm volatile("" ::"v"(st_val.x), "v"(st_val.y), "v"(st_val.z), "v"(st_val.w),
-                     "v"(st_ptr));
-    };
-    auto store_out = [&](int buf, int64_t ci) {
-      if (!SUMMARY && tid < OUT_PIECES) {
-        if (orow < nvalid_of(ci)) {
-          const uint4 v = sm.out[buf][orow][opc];
-          if (VEC) {
-            st_val = v;
-            st_ptr = reinterpret_cast<uint64_t>(out_st);
-            *reinterpret_cast<uint4*>(out_st) = v;
-          } else {
-            elem tmp[16 / ES];
-            *reinterpret_cast<uint4*>(tmp) = v;
-#pragma unroll
-            for (int e = 0; e < 16 / ES; ++e)
-              if (out_col + e < D) out_st[e] = tmp[e];
-          }
-        }
-        out_st += kT * D;
       }
     };
     auto own_in = [&](int buf, int ten) -> float {
@@ -270,27 +229,16 @@ struct ScanKernel {
     float dt_acc = 0.0f;  // summary pass: this lane's share of sum(dt) over the segment
 
     load_chunk(0);
-    stage_chunk(0, 0);
+    stage_chunk(0);
     __syncthreads();
 
-    // Waves of different workgroups sharing a SIMD would otherwise be served oldest first, so
-    // some finish early and the SIMD runs the end of the kernel with few waves.  A wave lowers
-    // its issue priority as it progresses, which keeps the waves of a SIMD close together.
-    int prio = 3;
-    __builtin_amdgcn_s_setprio(3);
-    const int64_t q1 = nchunks / 4, q2 = nchunks / 2, q3 = (3 * nchunks) / 4;
-
-    int buf = 0;
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
+    // One chunk: issue the loads of the next chunk, compute this one from LDS buffer BUF, stage
+    // the next chunk into the other buffer, then store this chunk's output tile.  BUF is a
+    // compile-time constant so that every LDS address is a register plus an immediate.
+    auto chunk = [&](int ci, auto bufc) {
+      constexpr int buf = decltype(bufc)::value;
       const bool has_next = ci + 1 < nchunks;
       if (has_next) load_chunk(ci + 1);
-
-      if (ci == q1 || ci == q2 || ci == q3) {  // uniform
-        --prio;
-        if (prio == 2) __builtin_amdgcn_s_setprio(2);
-        else if (prio == 1) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
-      }
 
       const bool own_ok = chan_ok && k < nvalid_of(ci);
       const float xu = own_in(buf, 0);
@@ -306,21 +254,45 @@ struct ScanKernel {
         wave_lds_sync();
         const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
         const float4 q0 = *reinterpret_cast<const float4*>(pr + 0);
-        const float4 q1v = *reinterpret_cast<const float4*>(pr + 4);
-        const float4 q2v = *reinterpret_cast<const float4*>(pr + 8);
-        const float4 q3v = *reinterpret_cast<const float4*>(pr + 12);
+        const float4 q1 = *reinterpret_cast<const float4*>(pr + 4);
+        const float4 q2 = *reinterpret_cast<const float4*>(pr + 8);
+        const float4 q3 = *reinterpret_cast<const float4*>(pr + 12);
         wave_lds_sync();
-        float y = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1v.x + q1v.y) + (q1v.z + q1v.w))) +
-                  (((q2v.x + q2v.y) + (q2v.z + q2v.w)) + ((q3v.x + q3v.y) + (q3v.z + q3v.w)));
+        float y = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w))) +
+                  (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
         y = fmaf(dskip, xu, y);
         if (GATE) y *= silu_f(own_in(buf, 2));
         reinterpret_cast<elem*>(&sm.out[buf][k][0])[cl] = IO::from_float(y);
       }
       hold_store();
-      if (has_next) stage_chunk(buf ^ 1, ci + 1);
+      if (has_next) stage_chunk(buf ^ 1);
       __syncthreads();
       store_out(buf, ci);
-      buf ^= 1;
+    };
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+
+    // Waves of different workgroups sharing a SIMD would otherwise be served oldest first, so
+    // some finish early and the SIMD runs the end of the kernel with few waves.  A wave lowers
+    // its issue priority by one at each quarter of its chunks, which keeps the waves of a SIMD
+    // close together.  Quarter boundaries are even, so chunk pairs always start on buffer 0.
+    int ci = 0;
+    for (int qi = 0; qi < 4; ++qi) {
+      switch (qi) {
+        case 0: __builtin_amdgcn_s_setprio(3); break;
+        case 1: __builtin_amdgcn_s_setprio(2); break;
+        case 2: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
+      }
+      const int c_end = qi == 3 ? nchunks : (((qi + 1) * nchunks) / 4) & ~1;
+      for (; ci + 1 < c_end; ci += 2) {
+        chunk(ci, Buf0{});
+        chunk(ci + 1, Buf1{});
+      }
+      if (ci < c_end) {  // odd chunk count: the last chunk, on buffer 0
+        chunk(ci, Buf0{});
+        ++ci;
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 

@@ -71,6 +71,11 @@ def test_scan_argument_errors_before_launch(lib):
     assert b"overlaps" in lib.ss_last_error()
     assert _scan(lib, u=FAKE + 1) == ops.SS_ERR_UNSUPPORTED         # misaligned bf16
     assert _scan(lib, L=1 << 62, d=1 << 10) == ops.SS_ERR_INVALID_ARG  # overflow
+    # 32-bit tile offsets and chunk counters bound d_inner and seqlen
+    assert _scan(lib, d=(1 << 24) + 16) == ops.SS_ERR_UNSUPPORTED
+    assert b"d_inner" in lib.ss_last_error()
+    assert _scan(lib, L=1 << 31) == ops.SS_ERR_UNSUPPORTED
+    assert b"seqlen" in lib.ss_last_error()
     # empty problems are no-ops that succeed without any launch
     assert _scan(lib, batch=0) == ops.SS_OK
     assert _scan(lib, d=0) == ops.SS_OK
