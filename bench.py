@@ -205,6 +205,53 @@ def bench_decode(args, torch, np, ops, wl):
     us_kernel = sum(per) / len(per)
     log(f"decode {us_e2e:.2f} us/step end-to-end, kernel {us_kernel:.2f} us (median "
         f"{per[len(per) // 2]:.2f})")
+
+    # the same launches captured once into a HIP graph and replayed (launch gaps shrink)
+    gsteps = min(steps, 200)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        for s in range(gsteps):  # warm the capture stream once outside the graph
+            ops.state_update(st, u[s], dl[s], A, B[s], C[s], D=D, z=z[s], delta_bias=db,
+                             out=out[s], stream=cap)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for s in range(gsteps):
+                ops.state_update(st, u[s], dl[s], A, B[s], C[s], D=D, z=z[s], delta_bias=db,
+                                 out=out[s], stream=cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // gsteps)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_graph = e0.elapsed_time(e1) * 1e3 / (reps * gsteps)
+    del graph
+
+    # cold: 8 state buffers used in turn (8 x 41.9 MB > the 256 MB Infinity Cache), as 8 layers
+    # of a model would, so every step streams its state from HBM
+    nbuf = 8
+    states = [st.clone() for _ in range(nbuf)]
+
+    def one_cold(s):
+        ops.state_update(states[s % nbuf], u[s], dl[s], A, B[s], C[s], D=D, z=z[s],
+                         delta_bias=db, out=out[s], stream=stream)
+
+    for s in range(min(2 * nbuf, steps)):
+        one_cold(s)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(steps):
+        one_cold(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_cold = e0.elapsed_time(e1) * 1e3 / steps
+    del states
+    log(f"decode graph {us_graph:.2f} us/step, cold (8 rotating states) {us_cold:.2f} us/step")
     nb = decode_bytes_per_step(w)
     return dict(
         workload=w.name, batch=w.batch, d_inner=w.d_inner, d_state=w.d_state, steps=steps,
@@ -215,7 +262,12 @@ def bench_decode(args, torch, np, ops, wl):
                       peak=PEAK_HBM_GBPS, unit="GB/s",
                       frac=round(nb / (us_kernel * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                       traffic=measured_traffic(w.name)),
-        note="state (41.9 MB) is resident across steps and fits the 256 MB Infinity Cache")
+        us_per_step_graph=round(us_graph, 3),
+        cold=dict(us_per_step_end_to_end=round(us_cold, 3), state_buffers=nbuf,
+                  achieved_GBps=round(nb / (us_cold * 1e-6) / 1e9, 1),
+                  frac=round(nb / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)),
+        note="warm: one state (41.9 MB) resident across steps, which fits the 256 MB Infinity "
+             "Cache; cold: 8 states used in turn")
 
 
 def cpu_baseline(args, np, w, p):

@@ -46,11 +46,21 @@ extern "C" {
 typedef enum {
   SS_OK = 0,
   SS_ERR_INVALID_ARG = 1, /* NULL required pointer, negative or inconsistent size, aliasing */
-  SS_ERR_UNSUPPORTED = 2, /* d_state outside 1..64, unknown dtype, misaligned element type */
+  SS_ERR_UNSUPPORTED = 2, /* d_state outside 1..64, unknown dtype or flag, misaligned element */
   SS_ERR_HIP = 3          /* the HIP runtime reported an error while launching */
 } ss_status;
 
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/*
+ * Option bits of the _ex entry points (any other bit -> SS_ERR_UNSUPPORTED).
+ *   SS_FLAG_ZOH_EXACT: the input term uses the exact zero-order-hold discretisation of the
+ *     continuous system (reading guide, "Método": B_bar = (dt A)^-1 (exp(dt A) - I) dt B, which
+ *     for the diagonal A is B_bar[n] = (exp(dt A[d,n]) - 1) / A[d,n] * B[n], and dt * B[n] where
+ *     A[d,n] == 0) in place of the first-order dt * B[n] of the default (aivaro.ru, section 3).
+ *     A_bar = exp(dt A) either way.  It costs a few more operations per state update.
+ */
+enum { SS_FLAG_ZOH_EXACT = 1 };
 
 /*
  * Prefill: the whole sequence in one call.
@@ -83,18 +93,19 @@ size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inne
                                    int64_t d_state, ss_dtype dtype);
 
 /*
- * Prefill with an explicit time split.  nseg > 0 forces the sequence to be cut into that many
- * segments (each scanned from a carried state; the carries come from a first summary pass over
- * the segments, the blockwise associative decomposition of the recurrence); nseg == 0 chooses
- * automatically.  Used to check that the result does not depend on the split.  The workspace
- * must hold ss_scan_fwd_ex_workspace_bytes(..., nseg) bytes.
+ * Prefill with an explicit time split and options.  nseg > 0 forces the sequence to be cut into
+ * that many segments (each scanned from a carried state; the carries come from a first summary
+ * pass over the segments, the blockwise associative decomposition of the recurrence); nseg == 0
+ * chooses automatically.  Used to check that the result does not depend on the split.  With
+ * nseg > 1 the workspace must hold ss_scan_fwd_ex_workspace_bytes(..., nseg) bytes
+ * (SS_ERR_INVALID_ARG otherwise).  flags: SS_FLAG_* bits (0 = the ss_scan_fwd operation).
  */
 ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z, const float* delta_bias,
                          int delta_softplus, const float* h0, float* h_last, void* out,
                          int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                          ss_dtype dtype, void* workspace, size_t workspace_bytes, int32_t nseg,
-                         void* stream);
+                         uint32_t flags, void* stream);
 
 size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                       int64_t d_state, ss_dtype dtype, int32_t nseg);
@@ -114,6 +125,13 @@ ss_status ss_state_update(float* state, const void* u, const void* delta, const 
                           const float* delta_bias, int delta_softplus, void* out,
                           int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
                           void* stream);
+
+/* Decode with options: flags are SS_FLAG_* bits (0 = the ss_state_update operation). */
+ss_status ss_state_update_ex(float* state, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, int delta_softplus, void* out,
+                             int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                             uint32_t flags, void* stream);
 
 /* Static description of a status code. */
 const char* ss_status_string(ss_status s);

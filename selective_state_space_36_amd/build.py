@@ -5,22 +5,25 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libssscan.so")
-SOURCES = ["ss_api.hip", "ss_scan_fwd.hip", "ss_state_update.hip"]
+SOURCES = ["ss_api.hip", "ss_scan_fwd.hip", "ss_scan_zoh.hip", "ss_state_update.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled (-packed-fp32-ops); the host pass warns that it
 # does not know the feature, which is harmless.
-FLAGS = [
-    "-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
+LINK_FLAGS = [f"--offload-arch={ARCH}", "-fPIC", "-shared"]
+NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -30,18 +33,30 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in res.stderr.splitlines() if NOISE not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared library."""
+    exe = hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[exe, *COMPILE_FLAGS, "-c", "-o", o, os.path.join(CSRC, s)]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([exe, *LINK_FLAGS, "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -95,14 +95,21 @@ ss_status check_dtype(ss_dtype dt, int64_t* esize) {
   return fail(SS_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
 }
 
+ss_status check_flags(uint32_t flags) {
+  if (flags & ~uint32_t(SS_FLAG_ZOH_EXACT))
+    return fail(SS_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags & ~uint32_t(SS_FLAG_ZOH_EXACT));
+  return SS_OK;
+}
+
 ss_status scan_impl(const void* u, const void* delta, const float* A, const void* B,
                     const void* C, const float* D, const void* z, const float* delta_bias,
                     int delta_softplus, const float* h0, float* h_last, void* out, int64_t batch,
                     int64_t seqlen, int64_t d_inner, int64_t d_state, ss_dtype dtype,
                     void* workspace, size_t workspace_bytes, int32_t nseg_req, bool forced,
-                    void* stream) {
+                    uint32_t flags, void* stream) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
     return fail(SS_ERR_INVALID_ARG, "negative size (batch=%lld seqlen=%lld d_inner=%lld "
                 "d_state=%lld)", (long long)batch, (long long)seqlen, (long long)d_inner,
@@ -194,6 +201,7 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
   a.d_state = static_cast<int32_t>(d_state);
   a.nseg = nseg;
   a.softplus = delta_softplus ? 1 : 0;
+  a.zoh = (flags & SS_FLAG_ZOH_EXACT) ? 1 : 0;
   // 16-byte tile accesses need whole 16-channel blocks and 16-byte aligned rows
   a.vec_io = (d_inner % ss::kChanPerWG == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
               aligned(delta, 16) && (!z || aligned(z, 16)) && aligned(out, 16)) ? 1 : 0;
@@ -223,57 +231,14 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
   return ok();
 }
 
-}  // namespace
-
-extern "C" {
-
-ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
-                      const void* C, const float* D, const void* z, const float* delta_bias,
-                      int delta_softplus, const float* h0, float* h_last, void* out,
-                      int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                      ss_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
-                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, 0, false, stream);
-}
-
-size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
-                                   int64_t d_state, ss_dtype dtype) {
-  (void)dtype;
-  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
-  int64_t seg_len;
-  int32_t nseg;
-  segments(seqlen, auto_nseg(batch, seqlen, d_inner), &seg_len, &nseg);
-  return ws_bytes(batch, d_inner, d_state, nseg);
-}
-
-ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
-                         const void* C, const float* D, const void* z, const float* delta_bias,
-                         int delta_softplus, const float* h0, float* h_last, void* out,
-                         int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                         ss_dtype dtype, void* workspace, size_t workspace_bytes, int32_t nseg,
-                         void* stream) {
-  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
-                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, nseg, true,
-                   stream);
-}
-
-size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
-                                      int64_t d_state, ss_dtype dtype, int32_t nseg) {
-  (void)dtype;
-  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
-  int64_t seg_len;
-  int32_t n;
-  segments(seqlen, nseg > 0 ? nseg : auto_nseg(batch, seqlen, d_inner), &seg_len, &n);
-  return ws_bytes(batch, d_inner, d_state, n);
-}
-
-ss_status ss_state_update(float* state, const void* u, const void* delta, const float* A,
-                          const void* B, const void* C, const float* D, const void* z,
-                          const float* delta_bias, int delta_softplus, void* out,
-                          int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
-                          void* stream) {
+ss_status decode_impl(float* state, const void* u, const void* delta, const float* A,
+                      const void* B, const void* C, const float* D, const void* z,
+                      const float* delta_bias, int delta_softplus, void* out, int64_t batch,
+                      int64_t d_inner, int64_t d_state, ss_dtype dtype, uint32_t flags,
+                      void* stream) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (batch < 0 || d_inner < 0 || d_state < 0)
     return fail(SS_ERR_INVALID_ARG, "negative size");
   if (d_state < 1 || d_state > 64)
@@ -312,6 +277,7 @@ ss_status ss_state_update(float* state, const void* u, const void* delta, const 
   while (g * 4 < d_state) g <<= 1;
   a.lanes_per_chan = g;
   a.softplus = delta_softplus ? 1 : 0;
+  a.zoh = (flags & SS_FLAG_ZOH_EXACT) ? 1 : 0;
   const int64_t bc_align = dtype == SS_BF16 ? 8 : 16;  // four io elements of B and C
   a.vec4 = (d_state % 4 == 0 && aligned(state, 16) && aligned(A, 16) && aligned(B, bc_align) &&
             aligned(C, bc_align)) ? 1 : 0;
@@ -320,6 +286,69 @@ ss_status ss_state_update(float* state, const void* u, const void* delta, const 
   const hipError_t e = ss::launch_decode(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int delta_softplus, const float* h0, float* h_last, void* out,
+                      int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      ss_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, 0, false, 0,
+                   stream);
+}
+
+size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                   int64_t d_state, ss_dtype dtype) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
+  int64_t seg_len;
+  int32_t nseg;
+  segments(seqlen, auto_nseg(batch, seqlen, d_inner), &seg_len, &nseg);
+  return ws_bytes(batch, d_inner, d_state, nseg);
+}
+
+ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* delta_bias,
+                         int delta_softplus, const float* h0, float* h_last, void* out,
+                         int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                         ss_dtype dtype, void* workspace, size_t workspace_bytes, int32_t nseg,
+                         uint32_t flags, void* stream) {
+  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, nseg, true, flags,
+                   stream);
+}
+
+size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                      int64_t d_state, ss_dtype dtype, int32_t nseg) {
+  (void)dtype;
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
+  int64_t seg_len;
+  int32_t n;
+  segments(seqlen, nseg > 0 ? nseg : auto_nseg(batch, seqlen, d_inner), &seg_len, &n);
+  return ws_bytes(batch, d_inner, d_state, n);
+}
+
+ss_status ss_state_update(float* state, const void* u, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D, const void* z,
+                          const float* delta_bias, int delta_softplus, void* out,
+                          int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                          void* stream) {
+  return decode_impl(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, batch,
+                     d_inner, d_state, dtype, 0, stream);
+}
+
+ss_status ss_state_update_ex(float* state, const void* u, const void* delta, const float* A,
+                             const void* B, const void* C, const float* D, const void* z,
+                             const float* delta_bias, int delta_softplus, void* out,
+                             int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                             uint32_t flags, void* stream) {
+  return decode_impl(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, batch,
+                     d_inner, d_state, dtype, flags, stream);
 }
 
 const char* ss_status_string(ss_status s) {
@@ -334,6 +363,6 @@ const char* ss_status_string(ss_status s) {
 
 const char* ss_last_error(void) { return g_err; }
 
-int ss_version(void) { return 100; }
+int ss_version(void) { return 101; }
 
 }  // extern "C"

@@ -41,7 +41,25 @@ __device__ __forceinline__ float softplus_f(float s) {
   const float w = 1.0f + e;
   const float l = log2_hw(w) * kLn2;
   const float c = e - (w - 1.0f);
-  return fmaxf(s, 0.0f) + (l + c);
+  // max(s, 0) as a median (no NaN canonicalisation, one instruction)
+  return __builtin_amdgcn_fmed3f(s, 0.0f, __builtin_inff()) + (l + c);
+}
+
+// (2^y - 1) / y, given u = 2^y; it tends to ln 2 at y = 0.  This is the exact zero-order-hold
+// input gain in base 2: (exp(x) - 1) / x = (2^y - 1) / (y ln 2) for x = y ln 2.  For |y| < 1/2
+// it is the Taylor series sum_k ln2^(k+1) y^k / (k+1)! cut after y^7 (the rest is below
+// 1e-9 relative there), which avoids the cancellation in 2^y - 1; elsewhere (u - 1) / y, where
+// |u - 1| >= 0.29 keeps that difference accurate.  u == 0 (large negative y) gives -1 / y.
+__device__ __forceinline__ float zoh_gain(float u, float y) {
+  float p = 1.3215486660556053e-06f;
+  p = fmaf(p, y, 1.5252733646775596e-05f);
+  p = fmaf(p, y, 0.0001540352968731895f);
+  p = fmaf(p, y, 0.0013333557872101665f);
+  p = fmaf(p, y, 0.009618128649890423f);
+  p = fmaf(p, y, 0.05550410971045494f);
+  p = fmaf(p, y, 0.24022650718688965f);
+  p = fmaf(p, y, 0.6931471824645996f);
+  return fabsf(y) < 0.5f ? p : (u - 1.0f) * rcp_hw(y);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z}).

@@ -36,6 +36,7 @@ struct ScanArgs {
   int32_t nseg;
   int32_t softplus;
   int32_t vec_io;      // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, out
+  int32_t zoh;         // exact zero-order-hold input term instead of dt * B
 };
 
 struct DecodeArgs {
@@ -54,11 +55,13 @@ struct DecodeArgs {
   int32_t lanes_per_chan;  // power of two >= ceil(d_state / 4)
   int32_t softplus;
   int32_t vec4;            // d_state % 4 == 0 and 16-byte aligned state/A
+  int32_t zoh;             // exact zero-order-hold input term instead of dt * B
 };
 
 // Prefill passes.  `summary` selects the first pass of a time-split scan (segments 0..nseg-2,
 // local end states and dt sums into seg_h/seg_dt); otherwise the output pass over all segments.
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
+hipError_t launch_scan_zoh(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
 
 // Fill h_last with h0 (or zeros) when the sequence is empty.
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -1,412 +1,24 @@
-// ss_scan_fwd.hip -- gfx950 prefill kernels of the selective scan.
-//
-// What is computed (per batch row b, channel d, state n; Mamba reading guide, sections "Método"
-// and "O Mecanismo de Seleção (S6)"):
-//     dt_t = softplus(delta + bias),  h_t = exp(dt_t A) h_{t-1} + dt_t B_t u_t,
-//     y_t = C_t . h_t + D u_t,  out = y_t * silu(z_t).
-// The (batch, L, d_inner, d_state) state never leaves registers; only y reaches HBM (reading
-// guide, "Expansão de Estado Ciente de Hardware").
-//
-// Work layout (chosen for CDNA4, not taken from the pages' GPU design):
-//   * One channel = one 16-lane DPP row; lane k of the row owns states n = k, k+16, k+32, k+48.
-//     A wave holds 4 channels, a workgroup 16.  A layer like (4, 4096, 5120, 16) thus yields
-//     1280 workgroups = 5 per CU and 5 waves per SIMD, with no ragged last round.
-//   * Time runs in 16-step chunks.  Lane k also owns the element work (softplus, dt*u, skip,
-//     gate) of step k of each chunk; the per-step dt and dt*u reach the other lanes of the row
-//     through DPP row broadcasts that the compiler folds into the multiplies consuming them.
-//   * Global memory is touched only by cooperative 16-byte loads and stores of whole tiles
-//     (u, delta, z and out as 16 steps x 16 channels; B and C as 16 steps x d_state), staged
-//     through LDS and double-buffered so that the next chunk's loads are in flight while the
-//     current chunk is computed.  The tiles are addressed as raw buffers sized to the valid
-//     steps, so the hardware range check handles the sequence tail.
-//   * The row's 16 partial sums C_t[n] h_t[n] go through a per-wave LDS tile; the owner lane of
-//     step t adds them up.  No atomics: results are bitwise reproducible.
-//   * Long sequences with few channels are cut into time segments.  A summary pass computes each
-//     segment's end state from a zero start and the sum of its dt; the output pass then starts
-//     segment s from h0 carried through segments 0..s-1 with h <- exp(A sum dt) h + h_end, the
-//     blockwise form of the associative recurrence (reading guide: parallel associative scan;
-//     IBM explainer: blocks combined hierarchically).
+// ss_scan_fwd.hip -- prefill launches with the first-order input term dt B u (the default), the
+// dispatch to the exact zero-order-hold instances, and the empty-sequence state copy.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-#include <utility>
-
-#include "ss_device.h"
 #include "ss_launch.h"
+#include "ss_scan_kernel.h"
 
 namespace ss {
 namespace {
-
-constexpr int kWaves = kPrefillThreads / 64;
-constexpr int kT = kChunk;               // steps per chunk (= lanes per row)
-constexpr int kTileStride = kT + 2;      // float2 slots per state row of the B/C tile (padding)
-constexpr int kPRow = 336;               // floats per channel row of the partial tile (padding)
-constexpr int kPTau = 20;                // floats per step of the partial tile (padding)
-static_assert(kT == 16, "one chunk step per row lane");
-
-template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC>
-struct ScanKernel {
-  using elem = typename IO::elem;
-  static constexpr int NP = 16 * NL;                         // padded state count
-  static constexpr int ES = sizeof(elem);                    // io element bytes
-  static constexpr int NTEN = SUMMARY ? 2 : (GATE ? 3 : 2);  // streamed inputs: u, delta, (z)
-  static constexpr int PIECES = kChanPerWG * ES / 16;        // 16-byte pieces per tile row
-  static_assert(kT * PIECES <= 64, "one 16-byte piece of a tile per lane of a wave");
-  static_assert(NTEN < kWaves, "a wave left over for the output tile");
-  static constexpr int BC_PER_THREAD = kT * NP / kPrefillThreads;
-
-  struct alignas(16) Smem {
-    float2 bc[2][NP][kTileStride];  // (B_t[n], C_t[n]) per chunk
-    uint4 in[2][NTEN][kT][PIECES];  // raw u, delta, z tiles per chunk
-    uint4 out[2][kT][PIECES];       // raw output tile per chunk
-    float p[kWaves][4 * kPRow];     // per-wave partial sums [row][step][lane]
-  };
-
-  static __device__ __forceinline__ void run(const ScanArgs& a) {
-    __shared__ Smem sm;
-    // Workgroup coordinates (all below 2^31: the host bounds the grid and d_inner); kept in
-    // scalar registers so that everything derived from them is scalar work.
-    const int64_t ncb_total = a.batch * a.n_cblk;
-    const int64_t lg = xcd_remap(blockIdx.x, a.n_wg);
-    const int64_t seg = __builtin_amdgcn_readfirstlane(static_cast<int>(lg / ncb_total));
-    const int64_t cb = lg - seg * ncb_total;
-    const int64_t b = __builtin_amdgcn_readfirstlane(static_cast<int>(cb / a.n_cblk));
-    const int64_t d0 =
-        __builtin_amdgcn_readfirstlane(static_cast<int>((cb - b * a.n_cblk) * kChanPerWG));
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int r = lane >> 4;      // channel within the wave
-    const int k = lane & 15;      // lane within the row = owned step of each chunk
-    const int cl = wave * 4 + r;  // channel within the workgroup
-    const int64_t d = d0 + cl;
-    const bool chan_ok = d < a.d_inner;
-    const int64_t row = b * a.d_inner + d;  // (b, d) row index
-    const int64_t t_begin = seg * a.seg_len;
-    const int64_t t_end = (t_begin + a.seg_len < a.seqlen) ? t_begin + a.seg_len : a.seqlen;
-
-    // Per-lane constants: A scaled by log2(e) so that exp(dt A) = 2^(dt A2).
-    float A2[NL], h[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int n = k + 16 * j;
-      const bool ok = chan_ok && n < a.d_state;
-      A2[j] = ok ? a.A[d * a.d_state + n] * kLog2e : 0.0f;
-      h[j] = 0.0f;
-    }
-    const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
-    const float dskip = (!SUMMARY && chan_ok && a.D) ? a.D[d] : 0.0f;
-
-    if (!SUMMARY) {
-      // Initial state of this segment: h0 carried through the summaries of segments 0..seg-1.
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int n = k + 16 * j;
-        if (a.h0 && chan_ok && n < a.d_state) h[j] = a.h0[row * a.d_state + n];
-      }
-      for (int64_t s = 0; s < seg; ++s) {
-        const int64_t srow = s * a.batch * a.d_inner + row;
-        const float dsum = chan_ok ? a.seg_dt[srow] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          const int n = k + 16 * j;
-          const float he = (chan_ok && n < a.d_state) ? a.seg_h[srow * a.d_state + n] : 0.0f;
-          h[j] = fmaf(exp2_hw(A2[j] * dsum), h[j], he);
-        }
-      }
-    }
-
-    // ---- cooperative tile traffic ----
-    // Tiles are addressed through raw buffer resources whose base moves by one chunk per call and
-    // whose size covers only the chunk's valid steps: loads past the end of the sequence return 0
-    // and stores past it are dropped by the hardware range check.  Each thread's byte offset
-    // inside a tile is therefore fixed for the whole loop, and no load or store needs a mask or an
-    // address update of its own.
-    // Roles: every thread loads element(s) (tau, n) of the B and C tiles, consecutive threads on
-    // consecutive n (contiguous in memory); wave w < NTEN loads tile w of (u, delta, z), one
-    // 16-byte piece (step row, piece) per lane; wave NTEN stores the output tile.  Global loads for
-    // chunk i+1 are issued before chunk i is computed and written to LDS after it.
-    const int64_t D = a.d_inner, N = a.d_state;
-    const int64_t row0 = b * a.seqlen + t_begin;  // (b, t_begin) row of u/delta/z/out, B/C
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int tl_row = lane / PIECES, tl_pc = lane % PIECES;  // piece of a u/delta/z/out tile
-    const bool tl_on = lane < kT * PIECES;
-    const uint32_t tl_off =
-        tl_on ? static_cast<uint32_t>((tl_row * D + tl_pc * (16 / ES)) * ES) : kOffNone;
-    const char* in_base = static_cast<const char*>(wave_u == 0 ? a.u : (wave_u == 1 ? a.delta
-                                                                                     : a.z));
-    const int64_t io_chunk_bytes = kT * D * ES;
-    const int64_t io_off0 = (row0 * D + d0) * ES;  // byte offset of chunk 0's tiles
-    int bc_tau[BC_PER_THREAD], bc_n[BC_PER_THREAD];
-    uint32_t bc_off[BC_PER_THREAD];
-#pragma unroll
-    for (int i = 0; i < BC_PER_THREAD; ++i) {
-      const int idx = tid + i * kPrefillThreads;  // < kT * NP
-      bc_tau[i] = idx / NP;
-      bc_n[i] = idx - bc_tau[i] * NP;
-      bc_off[i] = bc_n[i] < N ? static_cast<uint32_t>((bc_tau[i] * N + bc_n[i]) * ES) : kOffNone;
-    }
-    static_assert(BC_PER_THREAD * kPrefillThreads == kT * NP, "B/C tile split over threads");
-    int ncols = static_cast<int>(D - (d0 + tl_pc * (16 / ES)));  // valid channels of the piece
-    ncols = ncols < 0 ? 0 : (ncols > 16 / ES ? 16 / ES : ncols);
-    // chunk counters are 32-bit (scalar compares; the host bounds seqlen below 2^31)
-    const int nchunks = static_cast<int>((t_end - t_begin + kT - 1) / kT);
-
-    struct Pre {
-      elem rb[BC_PER_THREAD], rc[BC_PER_THREAD];
-      uint4 rin;
-    } pre;
-
-    // valid steps of chunk ci (kT except for a partial last chunk); uniform over the workgroup
-    const int last_valid = static_cast<int>(t_end - t_begin - int64_t(nchunks - 1) * kT);
-    auto nvalid_of = [&](int ci) { return ci == nchunks - 1 ? last_valid : kT; };
-    // The range ends with the last valid row: channels past d_inner in that row (reached only by
-    // the element path) read 0 and are not written.
-    auto io_buf = [&](const void* base, int ci) {
-      return make_buf(static_cast<const char*>(base) + io_off0 + int64_t(ci) * io_chunk_bytes,
-                      static_cast<uint32_t>((nvalid_of(ci) * D - d0) * ES));
-    };
-
-    auto load_chunk = [&](int ci) {
-      const int64_t bc_off0 = ((row0 + int64_t(ci) * kT) * N) * ES;
-      const uint32_t bc_bytes = static_cast<uint32_t>(nvalid_of(ci) * N * ES);
-      const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + bc_off0, bc_bytes);
-      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + bc_off0, bc_bytes);
-#pragma unroll
-      for (int i = 0; i < BC_PER_THREAD; ++i) {
-        pre.rb[i] = buf_load<elem>(rb, bc_off[i]);
-        pre.rc[i] = buf_load<elem>(rc, bc_off[i]);
-      }
-      if (wave_u < NTEN) {  // uniform
-        const rsrc_t ri = io_buf(in_base, ci);
-        if (VEC) {
-          pre.rin = buf_load<uint4>(ri, tl_off);
-        } else {
-          // element loads; channels past d_inner read the next row or 0 and are never used
-          elem tmp[16 / ES];
-#pragma unroll
-          for (int e = 0; e < 16 / ES; ++e) tmp[e] = buf_load<elem>(ri, tl_off + e * ES);
-          pre.rin = *reinterpret_cast<const uint4*>(tmp);
-        }
-      }
-    };
-    auto stage_chunk = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < BC_PER_THREAD; ++i)
-        sm.bc[buf][bc_n[i]][bc_tau[i]] = make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
-      if (wave_u < NTEN && tl_on) sm.in[buf][wave_u][tl_row][tl_pc] = pre.rin;
-    };
-    // The data registers of the last output store are kept live (hold_store) until the next
-    // chunk's compute is done: otherwise the allocator reuses them at once and the write to them
-    // has to wait for the store to complete.
-    uint4 st_val{0, 0, 0, 0};
-    auto hold_store = [&]() {
-      if (VEC && !SUMMARY)
-        asm volatile("" ::"v"(st_val.x), "v"(st_val.y), "v"(st_val.z), "v"(st_val.w));
-    };
-    auto store_out = [&](int buf, int ci) {
-      if (!SUMMARY && wave_u == NTEN && tl_on) {
-        const rsrc_t ro = io_buf(a.out, ci);
-        const uint4 v = sm.out[buf][tl_row][tl_pc];
-        if (VEC) {
-          st_val = v;
-          buf_store(v, ro, tl_off);
-        } else {
-          elem tmp[16 / ES];
-          *reinterpret_cast<uint4*>(tmp) = v;
-#pragma unroll
-          for (int e = 0; e < 16 / ES; ++e)
-            if (e < ncols) buf_store(tmp[e], ro, tl_off + e * ES);
-        }
-      }
-    };
-    auto own_in = [&](int buf, int ten) -> float {
-      const elem* t = reinterpret_cast<const elem*>(&sm.in[buf][ten][k][0]);
-      return IO::widen(t[cl]);
-    };
-
-    float dt_acc = 0.0f;  // summary pass: this lane's share of sum(dt) over the segment
-
-    load_chunk(0);
-    stage_chunk(0);
-    __syncthreads();
-
-    // One chunk: issue the loads of the next chunk, compute this one from LDS buffer BUF, stage
-    // the next chunk into the other buffer, then store this chunk's output tile.  BUF is a
-    // compile-time constant so that every LDS address is a register plus an immediate.
-    auto chunk = [&](int ci, auto bufc) {
-      constexpr int buf = decltype(bufc)::value;
-      const bool has_next = ci + 1 < nchunks;
-      if (has_next) load_chunk(ci + 1);
-
-      const bool own_ok = chan_ok && k < nvalid_of(ci);
-      const float xu = own_in(buf, 0);
-      const float sv = own_in(buf, 1) + bias;
-      float dt = a.softplus ? softplus_f(sv) : sv;
-      dt = own_ok ? dt : 0.0f;  // steps past the end leave h unchanged
-      const float du = own_ok ? dt * xu : 0.0f;
-      if (SUMMARY) dt_acc += dt;
-
-      chunk_steps(sm, buf, dt, du, A2, h, wave, r, k);
-
-      if (!SUMMARY) {
-        wave_lds_sync();
-        const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
-        const float4 q0 = *reinterpret_cast<const float4*>(pr + 0);
-        const float4 q1 = *reinterpret_cast<const float4*>(pr + 4);
-        const float4 q2 = *reinterpret_cast<const float4*>(pr + 8);
-        const float4 q3 = *reinterpret_cast<const float4*>(pr + 12);
-        wave_lds_sync();
-        float y = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w))) +
-                  (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
-        y = fmaf(dskip, xu, y);
-        if (GATE) y *= silu_f(own_in(buf, 2));
-        reinterpret_cast<elem*>(&sm.out[buf][k][0])[cl] = IO::from_float(y);
-      }
-      hold_store();
-      if (has_next) stage_chunk(buf ^ 1);
-      __syncthreads();
-      store_out(buf, ci);
-    };
-    using Buf0 = std::integral_constant<int, 0>;
-    using Buf1 = std::integral_constant<int, 1>;
-
-    // Waves of different workgroups sharing a SIMD would otherwise be served oldest first, so
-    // some finish early and the SIMD runs the end of the kernel with few waves.  A wave lowers
-    // its issue priority by one at each quarter of its chunks, which keeps the waves of a SIMD
-    // close together.  Quarter boundaries are even, so chunk pairs always start on buffer 0.
-    int ci = 0;
-    for (int qi = 0; qi < 4; ++qi) {
-      switch (qi) {
-        case 0: __builtin_amdgcn_s_setprio(3); break;
-        case 1: __builtin_amdgcn_s_setprio(2); break;
-        case 2: __builtin_amdgcn_s_setprio(1); break;
-        default: __builtin_amdgcn_s_setprio(0); break;
-      }
-      const int c_end = qi == 3 ? nchunks : (((qi + 1) * nchunks) / 4) & ~1;
-      for (; ci + 1 < c_end; ci += 2) {
-        chunk(ci, Buf0{});
-        chunk(ci + 1, Buf1{});
-      }
-      if (ci < c_end) {  // odd chunk count: the last chunk, on buffer 0
-        chunk(ci, Buf0{});
-        ++ci;
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-
-    if (SUMMARY) {
-      // segment summary: local end state and the row's total dt
-      float sdt = dt_acc;
-      sdt += __shfl_xor(sdt, 1, 16);
-      sdt += __shfl_xor(sdt, 2, 16);
-      sdt += __shfl_xor(sdt, 4, 16);
-      sdt += __shfl_xor(sdt, 8, 16);
-      if (chan_ok) {
-        const int64_t srow = seg * a.batch * a.d_inner + row;
-        if (k == 0) a.seg_dt[srow] = sdt;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          const int n = k + 16 * j;
-          if (n < a.d_state) a.seg_h[srow * a.d_state + n] = h[j];
-        }
-      }
-    } else if (a.h_last && chan_ok && seg == a.nseg - 1) {
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int n = k + 16 * j;
-        if (n < a.d_state) a.h_last[row * a.d_state + n] = h[j];
-      }
-    }
-  }
-
-  // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
-  // (B, C) pairs for this lane's states, two steps per float4.
-  template <int TAU>
-  static __device__ __forceinline__ void step(Smem& sm, const float4 (&bcv)[NL][kT / 2],
-                                              float dt, float du, const float (&A2)[NL],
-                                              float (&h)[NL], int wave, int r, int k) {
-    const float dtb = row_bcast<TAU>(dt);
-    const float dub = row_bcast<TAU>(du);
-    float p = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const float4 v = bcv[j][TAU / 2];
-      const float bb = (TAU & 1) ? v.z : v.x;
-      const float cc = (TAU & 1) ? v.w : v.y;
-      const float e = exp2_hw(dtb * A2[j]);
-      h[j] = fmaf(e, h[j], dub * bb);
-      p = (j == 0) ? cc * h[j] : fmaf(cc, h[j], p);
-    }
-    if (!SUMMARY) sm.p[wave][r * kPRow + TAU * kPTau + k] = p;
-  }
-
-  template <int... TAUS>
-  static __device__ __forceinline__ void steps(std::integer_sequence<int, TAUS...>, Smem& sm,
-                                               const float4 (&bcv)[NL][kT / 2], float dt,
-                                               float du, const float (&A2)[NL], float (&h)[NL],
-                                               int wave, int r, int k) {
-    (step<TAUS>(sm, bcv, dt, du, A2, h, wave, r, k), ...);
-  }
-
-  // The 16 recurrence steps of one chunk.  The B/C tile reads are issued together up front
-  // (16-byte reads, two steps each) so that the steps themselves are pure VALU work.
-  static __device__ __forceinline__ void chunk_steps(Smem& sm, int buf, float dt, float du,
-                                                     const float (&A2)[NL], float (&h)[NL],
-                                                     int wave, int r, int k) {
-    float4 bcv[NL][kT / 2];
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-#pragma unroll
-      for (int i = 0; i < kT / 2; ++i)
-        bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k + 16 * j][2 * i]);
-    steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, h, wave, r, k);
-  }
-};
-
-template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC>
-__global__ void __launch_bounds__(kPrefillThreads) scan_kernel(ScanArgs a) {
-  ScanKernel<IO, NL, GATE, SUMMARY, VEC>::run(a);
-}
 
 __global__ void __launch_bounds__(256) copy_state_kernel(float* dst, const float* src, int64_t n) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     dst[i] = src ? src[i] : 0.0f;
 }
 
-template <class IO, int NL, bool VEC>
-hipError_t launch3(const ScanArgs& a, bool summary, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(a.n_wg)), block(kPrefillThreads);
-  if (summary)
-    hipLaunchKernelGGL((scan_kernel<IO, NL, false, true, VEC>), grid, block, 0, stream, a);
-  else if (a.z != nullptr)
-    hipLaunchKernelGGL((scan_kernel<IO, NL, true, false, VEC>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((scan_kernel<IO, NL, false, false, VEC>), grid, block, 0, stream, a);
-  return hipGetLastError();
-}
-
-template <class IO, int NL>
-hipError_t launch2(const ScanArgs& a, bool summary, hipStream_t stream) {
-  return a.vec_io ? launch3<IO, NL, true>(a, summary, stream)
-                  : launch3<IO, NL, false>(a, summary, stream);
-}
-
-template <class IO>
-hipError_t launch1(const ScanArgs& a, bool summary, hipStream_t stream) {
-  switch ((a.d_state + 15) / 16) {
-    case 1: return launch2<IO, 1>(a, summary, stream);
-    case 2: return launch2<IO, 2>(a, summary, stream);
-    case 3: return launch2<IO, 3>(a, summary, stream);
-    default: return launch2<IO, 4>(a, summary, stream);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream) {
-  return bf16 ? launch1<BF16>(a, summary, stream) : launch1<F32>(a, summary, stream);
+  if (a.zoh) return launch_scan_zoh(a, bf16, summary, stream);
+  return launch_scan_instances<false>(a, bf16, summary, stream);
 }
 
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t stream) {

@@ -3,6 +3,8 @@
 // One call advances the resident float32 state (batch, d_inner, d_state) by one token, in place:
 //     dt = softplus(delta + bias),  h[n] <- exp(dt A[d,n]) h[n] + dt B[n] u,
 //     y = C . h + D u,  out = y * silu(z).
+// With ZOH the input term is the exact zero-order-hold one, (exp(dt A) - 1) / A * B u (reading
+// guide, "Método"), in place of dt B u.
 // (Mamba reading guide, "Perguntas": generation keeps only a fixed d_inner x d_state state per
 // layer and costs O(1) per token; "Método" for the recurrence.)
 //
@@ -49,7 +51,7 @@ struct Vec4In<BF16> {
 };
 
 // Vector path: d_state % 4 == 0, 16-byte aligned state and A, ITEMS 4-state items per thread.
-template <class IO, bool GATE, int ITEMS>
+template <class IO, bool GATE, bool ZOH, int ITEMS>
 __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs a) {
   using elem = typename IO::elem;
   using V = Vec4In<IO>;
@@ -101,7 +103,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
     float p = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      hh[j] = fmaf(exp2_hw(dt * (aa[j] * kLog2e)), hh[j], du * V::get(bv[i], j));
+      const float y = dt * (aa[j] * kLog2e);
+      const float e = exp2_hw(y);
+      const float inc = du * V::get(bv[i], j);
+      hh[j] = fmaf(e, hh[j], ZOH ? inc * (zoh_gain(e, y) * (1.0f / kLn2)) : inc);
       p = fmaf(V::get(cv[i], j), hh[j], p);
     }
     if (act[i])
@@ -118,7 +123,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
 }
 
 // Generic path: any d_state in 1..64 and any alignment; one 4-state item per thread.
-template <class IO, bool GATE>
+template <class IO, bool GATE, bool ZOH>
 __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeArgs a) {
   using elem = typename IO::elem;
   const int G = a.lanes_per_chan;
@@ -147,8 +152,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeAr
     const float* Ar = a.A + d * N + n0;
     const int64_t bc = b * N + n0;
     for (int i = 0; i < 4 && n0 + i < N; ++i) {
-      const float e = exp2_hw(dt * (Ar[i] * kLog2e));
-      const float hn = fmaf(e, st[i], du * IO::load(Bp, bc + i));
+      const float y = dt * (Ar[i] * kLog2e);
+      const float e = exp2_hw(y);
+      const float inc = du * IO::load(Bp, bc + i);
+      const float hn = fmaf(e, st[i], ZOH ? inc * (zoh_gain(e, y) * (1.0f / kLn2)) : inc);
       st[i] = hn;
       p = fmaf(IO::load(Cp, bc + i), hn, p);
     }
@@ -163,27 +170,33 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeAr
 
 constexpr int kItems = 4;
 
-template <class IO, bool GATE>
+template <class IO, bool GATE, bool ZOH>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t lanes = a.batch * a.d_inner * a.lanes_per_chan;
   if (a.vec4) {
     const int64_t per_block = int64_t(kDecodeThreads) * kItems;
     const dim3 grid(static_cast<unsigned>((lanes + per_block - 1) / per_block));
-    hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, kItems>), grid, dim3(kDecodeThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, kItems>), grid, dim3(kDecodeThreads),
+                       0, stream, a);
   } else {
     const dim3 grid(static_cast<unsigned>((lanes + kDecodeThreads - 1) / kDecodeThreads));
-    hipLaunchKernelGGL((decode_generic_kernel<IO, GATE>), grid, dim3(kDecodeThreads), 0, stream,
-                       a);
+    hipLaunchKernelGGL((decode_generic_kernel<IO, GATE, ZOH>), grid, dim3(kDecodeThreads), 0,
+                       stream, a);
   }
   return hipGetLastError();
+}
+
+template <bool ZOH>
+hipError_t launch_z(const DecodeArgs& a, bool bf16, hipStream_t stream) {
+  if (bf16)
+    return a.z ? launch_g<BF16, true, ZOH>(a, stream) : launch_g<BF16, false, ZOH>(a, stream);
+  return a.z ? launch_g<F32, true, ZOH>(a, stream) : launch_g<F32, false, ZOH>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream) {
-  if (bf16) return a.z ? launch_g<BF16, true>(a, stream) : launch_g<BF16, false>(a, stream);
-  return a.z ? launch_g<F32, true>(a, stream) : launch_g<F32, false>(a, stream);
+  return a.zoh ? launch_z<true>(a, bf16, stream) : launch_z<false>(a, bf16, stream);
 }
 
 }  // namespace ss

@@ -17,18 +17,22 @@ LIB_PATH = os.path.join(_HERE, "libssscan.so")
 
 SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_HIP = 0, 1, 2, 3
 SS_F32, SS_BF16 = 0, 1
+SS_FLAG_ZOH_EXACT = 1
 
 # Every symbol declared in include/ss_scan.h, with its ctypes signature.
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_u32 = ctypes.c_uint32
 SIGNATURES = {
     "ss_scan_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                            _i64, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "ss_scan_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "ss_scan_fwd_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
-                              _vp, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32, _vp]),
+                              _vp, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32, _u32, _vp]),
     "ss_scan_fwd_ex_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
     "ss_state_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                _i64, _i64, _i64, _i32, _vp]),
+    "ss_state_update_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
+                                  _vp, _i64, _i64, _i64, _i32, _u32, _vp]),
     "ss_status_string": (ctypes.c_char_p, [_i32]),
     "ss_last_error": (ctypes.c_char_p, []),
     "ss_version": (ctypes.c_int, []),
@@ -106,14 +110,15 @@ def workspace_bytes(batch, seqlen, d_inner, d_state, dtype=torch.bfloat16, nseg=
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
              return_last_state=False, out=None, h_last=None, workspace=None, nseg=None,
-             stream=None):
+             zoh_exact=False, stream=None):
     """Prefill selective scan on the GPU (ss_scan_fwd / ss_scan_fwd_ex).
 
     u, delta, z: (batch, L, d_inner); B, C: (batch, L, d_state); all the same io dtype (float32 or
     bfloat16).  A: (d_inner, d_state) float32; D, delta_bias: (d_inner,) float32; h0:
     (batch, d_inner, d_state) float32.  Returns out (and h_last when return_last_state).
     nseg: None = automatic time split (workspace sized and allocated here unless given), an int
-    forces that many segments (ss_scan_fwd_ex).
+    forces that many segments (ss_scan_fwd_ex).  zoh_exact: exact zero-order-hold input term
+    (SS_FLAG_ZOH_EXACT, through ss_scan_fwd_ex).
     """
     batch, L, d_inner = u.shape
     d_state = B.shape[-1]
@@ -141,15 +146,16 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     args = [_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             1 if delta_softplus else 0, _ptr(h0), _ptr(h_last), _ptr(out),
             batch, L, d_inner, d_state, code, ws_ptr, ws_len]
-    if nseg is None:
+    if nseg is None and not zoh_exact:
         _check(lib().ss_scan_fwd(*args, _stream(stream)))
     else:
-        _check(lib().ss_scan_fwd_ex(*args, int(nseg), _stream(stream)))
+        flags = SS_FLAG_ZOH_EXACT if zoh_exact else 0
+        _check(lib().ss_scan_fwd_ex(*args, int(nseg or 0), flags, _stream(stream)))
     return (out, h_last) if return_last_state else out
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                 delta_softplus=True, out=None, stream=None):
+                 delta_softplus=True, out=None, zoh_exact=False, stream=None):
     """One decode step on the GPU (ss_state_update); `state` is updated in place.
 
     state: (batch, d_inner, d_state) float32; u, delta, z: (batch, d_inner); B, C:
@@ -168,8 +174,10 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if out is None:
         out = torch.empty_like(u)
     _dev(out, "out", u.dtype, (batch, d_inner))
-    _check(lib().ss_state_update(
-        _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-        _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(out), batch, d_inner, d_state, code,
-        _stream(stream)))
+    args = [_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), 1 if delta_softplus else 0, _ptr(out), batch, d_inner, d_state, code]
+    if zoh_exact:
+        _check(lib().ss_state_update_ex(*args, SS_FLAG_ZOH_EXACT, _stream(stream)))
+    else:
+        _check(lib().ss_state_update(*args, _stream(stream)))
     return out

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("ss_scan_fwd", "ss_state_update", "ss_scan_fwd_workspace_bytes",
-                     "ss_scan_fwd_ex", "ss_status_string", "ss_last_error"):
+                     "ss_scan_fwd_ex", "ss_state_update_ex", "ss_status_string",
+                     "ss_last_error"):
         assert required in names
 
 
@@ -84,7 +85,8 @@ def test_scan_argument_errors_before_launch(lib):
 
 def test_forced_split_needs_workspace(lib):
     rc = lib.ss_scan_fwd_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
-                            None, None, FAKE * 6, 2, 4096, 64, 16, ops.SS_BF16, None, 0, 4, None)
+                            None, None, FAKE * 6, 2, 4096, 64, 16, ops.SS_BF16, None, 0, 4, 0,
+                            None)
     assert rc == ops.SS_ERR_INVALID_ARG and b"workspace" in lib.ss_last_error()
     assert lib.ss_scan_fwd_ex_workspace_bytes(2, 4096, 64, 16, ops.SS_BF16, 1) == 0
     nb = lib.ss_scan_fwd_ex_workspace_bytes(2, 4096, 64, 16, ops.SS_BF16, 4)
@@ -101,3 +103,17 @@ def test_decode_argument_errors(lib):
              FAKE * 8, 2, 8, 16, ops.SS_BF16, None) == ops.SS_ERR_INVALID_ARG  # out == state
     assert f(FAKE * 8, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
              FAKE * 6, 0, 8, 16, ops.SS_BF16, None) == ops.SS_OK
+
+
+def test_unknown_flag_bits_are_rejected(lib):
+    rc = lib.ss_scan_fwd_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
+                            None, None, FAKE * 6, 1, 16, 8, 16, ops.SS_BF16, None, 0, 0, 6, None)
+    assert rc == ops.SS_ERR_UNSUPPORTED and b"flag" in lib.ss_last_error()
+    rc = lib.ss_state_update_ex(FAKE * 8, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None,
+                                None, None, 1, FAKE * 6, 2, 8, 16, ops.SS_BF16, 0x80000000, None)
+    assert rc == ops.SS_ERR_UNSUPPORTED and b"flag" in lib.ss_last_error()
+    # the exact-hold bit alone is accepted: argument checks then proceed as usual
+    rc = lib.ss_state_update_ex(None, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None,
+                                None, 1, FAKE * 6, 2, 8, 16, ops.SS_BF16, ops.SS_FLAG_ZOH_EXACT,
+                                None)
+    assert rc == ops.SS_ERR_INVALID_ARG

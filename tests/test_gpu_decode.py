@@ -146,3 +146,46 @@ def test_decode_full_size_sampled():
         rng.integers(0, w.batch * w.d_inner, size=2000)])).astype(np.int64)
     print(f"  decode full size, {len(rows)} sampled rows", flush=True)
     _decode_steps(d, 50, rows=rows)
+
+
+def test_decode_graph_replays_match_eager():
+    """Decode steps captured into a HIP graph (as the benchmark's graph line does): each of
+    several replays, with eager work and synchronisation between them, matches the same steps
+    run eagerly from the same starting state, bit for bit."""
+    w = wl.WORKLOADS[4]
+    steps = 4
+    d = wl.make_decode(w, steps=steps, batch=5, d_inner=96)
+    A, D, db = dev(d["A"]), dev(d["D"]), dev(d["delta_bias"])
+    u, dl, z, B, C = (dev(d[k]) for k in ("u", "delta", "z", "B", "C"))
+    st0 = dev(d["state"])
+    o = ops()
+
+    def run(st, outs, stream):
+        for s in range(steps):
+            o.state_update(st, u[s], dl[s], A, B[s], C[s], D=D, z=z[s], delta_bias=db,
+                           out=outs[s], stream=stream)
+
+    st_e = st0.clone()
+    outs_e = torch.empty((steps,) + u.shape[1:], dtype=u.dtype, device="cuda")
+    run(st_e, outs_e, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    st_g = st0.clone()
+    outs_g = torch.empty_like(outs_e)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        run(st_g, outs_g, cap)  # warm-up outside the capture
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            run(st_g, outs_g, cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st_g.copy_(st0)
+        outs_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs_g, outs_e), f"replay {rep}: outputs differ from eager"
+        assert torch.equal(st_g, st_e), f"replay {rep}: state differs from eager"
