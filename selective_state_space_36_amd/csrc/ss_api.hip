@@ -279,8 +279,9 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
   a.softplus = delta_softplus ? 1 : 0;
   a.zoh = (flags & SS_FLAG_ZOH_EXACT) ? 1 : 0;
   const int64_t bc_align = dtype == SS_BF16 ? 8 : 16;  // four io elements of B and C
-  a.vec4 = (d_state % 4 == 0 && aligned(state, 16) && aligned(A, 16) && aligned(B, bc_align) &&
-            aligned(C, bc_align)) ? 1 : 0;
+  // the vector path addresses a batch row of the state with 32-bit byte offsets
+  a.vec4 = (d_state % 4 == 0 && d_inner * d_state < (int64_t(1) << 29) && aligned(state, 16) &&
+            aligned(A, 16) && aligned(B, bc_align) && aligned(C, bc_align)) ? 1 : 0;
   if ((rows * g + 255) / 256 > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many rows");
   const hipError_t e = ss::launch_decode(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));

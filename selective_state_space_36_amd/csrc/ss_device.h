@@ -92,6 +92,14 @@ __device__ __forceinline__ uint4 buf_load<uint4>(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 template <>
+__device__ __forceinline__ uint2 buf_load<uint2>(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float4 buf_load<float4>(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <>
 __device__ __forceinline__ uint16_t buf_load<uint16_t>(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
@@ -102,6 +110,9 @@ __device__ __forceinline__ float buf_load<float>(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_store(uint4 v, rsrc_t r, uint32_t off) {
   using v4u = __attribute__((ext_vector_type(4))) unsigned int;
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(float4 v, rsrc_t r, uint32_t off) {
+  buf_store(__builtin_bit_cast(uint4, v), r, off);
 }
 __device__ __forceinline__ void buf_store(uint16_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);

@@ -13,8 +13,9 @@
 // power-of-two group of lanes, 4 consecutive states per lane, so that a wave reads and writes one
 // contiguous run of the state with 16-byte accesses.  Each thread handles several such 4-state
 // items and issues all their loads before any arithmetic, to keep enough bytes in flight to cover
-// the memory latency.  The group reduces C . h with cross-lane shuffles; its first lane finishes
-// the element (skip, gate, store).
+// the memory latency.  The group reduces C . h with cross-lane DPP adds; its first lane finishes
+// the element (skip, gate, store).  Address arithmetic is kept to a few 32-bit operations per
+// item: with this little work per byte, index math alone would otherwise bound the kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,9 +32,6 @@ struct Vec4In;  // four consecutive io elements
 template <>
 struct Vec4In<F32> {
   using raw = float4;
-  static __device__ __forceinline__ raw load(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
-  }
   static __device__ __forceinline__ float get(const raw& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
   }
@@ -41,83 +39,143 @@ struct Vec4In<F32> {
 template <>
 struct Vec4In<BF16> {
   using raw = uint2;
-  static __device__ __forceinline__ raw load(const uint16_t* p) {
-    return *reinterpret_cast<const uint2*>(p);
-  }
   static __device__ __forceinline__ float get(const raw& v, int i) {
     const uint32_t w = (i < 2) ? v.x : v.y;
     return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
   }
 };
 
-// Vector path: d_state % 4 == 0, 16-byte aligned state and A, ITEMS 4-state items per thread.
-template <class IO, bool GATE, bool ZOH, int ITEMS>
+// Value of x held by lane J of this lane's quad (DPP quad_perm broadcast).
+template <int J>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), J * 0x55, 0xf, 0xf, false));
+}
+
+// Sum of x over aligned groups of G lanes (G a power of two <= 64), the result in every lane of
+// the group.  Groups of up to 4 use DPP quad permutations (no LDS traffic).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if (G >= 2)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+  if (G >= 4)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+  for (int m = 4; m < G; m <<= 1) x += __shfl_xor(x, m, G);
+  return x;
+}
+
+// Vector path: d_state % 4 == 0, 16-byte aligned state and A, d_inner * d_state < 2^29.
+// Grid: x over the lanes of one batch row (G lanes per channel, 4 consecutive states per lane),
+// y over batch rows (strided when batch exceeds the grid).  Every array is addressed as a raw
+// buffer based at the row (scalar registers) with 32-bit lane offsets, so the index math is a
+// few shifts, and lanes past the row get an offset beyond every range: their loads return 0 and
+// their stores are dropped by the hardware range check.  Each thread takes ITEMS lanes 256
+// apart and issues all their loads before any arithmetic.
+template <class IO, bool GATE, bool ZOH, int G, int ITEMS>
 __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs a) {
   using elem = typename IO::elem;
+  using raw4 = typename Vec4In<IO>::raw;  // four io elements
   using V = Vec4In<IO>;
-  const int G = a.lanes_per_chan;
+  constexpr int ES = sizeof(elem);
+  constexpr int LOG_G = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
+  static_assert((1 << LOG_G) == G && G <= 16, "lanes per channel");
   const int N = a.d_state;
-  const int64_t nch = a.batch * a.d_inner;
-  const elem* up = static_cast<const elem*>(a.u);
-  const elem* dp = static_cast<const elem*>(a.delta);
-  const elem* zp = static_cast<const elem*>(a.z);
-  const elem* Bp = static_cast<const elem*>(a.B);
-  const elem* Cp = static_cast<const elem*>(a.C);
+  const int D = static_cast<int>(a.d_inner);
+  const uint32_t st_bytes = static_cast<uint32_t>(D) * N * 4;
+  const rsrc_t rA = make_buf(a.A, st_bytes);
+  const rsrc_t rbias = make_buf(a.delta_bias, a.delta_bias ? D * 4u : 0u);
+  const rsrc_t rD = make_buf(a.D, a.D ? D * 4u : 0u);
 
-  int64_t ch[ITEMS];
-  int q[ITEMS];
-  bool act[ITEMS];
-  float4 hv[ITEMS], av[ITEMS];
-  typename V::raw bv[ITEMS], cv[ITEMS];
-  elem xr[ITEMS], dr[ITEMS], zr[ITEMS];
-  float bias[ITEMS], dsk[ITEMS];
-  // issue every load first
+  // Per-channel inputs.  With G >= 4 the four lanes of a quad (one channel) split them: lane 0
+  // of the quad loads u, lane 1 delta, lane 2 z, and lanes 0/1 also delta_bias/D; DPP quad
+  // broadcasts then hand them to the whole quad.  That is 2 narrow loads per lane instead of 5,
+  // and the narrow loads are what the memory pipeline spends the most instructions on.
+  constexpr bool QUAD = G >= 4;
+  const int qq = threadIdx.x & 3;
+  const elem* aux_base = static_cast<const elem*>(
+      qq == 0 ? a.u : (qq == 1 ? a.delta : (GATE && qq == 2 ? a.z : a.u)));
+  const float* f_src = qq == 0 ? a.delta_bias : a.D;
+  const bool f_ok = f_src != nullptr;
+  const float* f_base = f_ok ? f_src : a.A;  // any valid address; the value is then zeroed
+  uint32_t so[ITEMS], io[ITEMS], fo[ITEMS], bo[ITEMS], oo[ITEMS];
+  uint32_t dcl[ITEMS];  // channel clamped into the row
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int64_t item = (static_cast<int64_t>(blockIdx.x) * ITEMS + i) * kDecodeThreads +
-                         threadIdx.x;
-    ch[i] = item / G;
-    q[i] = static_cast<int>(item - ch[i] * G);
-    act[i] = ch[i] < nch && q[i] * 4 < N;
-    const int64_t c = ch[i] < nch ? ch[i] : nch - 1;  // clamped: always a valid address
-    const int n0 = (q[i] * 4 < N) ? q[i] * 4 : 0;
-    const int64_t b = c / a.d_inner, d = c - b * a.d_inner;
-    hv[i] = *reinterpret_cast<const float4*>(a.state + c * N + n0);
-    av[i] = *reinterpret_cast<const float4*>(a.A + d * N + n0);
-    bv[i] = V::load(Bp + b * N + n0);
-    cv[i] = V::load(Cp + b * N + n0);
-    xr[i] = up[c];
-    dr[i] = dp[c];
-    if (GATE) zr[i] = zp[c];
-    bias[i] = a.delta_bias ? a.delta_bias[d] : 0.0f;
-    dsk[i] = a.D ? a.D[d] : 0.0f;
+    const uint32_t l = (blockIdx.x * ITEMS + i) * kDecodeThreads + threadIdx.x;
+    const uint32_t d = l >> LOG_G, q = l & (G - 1);
+    const bool act = d < static_cast<uint32_t>(D) && q * 4 < static_cast<uint32_t>(N);
+    dcl[i] = d < static_cast<uint32_t>(D) ? d : D - 1;
+    so[i] = act ? (d * N + q * 4) * 4 : kOffNone;  // state and A
+    io[i] = act ? d * ES : kOffNone;                // u, delta, z
+    fo[i] = act ? d * 4 : kOffNone;                 // delta_bias, D
+    bo[i] = act ? q * 4 * ES : kOffNone;            // B, C
+    oo[i] = act && q == 0 ? d * ES : kOffNone;      // out (first lane of the group)
   }
+
+  for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
+    const rsrc_t rs = make_buf(a.state + b * D * N, st_bytes);
+    const rsrc_t ru = make_buf(static_cast<const elem*>(a.u) + b * D, D * ES);
+    const rsrc_t rd = make_buf(static_cast<const elem*>(a.delta) + b * D, D * ES);
+    const rsrc_t rz = make_buf(GATE ? static_cast<const elem*>(a.z) + b * D : nullptr,
+                               GATE ? D * ES : 0u);
+    const rsrc_t rB = make_buf(static_cast<const elem*>(a.B) + b * N, N * ES);
+    const rsrc_t rC = make_buf(static_cast<const elem*>(a.C) + b * N, N * ES);
+    const rsrc_t ro = make_buf(static_cast<elem*>(a.out) + b * D, D * ES);
+    float4 hv[ITEMS], av[ITEMS];
+    raw4 bv[ITEMS], cv[ITEMS];
+    elem xr[ITEMS], dr[ITEMS], zr[ITEMS];
+    float bias[ITEMS], dsk[ITEMS];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const float x = IO::widen(xr[i]);
-    const float s = IO::widen(dr[i]) + bias[i];
-    const float dt = a.softplus ? softplus_f(s) : s;
-    const float du = dt * x;
-    float hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
-    const float aa[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-    float p = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float y = dt * (aa[j] * kLog2e);
-      const float e = exp2_hw(y);
-      const float inc = du * V::get(bv[i], j);
-      hh[j] = fmaf(e, hh[j], ZOH ? inc * (zoh_gain(e, y) * (1.0f / kLn2)) : inc);
-      p = fmaf(V::get(cv[i], j), hh[j], p);
+    for (int i = 0; i < ITEMS; ++i) {
+      hv[i] = buf_load<float4>(rs, so[i]);
+      av[i] = buf_load<float4>(rA, so[i]);
+      bv[i] = buf_load<raw4>(rB, bo[i]);
+      cv[i] = buf_load<raw4>(rC, bo[i]);
+      if (QUAD) {
+        xr[i] = aux_base[b * D + dcl[i]];  // u, delta or z by lane of the quad
+        bias[i] = f_base[dcl[i]];          // delta_bias or D by lane of the quad
+      } else {
+        xr[i] = buf_load<elem>(ru, io[i]);
+        dr[i] = buf_load<elem>(rd, io[i]);
+        if (GATE) zr[i] = buf_load<elem>(rz, io[i]);
+        bias[i] = buf_load<float>(rbias, fo[i]);
+        dsk[i] = buf_load<float>(rD, fo[i]);
+      }
     }
-    if (act[i])
-      *reinterpret_cast<float4*>(a.state + ch[i] * N + q[i] * 4) =
-          make_float4(hh[0], hh[1], hh[2], hh[3]);
-    p = act[i] ? p : 0.0f;
-    for (int m = G >> 1; m >= 1; m >>= 1) p += __shfl_xor(p, m, G);
-    if (ch[i] < nch && q[i] == 0) {
-      float y = fmaf(dsk[i], x, p);
-      if (GATE) y *= silu_f(IO::widen(zr[i]));
-      static_cast<elem*>(a.out)[ch[i]] = IO::from_float(y);
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      float x, s, zv = 0.0f, dskip;
+      if (QUAD) {
+        const float w = IO::widen(xr[i]);
+        const float f = f_ok ? bias[i] : 0.0f;
+        x = quad_bcast<0>(w);
+        s = quad_bcast<1>(w) + quad_bcast<0>(f);
+        if (GATE) zv = quad_bcast<2>(w);
+        dskip = quad_bcast<1>(f);
+      } else {
+        x = IO::widen(xr[i]);
+        s = IO::widen(dr[i]) + bias[i];
+        if (GATE) zv = IO::widen(zr[i]);
+        dskip = dsk[i];
+      }
+      const float dt = a.softplus ? softplus_f(s) : s;
+      const float du = dt * x;
+      float hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+      const float aa[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+      float p = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = dt * (aa[j] * kLog2e);
+        const float e = exp2_hw(y);
+        const float inc = du * V::get(bv[i], j);
+        hh[j] = fmaf(e, hh[j], ZOH ? inc * (zoh_gain(e, y) * (1.0f / kLn2)) : inc);
+        p = fmaf(V::get(cv[i], j), hh[j], p);  // inactive lanes: C reads 0, p stays 0
+      }
+      buf_store(make_float4(hh[0], hh[1], hh[2], hh[3]), rs, so[i]);
+      p = group_sum<G>(p);
+      float y = fmaf(dskip, x, p);
+      if (GATE) y *= silu_f(zv);
+      buf_store(IO::from_float(y), ro, oo[i]);
     }
   }
 }
@@ -168,17 +226,30 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeAr
   }
 }
 
-constexpr int kItems = 4;
+constexpr int kItems = 1;
+
+template <class IO, bool GATE, bool ZOH, int G>
+void launch_vec(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t per_block = int64_t(kDecodeThreads) * kItems;
+  const int64_t row_lanes = a.d_inner * G;
+  const dim3 grid(static_cast<unsigned>((row_lanes + per_block - 1) / per_block),
+                  static_cast<unsigned>(a.batch < 65535 ? a.batch : 65535));
+  hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, G, kItems>), grid, dim3(kDecodeThreads),
+                     0, stream, a);
+}
 
 template <class IO, bool GATE, bool ZOH>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t lanes = a.batch * a.d_inner * a.lanes_per_chan;
   if (a.vec4) {
-    const int64_t per_block = int64_t(kDecodeThreads) * kItems;
-    const dim3 grid(static_cast<unsigned>((lanes + per_block - 1) / per_block));
-    hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, kItems>), grid, dim3(kDecodeThreads),
-                       0, stream, a);
+    switch (a.lanes_per_chan) {
+      case 1: launch_vec<IO, GATE, ZOH, 1>(a, stream); break;
+      case 2: launch_vec<IO, GATE, ZOH, 2>(a, stream); break;
+      case 4: launch_vec<IO, GATE, ZOH, 4>(a, stream); break;
+      case 8: launch_vec<IO, GATE, ZOH, 8>(a, stream); break;
+      default: launch_vec<IO, GATE, ZOH, 16>(a, stream); break;
+    }
   } else {
+    const int64_t lanes = a.batch * a.d_inner * a.lanes_per_chan;
     const dim3 grid(static_cast<unsigned>((lanes + kDecodeThreads - 1) / kDecodeThreads));
     hipLaunchKernelGGL((decode_generic_kernel<IO, GATE, ZOH>), grid, dim3(kDecodeThreads), 0,
                        stream, a);
