@@ -155,6 +155,24 @@ def bench_prefill(args, torch, np, ops, wl):
     log(f"prefill {ms_step * 1e3:.1f} us/step (kernel avg {ms_kernel * 1e3:.1f} us, "
         f"min {per[0] * 1e3:.1f})")
 
+    # the same layer with the exact zero-order-hold input term (SS_FLAG_ZOH_EXACT)
+    zoh_out = torch.empty_like(u)
+    zsteps = max(3, args.steps // 4)
+    for _ in range(2):
+        ops.scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=db, out=zoh_out, workspace=ws,
+                     zoh_exact=True, stream=stream)
+    torch.cuda.synchronize()
+    zs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(zsteps)]
+    for a_, b_ in zs:
+        a_.record(stream)
+        ops.scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=db, out=zoh_out, workspace=ws,
+                     zoh_exact=True, stream=stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms_zoh = sum(a_.elapsed_time(b_) for a_, b_ in zs) / zsteps
+    log(f"prefill exact-hold kernel avg {ms_zoh * 1e3:.1f} us")
+
     # spot parity check of the benchmarked output on a few rows
     import oracle
     rows = np.array([0, 1, w.d_inner - 1, (w.batch - 1) * w.d_inner + w.d_inner // 2],
@@ -165,7 +183,13 @@ def bench_prefill(args, torch, np, ops, wl):
                            delta_bias=p["delta_bias"], rows=rows)
     err = np.abs(g - r)
     ok = bool(np.all(err <= 2e-2 + 2e-2 * np.abs(r)))
-    return w, p, ms_step, ms_kernel, ok, float(err.max())
+    gz = zoh_out.float()[torch.from_numpy(rows // w.d_inner).cuda(), :,
+                         torch.from_numpy(rows % w.d_inner).cuda()].cpu().numpy().astype(np.float64)
+    rz, _ = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                            delta_bias=p["delta_bias"], rows=rows, zoh_exact=True)
+    errz = np.abs(gz - rz)
+    ok = ok and bool(np.all(errz <= 2e-2 + 2e-2 * np.abs(rz)))
+    return w, p, ms_step, ms_kernel, ms_zoh, ok, float(max(err.max(), errz.max()))
 
 
 def bench_decode(args, torch, np, ops, wl):
@@ -341,7 +365,7 @@ def main():
         return
     ops.lib()
 
-    w, p, ms_step, ms_kernel, ok, maxerr = bench_prefill(args, torch, np, ops, wl)
+    w, p, ms_step, ms_kernel, ms_zoh, ok, maxerr = bench_prefill(args, torch, np, ops, wl)
     elems = w.elements
     value = elems / (ms_step * 1e-3)
     nbytes = prefill_bytes(w)
@@ -373,6 +397,10 @@ def main():
                      "kernel_us": round(ms_kernel * 1e3, 2)},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(hbm_gbps, 1),
                 "peak_GBps": PEAK_HBM_GBPS, "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4)},
+        "zoh_exact": {"kernel_us": round(ms_zoh * 1e3, 2),
+                      "elements_per_s": round(elems / (ms_zoh * 1e-3), 1),
+                      "note": "same layer with the exact zero-order-hold input term; its extra "
+                              "per-update work (series or (2^y-1)/y) is not in the slot count"},
         "parity_spot_check": {"ok": ok, "max_abs_err": maxerr},
     }
     if not args.no_decode:

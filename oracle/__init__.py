@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ss_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libss_oracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 _lib = None
 
@@ -69,14 +69,16 @@ def restore_library(prev):
 
 def _bind(lib):
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.oracle_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
+    lib.oracle_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                     i64, i64, i64, i64, vp, i64, vp, vp, i32]
     lib.oracle_scan_fwd.restype = i32
     lib.oracle_scan_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
-                                            i64, i64, i64, i64, i64, vp, vp]
+                                            i32, i64, i64, i64, i64, i64, vp, vp]
     lib.oracle_scan_fwd_chunked.restype = i32
     lib.oracle_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
-                                        i64, i64, i64, vp, i64, vp, i32]
+                                        i32, i64, i64, i64, vp, i64, vp, i32]
+    lib.oracle_conv_silu.argtypes = [vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
+    lib.oracle_conv_silu.restype = i32
     lib.oracle_state_update.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
@@ -97,6 +99,16 @@ def _io(x, name):
     if x.dtype == np.uint16:
         return x, BF16
     raise TypeError(f"{name}: expected float32 or uint16 (bf16 bits), got {x.dtype}")
+
+
+def _io_u(u, io_dtype):
+    """u in the io dtype, or float64 (the output of conv_silu)."""
+    if isinstance(u, np.ndarray) and u.dtype == np.float64:
+        return np.ascontiguousarray(u), F64
+    u, dt = _io(u, "u")
+    if dt != io_dtype:
+        raise TypeError("u: io dtype differs from delta's")
+    return u, dt
 
 
 def _f32(x, shape, name):
@@ -131,11 +143,13 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     h0: (batch, d_inner, d_state) float64 or None.  rows: optional 1-D array of row ids
     b*d_inner + d.
 
+    u may instead be float64 (the unrounded output of conv_silu).
+
     Returns (out, h_last): without rows, out is (batch, L, d_inner) and h_last is
     (batch, d_inner, d_state); with rows, out is (len(rows), L) and h_last (len(rows), d_state).
     """
-    u, dt = _io(u, "u")
-    delta, _ = _io(delta, "delta")
+    delta, dt = _io(delta, "delta")
+    u, udt = _io_u(u, dt)
     B, _ = _io(B, "B")
     C, _ = _io(C, "C")
     z, _ = _io(z, "z")
@@ -160,7 +174,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
         nthreads = max(1, len(os.sched_getaffinity(0)))
     rc = _load().oracle_scan_fwd(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt,
+        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt, udt,
         batch, L, d_inner, d_state, _ptr(rows), nrows, _ptr(out), _ptr(h_last), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_scan_fwd rejected its arguments")
@@ -173,8 +187,8 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
 def scan_fwd_chunked(u, delta, A, B, C, chunk, D=None, z=None, delta_bias=None,
                      delta_softplus=True, h0=None, zoh_exact=False):
     """Same result as scan_fwd via the blockwise associative decomposition (block = chunk)."""
-    u, dt = _io(u, "u")
-    delta, _ = _io(delta, "delta")
+    delta, dt = _io(delta, "delta")
+    u, udt = _io_u(u, dt)
     B, _ = _io(B, "B")
     C, _ = _io(C, "C")
     z, _ = _io(z, "z")
@@ -192,7 +206,7 @@ def scan_fwd_chunked(u, delta, A, B, C, chunk, D=None, z=None, delta_bias=None,
     h_last = np.empty((batch * d_inner, d_state), dtype=np.float64)
     rc = _load().oracle_scan_fwd_chunked(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt,
+        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt, udt,
         batch, L, d_inner, d_state, int(chunk), _ptr(out), _ptr(h_last))
     if rc != 0:
         raise ValueError("oracle_scan_fwd_chunked rejected its arguments")
@@ -208,8 +222,8 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if not (isinstance(state, np.ndarray) and state.dtype == np.float64
             and state.flags.c_contiguous):
         raise TypeError("state must be a C-contiguous float64 array (updated in place)")
-    u, dt = _io(u, "u")
-    delta, _ = _io(delta, "delta")
+    delta, dt = _io(delta, "delta")
+    u, udt = _io_u(u, dt)
     B, _ = _io(B, "B")
     C, _ = _io(C, "C")
     z, _ = _io(z, "z")
@@ -232,8 +246,42 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
         nthreads = max(1, len(os.sched_getaffinity(0)))
     rc = _load().oracle_state_update(
         _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-        _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh_exact)), dt,
+        _ptr(delta_bias), int(bool(delta_softplus)), int(bool(zoh_exact)), dt, udt,
         batch, d_inner, d_state, _ptr(rows), nrows, _ptr(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_state_update rejected its arguments")
     return out.reshape(batch, d_inner) if rows is None else out
+
+
+def conv_silu(x, w, b=None, x_prev=None):
+    """The block's front end in fp64: u = silu(causal depthwise conv of x + b), see
+    oracle_conv_silu in ss_oracle.c.  x: (batch, L, d_inner) float32 or bf16 bits; w:
+    (d_inner, k) float32; b: (d_inner,) float32 or None; x_prev: (batch, k-1, d_inner) in x's
+    dtype (the inputs before t = 0) or None for zeros.  Returns u: (batch, L, d_inner) float64."""
+    x, dt = _io(x, "x")
+    batch, L, d_inner = x.shape
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2 or w.shape[0] != d_inner:
+        raise ValueError(f"w: shape {w.shape}, expected ({d_inner}, k)")
+    k = w.shape[1]
+    b = _f32(b, (d_inner,), "b")
+    if x_prev is not None:
+        x_prev, pdt = _io(x_prev, "x_prev")
+        if pdt != dt or x_prev.shape != (batch, k - 1, d_inner):
+            raise ValueError(f"x_prev: expected {(batch, k - 1, d_inner)} in x's dtype")
+    u = np.empty((batch, L, d_inner), dtype=np.float64)
+    rc = _load().oracle_conv_silu(_ptr(x), _ptr(w), _ptr(b), _ptr(x_prev), k, dt, batch, L,
+                                  d_inner, _ptr(u))
+    if rc != 0:
+        raise ValueError("oracle_conv_silu rejected its arguments")
+    return u
+
+
+def conv_step(conv_state, x, w, b=None):
+    """One decode step of the front end: conv_state (batch, k-1, d_inner) holds the k-1 previous
+    inputs (oldest first), x (batch, d_inner) the new one.  Returns (u float64 (batch, d_inner),
+    the new conv_state): the window shifted by one with x appended."""
+    x = np.ascontiguousarray(x)
+    u = conv_silu(x[:, None, :], w, b, x_prev=conv_state)[:, 0, :]
+    new_state = np.concatenate([conv_state, x[:, None, :]], axis=1)[:, 1:, :]
+    return u, np.ascontiguousarray(new_state)

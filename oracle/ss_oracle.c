@@ -44,10 +44,12 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 
-/* Read element i of an io-dtype array exactly (bf16 -> fp32 is a 16-bit shift). */
+/* Read element i of an io-dtype array exactly (bf16 -> fp32 is a 16-bit shift; f64 is only used
+ * for an input u that the convolution front end below produced in double). */
 static double rd(const void* p, int64_t i, int dtype) {
+  if (dtype == OR_F64) return ((const double*)p)[i];
   if (dtype == OR_BF16) {
     uint32_t bits = ((uint32_t)((const uint16_t*)p)[i]) << 16;
     float f;
@@ -88,17 +90,19 @@ static double bbar_factor(double dt, double a, int zoh_exact) {
  *   rows        : row ids r = b*d_inner + d to evaluate; NULL = all rows in order
  *   out         : (nrows, seqlen) f64, out[i*seqlen + t] for rows[i]
  *   h_last      : (nrows, d_state) f64 or NULL
+ * u is read as u_dtype (the io dtype, or f64 when it comes from oracle_conv_silu).
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
                     const void* C, const float* D, const void* z, const float* delta_bias,
                     int delta_softplus, const double* h0, int zoh_exact, int io_dtype,
-                    int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                    int u_dtype, int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                     const int64_t* rows, int64_t nrows, double* out, double* h_last,
                     int nthreads) {
   if (!u || !delta || !A || !B || !C || !out) return -1;
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > 256) return -1;
   if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  if (u_dtype != io_dtype && u_dtype != OR_F64) return -1;
   if (!rows) nrows = batch * d_inner;
   if (nthreads < 1) nthreads = 1;
   int bad = 0;
@@ -112,7 +116,7 @@ int oracle_scan_fwd(const void* u, const void* delta, const float* A, const void
     for (int64_t t = 0; t < seqlen; ++t) {
       int64_t e = (b * seqlen + t) * d_inner + d;      /* (b, t, d) element */
       int64_t bc = (b * seqlen + t) * d_state;         /* (b, t, 0) of B and C */
-      double x = rd(u, e, io_dtype);
+      double x = rd(u, e, u_dtype);
       double dt = step_size(rd(delta, e, io_dtype), delta_bias, d, delta_softplus);
       double y = 0.0;
       for (int64_t n = 0; n < d_state; ++n) {
@@ -144,12 +148,14 @@ int oracle_scan_fwd(const void* u, const void* delta, const float* A, const void
 int oracle_scan_fwd_chunked(const void* u, const void* delta, const float* A, const void* B,
                             const void* C, const float* D, const void* z,
                             const float* delta_bias, int delta_softplus, const double* h0,
-                            int zoh_exact, int io_dtype, int64_t batch, int64_t seqlen,
+                            int zoh_exact, int io_dtype, int u_dtype, int64_t batch,
+                            int64_t seqlen,
                             int64_t d_inner, int64_t d_state, int64_t chunk, double* out,
                             double* h_last) {
   if (!u || !delta || !A || !B || !C || !out) return -1;
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > 256 || chunk < 1)
     return -1;
+  if (u_dtype != io_dtype && u_dtype != OR_F64) return -1;
   for (int64_t r = 0; r < batch * d_inner; ++r) {
     int64_t b = r / d_inner, d = r % d_inner;
     double h_in[256], hloc[256], prod[256];
@@ -160,7 +166,7 @@ int oracle_scan_fwd_chunked(const void* u, const void* delta, const float* A, co
       for (int64_t t = t0; t < t1; ++t) {
         int64_t e = (b * seqlen + t) * d_inner + d;
         int64_t bc = (b * seqlen + t) * d_state;
-        double x = rd(u, e, io_dtype);
+        double x = rd(u, e, u_dtype);
         double dt = step_size(rd(delta, e, io_dtype), delta_bias, d, delta_softplus);
         double y = 0.0;
         for (int64_t n = 0; n < d_state; ++n) {
@@ -194,11 +200,13 @@ int oracle_scan_fwd_chunked(const void* u, const void* delta, const float* A, co
 int oracle_state_update(double* state, const void* u, const void* delta, const float* A,
                         const void* B, const void* C, const float* D, const void* z,
                         const float* delta_bias, int delta_softplus, int zoh_exact,
-                        int io_dtype, int64_t batch, int64_t d_inner, int64_t d_state,
-                        const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+                        int io_dtype, int u_dtype, int64_t batch, int64_t d_inner,
+                        int64_t d_state, const int64_t* rows, int64_t nrows, double* out,
+                        int nthreads) {
   if (!state || !u || !delta || !A || !B || !C || !out) return -1;
   if (batch < 0 || d_inner < 0 || d_state < 1 || d_state > 256) return -1;
   if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  if (u_dtype != io_dtype && u_dtype != OR_F64) return -1;
   if (!rows) nrows = batch * d_inner;
   if (nthreads < 1) nthreads = 1;
   int bad = 0;
@@ -207,7 +215,7 @@ int oracle_state_update(double* state, const void* u, const void* delta, const f
     int64_t r = rows ? rows[i] : i;
     if (r < 0 || r >= batch * d_inner) { bad = 1; continue; }
     int64_t b = r / d_inner, d = r % d_inner;
-    double x = rd(u, r, io_dtype);
+    double x = rd(u, r, u_dtype);
     double dt = step_size(rd(delta, r, io_dtype), delta_bias, d, delta_softplus);
     double y = 0.0;
     for (int64_t n = 0; n < d_state; ++n) {
@@ -221,6 +229,41 @@ int oracle_state_update(double* state, const void* u, const void* delta, const f
     out[i] = y;
   }
   return bad ? -1 : 0;
+}
+
+/*
+ * Front end of the block's SSM path [P2 Mamba block: x_proj goes through a one-dimensional
+ * convolution whose output passes SiLU, giving x_act, the SSM's input].  The convolution is
+ * depthwise (one kernel per channel) over time and causal (output t sees inputs up to t only, as
+ * a sequence model run token by token must; [P5] installs the causal-conv1d package), width k:
+ *   u[b,t,d] = silu( conv_b[d] + sum_{j=0}^{k-1} conv_w[d*k + j] * x[b, t-(k-1)+j, d] )
+ * Inputs before t = 0 are x_prev[b, k-1+t', d] for t' = t-(k-1)+j < 0 (the k-1 steps that came
+ * before), or 0 when x_prev is NULL.  conv_b NULL means 0.
+ *   x      : (batch, seqlen, d_inner) io dtype;  x_prev : (batch, k-1, d_inner) io dtype
+ *   conv_w : (d_inner, k) f32;  conv_b : (d_inner) f32
+ *   u      : (batch, seqlen, d_inner) f64 output, unrounded
+ */
+int oracle_conv_silu(const void* x, const float* conv_w, const float* conv_b,
+                     const void* x_prev, int64_t k, int io_dtype, int64_t batch,
+                     int64_t seqlen, int64_t d_inner, double* u) {
+  if (!x || !conv_w || !u || k < 1 || batch < 0 || seqlen < 0 || d_inner < 0) return -1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t t = 0; t < seqlen; ++t)
+      for (int64_t d = 0; d < d_inner; ++d) {
+        double acc = conv_b ? (double)conv_b[d] : 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+          int64_t ts = t - (k - 1) + j; /* time of the input this tap multiplies */
+          double xv;
+          if (ts >= 0)
+            xv = rd(x, (b * seqlen + ts) * d_inner + d, io_dtype);
+          else
+            xv = x_prev ? rd(x_prev, (b * (k - 1) + (k - 1) + ts) * d_inner + d, io_dtype) : 0.0;
+          acc += (double)conv_w[d * k + j] * xv;
+        }
+        u[(b * seqlen + t) * d_inner + d] = silu(acc);
+      }
+  return 0;
 }
 
 /* Number of threads OpenMP would use by default (for reporting the CPU baseline). */

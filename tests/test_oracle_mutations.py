@@ -6,6 +6,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_conv as conv_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
@@ -42,9 +43,24 @@ MUTATIONS = [
      "      double hn = exp(dt * a) * (*h) + bbar_factor"),
     ("chunk carry dropped", "          y += rd(C, bc + n, io_dtype) * (hloc[n] + prod[n] * h_in[n]);",
      "          y += rd(C, bc + n, io_dtype) * hloc[n];"),
+    ("conv taps reversed", "          int64_t ts = t - (k - 1) + j;", "          int64_t ts = t - j;"),
+    ("conv bias dropped", "        double acc = conv_b ? (double)conv_b[d] : 0.0;",
+     "        double acc = 0.0;"),
+    ("conv history ignored",
+     "            xv = x_prev ? rd(x_prev, (b * (k - 1) + (k - 1) + ts) * d_inner + d, io_dtype) : 0.0;",
+     "            xv = 0.0;"),
+    ("conv without silu", "        u[(b * seqlen + t) * d_inner + d] = silu(acc);",
+     "        u[(b * seqlen + t) * d_inner + d] = acc;"),
+    ("conv looks ahead", "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + ts) * d_inner + d, io_dtype);",
+     "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + (ts + 1 < seqlen ? ts + 1 : ts)) * d_inner + d, io_dtype);"),
 ]
 
 PIN_CALLS = [
+    lambda: conv_pins.test_matches_numpy_convolution(4, False, True),
+    lambda: conv_pins.test_matches_numpy_convolution(2, True, False),
+    conv_pins.test_last_tap_only_is_pointwise_silu,
+    conv_pins.test_first_tap_only_is_a_delay,
+    conv_pins.test_causal,
     lambda: pins.test_golden_worked_examples("gated_rnn", False),
     lambda: pins.test_golden_worked_examples("gated_rnn", True),
     lambda: pins.test_golden_worked_examples("sum_and_reset", False),
