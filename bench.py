@@ -173,6 +173,27 @@ def bench_prefill(args, torch, np, ops, wl):
     ms_zoh = sum(a_.elapsed_time(b_) for a_, b_ in zs) / zsteps
     log(f"prefill exact-hold kernel avg {ms_zoh * 1e3:.1f} us")
 
+    # the same layer with the block's front end fused in (ss_scan_fwd_conv): the benchmark's u
+    # plays x, and u = silu(causal depthwise conv of width 4 + bias) is formed in the kernel
+    g = torch.Generator(device="cuda").manual_seed(77)
+    cw = 0.5 * torch.randn((w.d_inner, 4), device="cuda", generator=g)
+    cbias = 0.2 * torch.randn((w.d_inner,), device="cuda", generator=g)
+    conv_out = torch.empty_like(u)
+    for _ in range(2):
+        ops.scan_fwd_conv(u, cw, cbias, dl, A, B, C, D=D, z=z, delta_bias=db, out=conv_out,
+                          workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    cs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(zsteps)]
+    for a_, b_ in cs:
+        a_.record(stream)
+        ops.scan_fwd_conv(u, cw, cbias, dl, A, B, C, D=D, z=z, delta_bias=db, out=conv_out,
+                          workspace=ws, stream=stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms_conv = sum(a_.elapsed_time(b_) for a_, b_ in cs) / zsteps
+    log(f"prefill with fused conv front end kernel avg {ms_conv * 1e3:.1f} us")
+
     # spot parity check of the benchmarked output on a few rows
     import oracle
     rows = np.array([0, 1, w.d_inner - 1, (w.batch - 1) * w.d_inner + w.d_inner // 2],
@@ -189,7 +210,24 @@ def bench_prefill(args, torch, np, ops, wl):
                             delta_bias=p["delta_bias"], rows=rows, zoh_exact=True)
     errz = np.abs(gz - rz)
     ok = ok and bool(np.all(errz <= 2e-2 + 2e-2 * np.abs(rz)))
-    return w, p, ms_step, ms_kernel, ms_zoh, ok, float(max(err.max(), errz.max()))
+    # fused front end: oracle conv_silu on the sampled rows' channels, then the scan
+    sel_b, sel_d = rows // w.d_inner, rows % w.d_inner
+    cw_h, cb_h = cw.cpu().numpy(), cbias.cpu().numpy()
+    gc = conv_out.float()[torch.from_numpy(sel_b).cuda(), :,
+                          torch.from_numpy(sel_d).cuda()].cpu().numpy().astype(np.float64)
+    errc = 0.0
+    for i, (bi, di) in enumerate(zip(sel_b, sel_d)):
+        one = lambda k: np.ascontiguousarray(p[k][bi:bi + 1, :, di:di + 1])
+        uc = oracle.conv_silu(one("u"), cw_h[di:di + 1], cb_h[di:di + 1])
+        rc, _ = oracle.scan_fwd(uc, one("delta"), p["A"][di:di + 1],
+                                np.ascontiguousarray(p["B"][bi:bi + 1]),
+                                np.ascontiguousarray(p["C"][bi:bi + 1]), D=p["D"][di:di + 1],
+                                z=one("z"), delta_bias=p["delta_bias"][di:di + 1])
+        e = np.abs(gc[i] - rc[0, :, 0])
+        ok = ok and bool(np.all(e <= 2e-2 + 2e-2 * np.abs(rc[0, :, 0])))
+        errc = max(errc, float(e.max()))
+    return (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ok,
+            float(max(err.max(), errz.max(), errc)))
 
 
 def bench_decode(args, torch, np, ops, wl):
@@ -365,7 +403,8 @@ def main():
         return
     ops.lib()
 
-    w, p, ms_step, ms_kernel, ms_zoh, ok, maxerr = bench_prefill(args, torch, np, ops, wl)
+    w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ok, maxerr = bench_prefill(args, torch, np, ops,
+                                                                         wl)
     elems = w.elements
     value = elems / (ms_step * 1e-3)
     nbytes = prefill_bytes(w)
@@ -401,6 +440,12 @@ def main():
                       "elements_per_s": round(elems / (ms_zoh * 1e-3), 1),
                       "note": "same layer with the exact zero-order-hold input term; its extra "
                               "per-update work (series or (2^y-1)/y) is not in the slot count"},
+        "conv_front_end": {"kernel_us": round(ms_conv * 1e3, 2),
+                           "elements_per_s": round(elems / (ms_conv * 1e-3), 1),
+                           "hbm_bytes_avoided": 2 * elems * (2 if w.io_dtype == "bf16" else 4),
+                           "note": "ss_scan_fwd_conv, width-4 causal depthwise conv + SiLU on x "
+                                   "fused in; an unfused front end would write u and read it "
+                                   "back (hbm_bytes_avoided)"},
         "parity_spot_check": {"ok": ok, "max_abs_err": maxerr},
     }
     if not args.no_decode:

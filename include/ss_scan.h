@@ -111,6 +111,32 @@ size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_i
                                       int64_t d_state, ss_dtype dtype, int32_t nseg);
 
 /*
+ * Prefill with the block's front end fused in: instead of u the call takes the block's x and
+ * forms the SSM input itself (IBM explainer, Mamba-block walk-through: x_proj passes a
+ * one-dimensional convolution, then SiLU, and the result feeds the SSM):
+ *
+ *     u[b,t,d] = silu( conv_bias[d] + sum_{j<conv_k} conv_weight[d,j] * x[b, t-conv_k+1+j, d] )
+ *
+ * a causal (step t sees x up to t), depthwise (one kernel per channel) convolution of width
+ * conv_k in 1..4 (the pages give no width; 4 is the usual choice).  u is kept in float32 and
+ * never written to memory.  Everything else is ss_scan_fwd_ex with u replaced by:
+ *   x            : (batch, seqlen, d_inner), io dtype.
+ *   conv_weight  : (d_inner, conv_k) float32, required.
+ *   conv_bias    : (d_inner) float32; NULL means 0.
+ *   x_prev       : (batch, conv_k - 1, d_inner), io dtype: the conv_k - 1 inputs that came
+ *                  before t = 0 (oldest first), e.g. the end of the previous call's x; NULL
+ *                  means zeros.
+ * conv_k outside 1..4 -> SS_ERR_UNSUPPORTED; conv_weight NULL -> SS_ERR_INVALID_ARG.
+ */
+ss_status ss_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
+                           const void* x_prev, int32_t conv_k, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, int delta_softplus, const float* h0,
+                           float* h_last, void* out, int64_t batch, int64_t seqlen,
+                           int64_t d_inner, int64_t d_state, ss_dtype dtype, void* workspace,
+                           size_t workspace_bytes, int32_t nseg, uint32_t flags, void* stream);
+
+/*
  * Decode: advance a resident state by ONE token (the recurrence above for a single t).
  *
  *   state        : (batch, d_inner, d_state) float32, read and overwritten IN PLACE.

@@ -106,7 +106,9 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
                     int delta_softplus, const float* h0, float* h_last, void* out, int64_t batch,
                     int64_t seqlen, int64_t d_inner, int64_t d_state, ss_dtype dtype,
                     void* workspace, size_t workspace_bytes, int32_t nseg_req, bool forced,
-                    uint32_t flags, void* stream) {
+                    uint32_t flags, void* stream, const float* conv_w = nullptr,
+                    const float* conv_b = nullptr, const void* x_prev = nullptr,
+                    int32_t conv_k = 0) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
@@ -117,6 +119,8 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
   if (d_state < 1 || d_state > 64)
     return fail(SS_ERR_UNSUPPORTED, "d_state=%lld outside 1..64", (long long)d_state);
   if (nseg_req < 0) return fail(SS_ERR_INVALID_ARG, "nseg=%d is negative", nseg_req);
+  if (conv_w && (conv_k < 1 || conv_k > 4))
+    return fail(SS_ERR_UNSUPPORTED, "conv_k=%d outside 1..4", conv_k);
   int64_t rows, elems, bc_elems, st_elems;
   if (!mul_ok(batch, d_inner, &rows) || !mul_ok(rows, seqlen, &elems) ||
       !mul_ok(batch * seqlen, d_state, &bc_elems) || !mul_ok(rows, d_state, &st_elems) ||
@@ -147,12 +151,12 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
   if (!u || !delta || !A || !B || !C || !out)
     return fail(SS_ERR_INVALID_ARG, "required pointer is NULL (u, delta, A, B, C and out are "
                 "required)");
-  const void* io_ptrs[] = {u, delta, B, C, z, out};
+  const void* io_ptrs[] = {u, delta, B, C, z, out, x_prev};
   for (const void* p : io_ptrs)
     if (p && !aligned(p, es))
       return fail(SS_ERR_UNSUPPORTED, "io pointer %p not aligned to its %lld-byte element", p,
                   (long long)es);
-  const void* f_ptrs[] = {A, D, delta_bias, h0, h_last};
+  const void* f_ptrs[] = {A, D, delta_bias, h0, h_last, conv_w, conv_b};
   for (const void* p : f_ptrs)
     if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
   if (int64_t(d_inner) * d_state > (int64_t(1) << 40))
@@ -162,7 +166,10 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
                        range("z", z, elems, es), range("B", B, bc_elems, es),
                        range("C", C, bc_elems, es), range("A", A, d_inner * d_state, 4),
                        range("D", D, d_inner, 4), range("delta_bias", delta_bias, d_inner, 4),
-                       range("h0", h0, st_elems, 4)};
+                       range("h0", h0, st_elems, 4),
+                       range("conv_w", conv_w, d_inner * conv_k, 4),
+                       range("conv_b", conv_w ? conv_b : nullptr, d_inner, 4),
+                       range("x_prev", conv_w ? x_prev : nullptr, batch * (conv_k - 1) * d_inner, es)};
   const Range ro = range("out", out, elems, es);
   const Range rh = range("h_last", h_last, st_elems, 4);
   for (const Range& in : ins) {
@@ -202,6 +209,12 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
   a.nseg = nseg;
   a.softplus = delta_softplus ? 1 : 0;
   a.zoh = (flags & SS_FLAG_ZOH_EXACT) ? 1 : 0;
+  if (conv_w) {
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    a.x_prev = conv_k > 1 ? x_prev : nullptr;
+    a.conv_k = conv_k;
+  }
   // 16-byte tile accesses need whole 16-channel blocks and 16-byte aligned rows
   a.vec_io = (d_inner % ss::kChanPerWG == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
               aligned(delta, 16) && (!z || aligned(z, 16)) && aligned(out, 16)) ? 1 : 0;
@@ -332,6 +345,19 @@ size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_i
   int32_t n;
   segments(seqlen, nseg > 0 ? nseg : auto_nseg(batch, seqlen, d_inner), &seg_len, &n);
   return ws_bytes(batch, d_inner, d_state, n);
+}
+
+ss_status ss_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,
+                           const void* x_prev, int32_t conv_k, const void* delta, const float* A,
+                           const void* B, const void* C, const float* D, const void* z,
+                           const float* delta_bias, int delta_softplus, const float* h0,
+                           float* h_last, void* out, int64_t batch, int64_t seqlen,
+                           int64_t d_inner, int64_t d_state, ss_dtype dtype, void* workspace,
+                           size_t workspace_bytes, int32_t nseg, uint32_t flags, void* stream) {
+  if (!conv_weight) return fail(SS_ERR_INVALID_ARG, "conv_weight is NULL");
+  return scan_impl(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, nseg, true, flags,
+                   stream, conv_weight, conv_bias, x_prev, conv_k);
 }
 
 ss_status ss_state_update(float* state, const void* u, const void* delta, const float* A,

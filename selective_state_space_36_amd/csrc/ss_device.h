@@ -121,6 +121,15 @@ __device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// Value of `x` held by lane (k - S) mod 16 of this lane's 16-lane row, k being this lane's
+// index in the row (DPP row_ror:S).
+template <int S>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(S >= 1 && S < 16, "rotation");
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + S, 0xf, 0xf, false));
+}
+
 // Make this wavefront's LDS writes visible to all of its lanes (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

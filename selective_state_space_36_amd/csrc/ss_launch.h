@@ -37,6 +37,11 @@ struct ScanArgs {
   int32_t softplus;
   int32_t vec_io;      // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, out
   int32_t zoh;         // exact zero-order-hold input term instead of dt * B
+  // front end (conv_w != nullptr): u holds the block's x; u = silu(causal conv of x + conv_b)
+  const float* conv_w;  // (d_inner, conv_k)
+  const float* conv_b;  // (d_inner), nullptr: 0
+  const void* x_prev;   // (batch, conv_k - 1, d_inner) io dtype: x before t = 0; nullptr: 0
+  int32_t conv_k;       // 1..4
 };
 
 struct DecodeArgs {
@@ -62,6 +67,8 @@ struct DecodeArgs {
 // local end states and dt sums into seg_h/seg_dt); otherwise the output pass over all segments.
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
 hipError_t launch_scan_zoh(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
+hipError_t launch_scan_conv(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
+hipError_t launch_scan_conv_zoh(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream);
 
 // Fill h_last with h0 (or zeros) when the sequence is empty.
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -1,5 +1,6 @@
-// ss_scan_fwd.hip -- prefill launches with the first-order input term dt B u (the default), the
-// dispatch to the exact zero-order-hold instances, and the empty-sequence state copy.
+// ss_scan_fwd.hip -- prefill launches with the first-order input term dt B u and u given (the
+// default), the dispatch to the exact zero-order-hold and convolution front-end instances, and
+// the empty-sequence state copy.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,8 +18,11 @@ __global__ void __launch_bounds__(256) copy_state_kernel(float* dst, const float
 }  // namespace
 
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream) {
+  if (a.conv_w)
+    return a.zoh ? launch_scan_conv_zoh(a, bf16, summary, stream)
+                 : launch_scan_conv(a, bf16, summary, stream);
   if (a.zoh) return launch_scan_zoh(a, bf16, summary, stream);
-  return launch_scan_instances<false>(a, bf16, summary, stream);
+  return launch_scan_instances<false, false>(a, bf16, summary, stream);
 }
 
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t stream) {

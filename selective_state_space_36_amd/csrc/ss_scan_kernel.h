@@ -7,6 +7,12 @@
 //     y_t = C_t . h_t + D u_t,  out = y_t * silu(z_t).
 // With ZOH the input term is the exact zero-order-hold one, (exp(dt_t A) - 1) / A * B_t u_t
 // (reading guide, "Método"), in place of the first-order dt_t B_t u_t.
+// With CONV the kernel reads the block's x instead of u and forms u itself (IBM explainer,
+// Mamba-block walk-through: x passes a 1-D convolution, then SiLU):
+//     u_t = silu(conv_b + sum_{j<k} conv_w[j] x_{t-k+1+j}),   k <= 4, causal, per channel,
+// so u never makes a round trip through HBM.  The owner lane of step t holds x_t; the earlier
+// taps come from the lanes of steps t-1..t-3 by DPP row rotations, from the previous chunk's
+// values for the first three steps of a chunk.
 // The (batch, L, d_inner, d_state) state never leaves registers; only y reaches HBM (reading
 // guide, "Expansão de Estado Ciente de Hardware").
 //
@@ -50,7 +56,7 @@ constexpr int kPRow = 336;               // floats per channel row of the partia
 constexpr int kPTau = 20;                // floats per step of the partial tile (padding)
 static_assert(kT == 16, "one chunk step per row lane");
 
-template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC, bool ZOH>
+template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC, bool ZOH, bool CONV>
 struct ScanKernel {
   using elem = typename IO::elem;
   static constexpr int NP = 16 * NL;                         // padded state count
@@ -102,6 +108,31 @@ struct ScanKernel {
     }
     const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
     const float dskip = (!SUMMARY && chan_ok && a.D) ? a.D[d] : 0.0f;
+
+    // Front end (CONV): tap weights of a 4-wide window ending at this lane's step, split by
+    // whether the tap's step lies in this chunk (cw_cur) or the previous one (cw_prev), and the
+    // lane's x of the previous chunk (for the first chunk, x before the segment: from x itself,
+    // from the caller's history x_prev before t = 0, or 0).
+    float cw_own = 0.0f, cbias = 0.0f, cw_cur[3] = {0.0f, 0.0f, 0.0f};
+    float cw_prev[3] = {0.0f, 0.0f, 0.0f};
+    float xprev = 0.0f;
+    if (CONV && chan_ok) {
+      const int K = a.conv_k;
+#pragma unroll
+      for (int s = 1; s <= 3; ++s) {  // tap at step t - s
+        const float w = s < K ? a.conv_w[d * K + (K - 1 - s)] : 0.0f;
+        cw_cur[s - 1] = k >= s ? w : 0.0f;
+        cw_prev[s - 1] = k < s ? w : 0.0f;
+      }
+      cw_own = a.conv_w[d * K + (K - 1)];
+      cbias = a.conv_b ? a.conv_b[d] : 0.0f;
+      const int64_t tp = t_begin - kT + k;  // the step this lane held in the "previous chunk"
+      if (tp >= 0)
+        xprev = IO::load(static_cast<const elem*>(a.u), (b * a.seqlen + tp) * a.d_inner + d);
+      else if (a.x_prev && tp >= -(K - 1))
+        xprev = IO::load(static_cast<const elem*>(a.x_prev),
+                         (b * (K - 1) + (K - 1) + tp) * a.d_inner + d);
+    }
 
     if (!SUMMARY) {
       // Initial state of this segment: h0 carried through the summaries of segments 0..seg-1.
@@ -246,7 +277,19 @@ struct ScanKernel {
       if (has_next) load_chunk(ci + 1);
 
       const bool own_ok = chan_ok && k < nvalid_of(ci);
-      const float xu = own_in(buf, 0);
+      float xu = own_in(buf, 0);
+      if (CONV) {  // xu holds x_t here; u_t = silu(conv)
+        const float xc = xu;
+        float acc = fmaf(cw_own, xc, cbias);
+        acc = fmaf(cw_cur[0], row_ror<1>(xc), acc);
+        acc = fmaf(cw_prev[0], row_ror<1>(xprev), acc);
+        acc = fmaf(cw_cur[1], row_ror<2>(xc), acc);
+        acc = fmaf(cw_prev[1], row_ror<2>(xprev), acc);
+        acc = fmaf(cw_cur[2], row_ror<3>(xc), acc);
+        acc = fmaf(cw_prev[2], row_ror<3>(xprev), acc);
+        xprev = xc;
+        xu = silu_f(acc);
+      }
       const float sv = own_in(buf, 1) + bias;
       float dt = a.softplus ? softplus_f(sv) : sv;
       dt = own_ok ? dt : 0.0f;  // steps past the end leave h unchanged
@@ -373,47 +416,50 @@ struct ScanKernel {
   }
 };
 
-template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC, bool ZOH>
+template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC, bool ZOH, bool CONV>
 __global__ void __launch_bounds__(kPrefillThreads) scan_kernel(ScanArgs a) {
-  ScanKernel<IO, NL, GATE, SUMMARY, VEC, ZOH>::run(a);
+  ScanKernel<IO, NL, GATE, SUMMARY, VEC, ZOH, CONV>::run(a);
 }
 
-template <class IO, int NL, bool VEC, bool ZOH>
+template <class IO, int NL, bool VEC, bool ZOH, bool CONV>
 hipError_t launch3(const ScanArgs& a, bool summary, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.n_wg)), block(kPrefillThreads);
   if (summary)
-    hipLaunchKernelGGL((scan_kernel<IO, NL, false, true, VEC, ZOH>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((scan_kernel<IO, NL, false, true, VEC, ZOH, CONV>), grid, block, 0, stream,
+                       a);
   else if (a.z != nullptr)
-    hipLaunchKernelGGL((scan_kernel<IO, NL, true, false, VEC, ZOH>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((scan_kernel<IO, NL, true, false, VEC, ZOH, CONV>), grid, block, 0, stream,
+                       a);
   else
-    hipLaunchKernelGGL((scan_kernel<IO, NL, false, false, VEC, ZOH>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((scan_kernel<IO, NL, false, false, VEC, ZOH, CONV>), grid, block, 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-template <class IO, int NL, bool ZOH>
+template <class IO, int NL, bool ZOH, bool CONV>
 hipError_t launch2(const ScanArgs& a, bool summary, hipStream_t stream) {
-  return a.vec_io ? launch3<IO, NL, true, ZOH>(a, summary, stream)
-                  : launch3<IO, NL, false, ZOH>(a, summary, stream);
+  return a.vec_io ? launch3<IO, NL, true, ZOH, CONV>(a, summary, stream)
+                  : launch3<IO, NL, false, ZOH, CONV>(a, summary, stream);
 }
 
-// Instance selection for one discretisation: io dtype, state registers per lane (NL), 16-byte
-// tile path, gate and pass.
-template <bool ZOH>
+// Instance selection for one discretisation and front end: io dtype, state registers per lane
+// (NL), 16-byte tile path, gate and pass.
+template <bool ZOH, bool CONV>
 hipError_t launch_scan_instances(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream) {
   const int nl = (a.d_state + 15) / 16;
   if (bf16) {
     switch (nl) {
-      case 1: return launch2<BF16, 1, ZOH>(a, summary, stream);
-      case 2: return launch2<BF16, 2, ZOH>(a, summary, stream);
-      case 3: return launch2<BF16, 3, ZOH>(a, summary, stream);
-      default: return launch2<BF16, 4, ZOH>(a, summary, stream);
+      case 1: return launch2<BF16, 1, ZOH, CONV>(a, summary, stream);
+      case 2: return launch2<BF16, 2, ZOH, CONV>(a, summary, stream);
+      case 3: return launch2<BF16, 3, ZOH, CONV>(a, summary, stream);
+      default: return launch2<BF16, 4, ZOH, CONV>(a, summary, stream);
     }
   }
   switch (nl) {
-    case 1: return launch2<F32, 1, ZOH>(a, summary, stream);
-    case 2: return launch2<F32, 2, ZOH>(a, summary, stream);
-    case 3: return launch2<F32, 3, ZOH>(a, summary, stream);
-    default: return launch2<F32, 4, ZOH>(a, summary, stream);
+    case 1: return launch2<F32, 1, ZOH, CONV>(a, summary, stream);
+    case 2: return launch2<F32, 2, ZOH, CONV>(a, summary, stream);
+    case 3: return launch2<F32, 3, ZOH, CONV>(a, summary, stream);
+    default: return launch2<F32, 4, ZOH, CONV>(a, summary, stream);
   }
 }
 

@@ -10,7 +10,7 @@
 namespace ss {
 
 hipError_t launch_scan_zoh(const ScanArgs& a, bool bf16, bool summary, hipStream_t stream) {
-  return launch_scan_instances<true>(a, bf16, summary, stream);
+  return launch_scan_instances<true, false>(a, bf16, summary, stream);
 }
 
 }  // namespace ss

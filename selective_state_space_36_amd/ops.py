@@ -29,6 +29,9 @@ SIGNATURES = {
     "ss_scan_fwd_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
                               _vp, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32, _u32, _vp]),
     "ss_scan_fwd_ex_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
+    "ss_scan_fwd_conv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp,
+                                _sz, _i32, _u32, _vp]),
     "ss_state_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                _i64, _i64, _i64, _i32, _vp]),
     "ss_state_update_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
@@ -151,6 +154,49 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     else:
         flags = SS_FLAG_ZOH_EXACT if zoh_exact else 0
         _check(lib().ss_scan_fwd_ex(*args, int(nseg or 0), flags, _stream(stream)))
+    return (out, h_last) if return_last_state else out
+
+
+def scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, delta_bias=None,
+                  delta_softplus=True, x_prev=None, h0=None, return_last_state=False, out=None,
+                  h_last=None, workspace=None, nseg=None, zoh_exact=False, stream=None):
+    """Prefill with the fused front end (ss_scan_fwd_conv): u = silu(causal depthwise conv of x).
+
+    x: (batch, L, d_inner) in the io dtype; conv_weight: (d_inner, k) float32, k in 1..4;
+    conv_bias: (d_inner,) float32 or None; x_prev: (batch, k-1, d_inner) io dtype or None.  The
+    rest as in scan_fwd.
+    """
+    batch, L, d_inner = x.shape
+    d_state = B.shape[-1]
+    code = _dtype_code(x)
+    k = conv_weight.shape[-1]
+    for name, t in (("x", x), ("delta", delta), ("z", z)):
+        _dev(t, name, x.dtype, (batch, L, d_inner))
+    for name, t in (("B", B), ("C", C)):
+        _dev(t, name, x.dtype, (batch, L, d_state))
+    _dev(conv_weight, "conv_weight", torch.float32, (d_inner, k))
+    _dev(conv_bias, "conv_bias", torch.float32, (d_inner,))
+    _dev(x_prev, "x_prev", x.dtype, (batch, k - 1, d_inner))
+    _dev(A, "A", torch.float32, (d_inner, d_state))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(delta_bias, "delta_bias", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, d_state))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype, (batch, L, d_inner))
+    if return_last_state and h_last is None:
+        h_last = torch.empty((batch, d_inner, d_state), dtype=torch.float32, device=x.device)
+    _dev(h_last, "h_last", torch.float32, (batch, d_inner, d_state))
+    if workspace is None:
+        nbytes = workspace_bytes(batch, L, d_inner, d_state, x.dtype, nseg)
+        workspace = (torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes
+                     else None)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ss_scan_fwd_conv(
+        _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(x_prev), int(k), _ptr(delta), _ptr(A),
+        _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), 1 if delta_softplus else 0,
+        _ptr(h0), _ptr(h_last), _ptr(out), batch, L, d_inner, d_state, code, _ptr(workspace),
+        ws_len, int(nseg or 0), SS_FLAG_ZOH_EXACT if zoh_exact else 0, _stream(stream)))
     return (out, h_last) if return_last_state else out
 
 
