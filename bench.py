@@ -65,12 +65,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# Sources each measured kernel is built from: a counter summary under profiles/ stays valid only
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "mamba2.8b-prefill": ["ss_device.h", "ss_launch.h", "ss_scan_kernel.h", "ss_scan_fwd.hip"],
+    "decode-b128": ["ss_device.h", "ss_launch.h", "ss_state_update.hip"],
+}
+
+
+def kernel_source_hash(name: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_36_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
+    for fname in sorted(KERNEL_SOURCES[name]):
+        with open(os.path.join(csrc, fname), "rb") as f:
+            h.update(fname.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -88,7 +96,7 @@ def measured_traffic(name: str):
             key, sep, val = line.partition(":")
             if sep:
                 vals[key.strip()] = val.strip()
-    if vals.get("source_hash") != kernel_source_hash():
+    if vals.get("source_hash") != kernel_source_hash(name):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
