@@ -79,6 +79,9 @@ def _bind(lib):
                                         i32, i64, i64, i64, vp, i64, vp, i32]
     lib.oracle_conv_silu.argtypes = [vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
     lib.oracle_conv_silu.restype = i32
+    lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64,
+                                    i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_scan_bwd.restype = i32
     lib.oracle_state_update.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
@@ -285,3 +288,44 @@ def conv_step(conv_state, x, w, b=None):
     u = conv_silu(x[:, None, :], w, b, x_prev=conv_state)[:, 0, :]
     new_state = np.concatenate([conv_state, x[:, None, :]], axis=1)[:, 1:, :]
     return u, np.ascontiguousarray(new_state)
+
+
+def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, dh_last=None):
+    """fp64 gradients of scan_fwd (first-order discretisation) for upstream gradients dout
+    (batch, L, d_inner) and dh_last (batch, d_inner, d_state) or None.  Inputs as for scan_fwd
+    (u in the io dtype).  Returns a dict with du, ddelta, dz (None without z), dA, dB, dC, dD,
+    ddelta_bias, dh0 -- float64 arrays shaped like the corresponding inputs."""
+    delta, dt = _io(delta, "delta")
+    u, udt = _io_u(u, dt)
+    if udt != dt:
+        raise TypeError("scan_bwd takes u in the io dtype")
+    B, _ = _io(B, "B")
+    C, _ = _io(C, "C")
+    z, _ = _io(z, "z")
+    batch, L, d_inner = u.shape
+    d_state = B.shape[2]
+    _check_io([("delta", delta), ("z", z), ("B", B), ("C", C)],
+              [(batch, L, d_inner), (batch, L, d_inner), (batch, L, d_state),
+               (batch, L, d_state)], dt)
+    A = _f32(A, (d_inner, d_state), "A")
+    D = _f32(D, (d_inner,), "D")
+    delta_bias = _f32(delta_bias, (d_inner,), "delta_bias")
+    if h0 is not None:
+        h0 = np.ascontiguousarray(h0, dtype=np.float64).reshape(batch, d_inner, d_state)
+    dout = np.ascontiguousarray(dout, dtype=np.float64).reshape(batch, L, d_inner)
+    if dh_last is not None:
+        dh_last = np.ascontiguousarray(dh_last, dtype=np.float64).reshape(batch, d_inner, d_state)
+    g = dict(du=np.empty((batch, L, d_inner)), ddelta=np.empty((batch, L, d_inner)),
+             dz=np.empty((batch, L, d_inner)) if z is not None else None,
+             dA=np.empty((d_inner, d_state)), dB=np.empty((batch, L, d_state)),
+             dC=np.empty((batch, L, d_state)), dD=np.empty(d_inner),
+             ddelta_bias=np.empty(d_inner), dh0=np.empty((batch, d_inner, d_state)))
+    rc = _load().oracle_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        int(bool(delta_softplus)), _ptr(h0), dt, batch, L, d_inner, d_state, _ptr(dout),
+        _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]),
+        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]))
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd rejected its arguments")
+    return g

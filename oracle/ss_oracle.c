@@ -38,6 +38,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -263,6 +264,111 @@ int oracle_conv_silu(const void* x, const float* conv_w, const float* conv_b,
         }
         u[(b * seqlen + t) * d_inner + d] = silu(acc);
       }
+  return 0;
+}
+
+/*
+ * Gradients of the prefill (first-order Bbar = dt B) by reverse-mode differentiation of the
+ * recurrence, in double.  For one row (b, d), with x_t = u, s_t = delta + bias, dt_t =
+ * softplus(s_t), e_{t,n} = exp(dt_t a_n), h_t = e_t h_{t-1} + dt_t B_t x_t,
+ * y_t = C_t . h_t + D x_t and out_t = y_t silu(z_t), given g_t = dL/d out_t and dL/dh_{L-1}:
+ *   gy_t       = g_t silu(z_t);       dz_t = g_t y_t silu'(z_t)
+ *   lam_t[n]   = gy_t C_t[n] + e_{t+1,n} lam_{t+1}[n]      (lam_{L-1} also gets dL/dh_{L-1})
+ *   ddt_t      = sum_n lam_t[n] (a_n e_{t,n} h_{t-1}[n] + B_t[n] x_t)
+ *   du_t       = gy_t D + sum_n lam_t[n] dt_t B_t[n]
+ *   dB_t[n]   += lam_t[n] dt_t x_t            dC_t[n] += gy_t h_t[n]       (summed over d)
+ *   dA[d,n]   += sum_t lam_t[n] dt_t e_{t,n} h_{t-1}[n]
+ *   dD[d]     += sum_t gy_t x_t
+ *   ddelta_t   = ddt_t softplus'(s_t) = ddt_t sigmoid(s_t)   (ddt_t with softplus off)
+ *   dbias[d]  += sum_t ddelta_t;          dh0 = e_0 lam_0
+ * The recurrence and the output equation are those of oracle_scan_fwd [P1 Method; P2 output
+ * equation and Mamba block]; the derivative rules are the chain rule.
+ *   dout : (batch, seqlen, d_inner) f64;  dh_last : (batch, d_inner, d_state) f64 or NULL
+ *   du, ddelta, dz : (batch, seqlen, d_inner) f64 (dz ignored without z)
+ *   dB, dC : (batch, seqlen, d_state) f64;  dA : (d_inner, d_state);  dD, dbias : (d_inner)
+ *   dh0 : (batch, d_inner, d_state) f64 or NULL.  Every output is overwritten.
+ */
+int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                    const void* C, const float* D, const void* z, const float* delta_bias,
+                    int delta_softplus, const double* h0, int io_dtype, int64_t batch,
+                    int64_t seqlen, int64_t d_inner, int64_t d_state, const double* dout,
+                    const double* dh_last, double* du, double* ddelta, double* dz, double* dA,
+                    double* dB, double* dC, double* dD, double* dbias, double* dh0) {
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC || !dD ||
+      !dbias)
+    return -1;
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 1 || d_state > 256) return -1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  memset(dA, 0, sizeof(double) * d_inner * d_state);
+  memset(dB, 0, sizeof(double) * batch * seqlen * d_state);
+  memset(dC, 0, sizeof(double) * batch * seqlen * d_state);
+  memset(dD, 0, sizeof(double) * d_inner);
+  memset(dbias, 0, sizeof(double) * d_inner);
+  double* hist = (double*)malloc(sizeof(double) * (seqlen + 1) * d_state); /* h_{-1..L-1} */
+  double* dts = (double*)malloc(sizeof(double) * (seqlen > 0 ? seqlen : 1));
+  if (!hist || !dts) { free(hist); free(dts); return -1; }
+  for (int64_t r = 0; r < batch * d_inner; ++r) {
+    int64_t b = r / d_inner, d = r % d_inner;
+    /* forward, keeping every state */
+    for (int64_t n = 0; n < d_state; ++n) hist[n] = h0 ? h0[r * d_state + n] : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      int64_t e = (b * seqlen + t) * d_inner + d, bc = (b * seqlen + t) * d_state;
+      double x = rd(u, e, io_dtype);
+      double dt = step_size(rd(delta, e, io_dtype), delta_bias, d, delta_softplus);
+      dts[t] = dt;
+      for (int64_t n = 0; n < d_state; ++n) {
+        double a = (double)A[d * d_state + n];
+        hist[(t + 1) * d_state + n] =
+            exp(dt * a) * hist[t * d_state + n] + dt * rd(B, bc + n, io_dtype) * x;
+      }
+    }
+    /* reverse */
+    double lam[256], e_next[256];
+    for (int64_t n = 0; n < d_state; ++n) {
+      lam[n] = dh_last ? dh_last[r * d_state + n] : 0.0;
+      e_next[n] = 1.0;
+    }
+    for (int64_t t = seqlen - 1; t >= 0; --t) {
+      int64_t e = (b * seqlen + t) * d_inner + d, bc = (b * seqlen + t) * d_state;
+      double x = rd(u, e, io_dtype), dt = dts[t];
+      const double* h = &hist[(t + 1) * d_state];
+      const double* hp = &hist[t * d_state];
+      double y = 0.0;
+      for (int64_t n = 0; n < d_state; ++n) y += rd(C, bc + n, io_dtype) * h[n];
+      if (D) y += (double)D[d] * x;
+      double gy = dout[e];
+      if (z) {
+        double zv = rd(z, e, io_dtype), sg = 1.0 / (1.0 + exp(-zv));
+        gy = dout[e] * zv * sg;
+        if (dz) dz[e] = dout[e] * y * sg * (1.0 + zv * (1.0 - sg));
+      }
+      double ddt = 0.0, dx = D ? gy * (double)D[d] : 0.0;
+      for (int64_t n = 0; n < d_state; ++n) {
+        double a = (double)A[d * d_state + n];
+        double bn = rd(B, bc + n, io_dtype), cn = rd(C, bc + n, io_dtype);
+        double et = exp(dt * a);
+        /* the state's adjoint: from y_t, and from h_{t+1} through e_{t+1} (or dh_last) */
+        lam[n] = gy * cn + (t == seqlen - 1 ? lam[n] : e_next[n] * lam[n]);
+        ddt += lam[n] * (a * et * hp[n] + bn * x);
+        dx += lam[n] * dt * bn;
+        dB[bc + n] += lam[n] * dt * x;
+        dC[bc + n] += gy * h[n];
+        dA[d * d_state + n] += lam[n] * dt * et * hp[n];
+        e_next[n] = et;
+      }
+      dD[d] += gy * x; /* the gradient at D (0 when D is absent) */
+      double s = rd(delta, e, io_dtype) + (delta_bias ? (double)delta_bias[d] : 0.0);
+      double dd = delta_softplus ? ddt / (1.0 + exp(-s)) : ddt;
+      ddelta[e] = dd;
+      dbias[d] += dd;
+      du[e] = dx;
+    }
+    if (dh0)
+      for (int64_t n = 0; n < d_state; ++n)
+        dh0[r * d_state + n] = (seqlen > 0 ? e_next[n] * lam[n] : lam[n]);
+  }
+  free(hist);
+  free(dts);
   return 0;
 }
 

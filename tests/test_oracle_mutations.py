@@ -6,6 +6,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_bwd as bwd_pins
 from tests import test_oracle_conv as conv_pins
 from tests import test_oracle_pins as pins
 
@@ -51,11 +52,25 @@ MUTATIONS = [
      "            xv = 0.0;"),
     ("conv without silu", "        u[(b * seqlen + t) * d_inner + d] = silu(acc);",
      "        u[(b * seqlen + t) * d_inner + d] = acc;"),
+    ("adjoint without decay",
+     "        lam[n] = gy * cn + (t == seqlen - 1 ? lam[n] : e_next[n] * lam[n]);",
+     "        lam[n] = gy * cn + lam[n];"),
+    ("softplus derivative dropped", "      double dd = delta_softplus ? ddt / (1.0 + exp(-s)) : ddt;",
+     "      double dd = ddt;"),
+    ("dC from the previous state", "        dC[bc + n] += gy * h[n];", "        dC[bc + n] += gy * hp[n];"),
+    ("dA without the decay factor", "        dA[d * d_state + n] += lam[n] * dt * et * hp[n];",
+     "        dA[d * d_state + n] += lam[n] * dt * hp[n];"),
+    ("gate derivative without the z term",
+     "        if (dz) dz[e] = dout[e] * y * sg * (1.0 + zv * (1.0 - sg));",
+     "        if (dz) dz[e] = dout[e] * y * sg;"),
     ("conv looks ahead", "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + ts) * d_inner + d, io_dtype);",
      "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + (ts + 1 < seqlen ? ts + 1 : ts)) * d_inner + d, io_dtype);"),
 ]
 
 PIN_CALLS = [
+    lambda: bwd_pins.test_gradients_match_finite_differences(True),
+    lambda: bwd_pins.test_gradients_match_finite_differences(False),
+    bwd_pins.test_decay_free_linear_closed_form,
     lambda: conv_pins.test_matches_numpy_convolution(4, False, True),
     lambda: conv_pins.test_matches_numpy_convolution(2, True, False),
     conv_pins.test_last_tap_only_is_pointwise_silu,
