@@ -159,6 +159,49 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
                              int64_t batch, int64_t d_inner, int64_t d_state, ss_dtype dtype,
                              uint32_t flags, void* stream);
 
+/*
+ * Backward of the prefill (first-order input term): given dout = dL/d out (and optionally
+ * dh_last = dL/d h_last), the gradients of every input.  Reverse-mode differentiation of the
+ * recurrence above (reading guide, "Método"), with the states recomputed from stored chunk-end
+ * states rather than kept (reading guide, "Expansão de Estado Ciente de Hardware": recomputation
+ * in the backward pass):
+ *     lam_t[n] = gy_t C_t[n] + exp(dt_{t+1} A[d,n]) lam_{t+1}[n],  gy_t = dout_t silu(z_t)
+ *     du_t = gy_t D + dt_t sum_n lam_t B_t,  ddt_t = sum_n lam_t (A e_t h_{t-1} + B_t u_t)
+ *     ddelta_t = ddt_t sigmoid(delta_t + bias) (softplus') or ddt_t,  dz_t = dout_t y_t silu'(z_t)
+ *     dB_t += lam_t dt_t u_t,  dC_t += gy_t h_t (over channels),  dA += lam_t dt_t e_t h_{t-1},
+ *     dD += gy_t u_t,  ddelta_bias += ddelta_t,  dh0 = e_0 lam_0.
+ *
+ *   inputs            : exactly as given to ss_scan_fwd (u, delta, A, B, C, D, z, delta_bias,
+ *                       delta_softplus, h0, sizes, dtype).
+ *   dout              : (batch, seqlen, d_inner) io dtype, required.
+ *   dh_last           : (batch, d_inner, d_state) float32; NULL means 0.
+ *   du, ddelta        : (batch, seqlen, d_inner) io dtype, required, overwritten.
+ *   dz                : (batch, seqlen, d_inner) io dtype, required iff z is given.
+ *   dA                : (d_inner, d_state) float32, required, overwritten.
+ *   dB, dC            : (batch, seqlen, d_state) float32, required, overwritten.
+ *   dD, ddelta_bias   : (d_inner) float32, overwritten when non-NULL (the gradient at the given
+ *                       D / bias, also when D or delta_bias is NULL, i.e. 0).
+ *   dh0               : (batch, d_inner, d_state) float32, written when non-NULL.
+ *   workspace         : device scratch of ss_scan_bwd_workspace_bytes() bytes (the chunk-end
+ *                       states, batch * d_inner * ceil(seqlen / 16) * d_state floats), required
+ *                       when that is non-zero; SS_ERR_INVALID_ARG if smaller.
+ * dA, dB, dC, dD and ddelta_bias are sums formed with float atomics: they are reproducible up
+ * to rounding order only.  d_state above 16 and SS_FLAG_ZOH_EXACT -> SS_ERR_UNSUPPORTED.
+ * Outputs must not overlap inputs, each other or the workspace.
+ */
+ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int delta_softplus, const float* h0, const void* dout,
+                      const float* dh_last, void* du, void* ddelta, void* dz, float* dA,
+                      float* dB, float* dC, float* dD, float* ddelta_bias, float* dh0,
+                      int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      ss_dtype dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+                      void* stream);
+
+/* Workspace bytes ss_scan_bwd needs for this shape (0 for an empty problem or d_state > 16). */
+size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                   int64_t d_state, ss_dtype dtype);
+
 /* Static description of a status code. */
 const char* ss_status_string(ss_status s);
 

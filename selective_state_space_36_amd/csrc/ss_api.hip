@@ -10,6 +10,7 @@
 #include <algorithm>
 
 #include "ss_scan.h"
+#include "ss_bwd.h"
 #include "ss_launch.h"
 
 namespace {
@@ -302,6 +303,96 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
   return ok();
 }
 
+size_t bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 16) return 0;
+  const int64_t nchunks = (seqlen + ss::kBwdChunk - 1) / ss::kBwdChunk;
+  int64_t n;
+  if (!mul_ok(batch * d_inner, nchunks, &n) || !mul_ok(n, d_state * 4, &n)) return 0;
+  return static_cast<size_t>(n);
+}
+
+ss_status bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                   const float* h0, const void* dout, const float* dh_last, void* du,
+                   void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                   float* ddelta_bias, float* dh0, int64_t batch, int64_t seqlen,
+                   int64_t d_inner, int64_t d_state, ss_dtype dtype, void* workspace,
+                   size_t workspace_bytes, uint32_t flags, void* stream) {
+  int64_t es = 0;
+  if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (flags & SS_FLAG_ZOH_EXACT)
+    return fail(SS_ERR_UNSUPPORTED, "the backward implements the first-order input term only");
+  if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
+    return fail(SS_ERR_INVALID_ARG, "negative size");
+  if (d_state < 1 || d_state > 16)
+    return fail(SS_ERR_UNSUPPORTED, "backward: d_state=%lld outside 1..16", (long long)d_state);
+  int64_t rows, elems, bc_elems, st_elems;
+  if (!mul_ok(batch, d_inner, &rows) || !mul_ok(rows, seqlen, &elems) ||
+      !mul_ok(batch * seqlen, d_state, &bc_elems) || !mul_ok(rows, d_state, &st_elems) ||
+      !mul_ok(elems, 8, &elems) || !mul_ok(bc_elems, 8, &bc_elems))
+    return fail(SS_ERR_INVALID_ARG, "sizes overflow 64-bit byte offsets");
+  elems /= 8;
+  bc_elems /= 8;
+  if (d_inner > (int64_t(1) << 24))
+    return fail(SS_ERR_UNSUPPORTED, "d_inner=%lld above 16777216", (long long)d_inner);
+  if (seqlen > int64_t(0x7fffffff))
+    return fail(SS_ERR_UNSUPPORTED, "seqlen=%lld above 2147483647", (long long)seqlen);
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC)
+    return fail(SS_ERR_INVALID_ARG, "required pointer is NULL (u, delta, A, B, C, dout, du, "
+                "ddelta, dA, dB, dC are required)");
+  if (z && !dz) return fail(SS_ERR_INVALID_ARG, "dz is required when z is given");
+  const void* io_ptrs[] = {u, delta, B, C, z, dout, du, ddelta, dz};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es))
+      return fail(SS_ERR_UNSUPPORTED, "io pointer %p not aligned to its %lld-byte element", p,
+                  (long long)es);
+  const void* f_ptrs[] = {A, D, delta_bias, h0, dh_last, dA, dB, dC, dD, ddelta_bias, dh0};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
+  const size_t need = bwd_ws_bytes(batch, seqlen, d_inner, d_state);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+    return fail(SS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes the "
+                "backward needs (ss_scan_bwd_workspace_bytes)", workspace_bytes, need);
+  const Range ins[] = {range("u", u, elems, es), range("delta", delta, elems, es),
+                       range("z", z, elems, es), range("B", B, bc_elems, es),
+                       range("C", C, bc_elems, es), range("A", A, d_inner * d_state, 4),
+                       range("D", D, d_inner, 4), range("delta_bias", delta_bias, d_inner, 4),
+                       range("h0", h0, st_elems, 4), range("dout", dout, elems, es),
+                       range("dh_last", dh_last, st_elems, 4)};
+  const Range outs[] = {range("du", du, elems, es), range("ddelta", ddelta, elems, es),
+                        range("dz", z ? dz : nullptr, elems, es),
+                        range("dA", dA, d_inner * d_state, 4), range("dB", dB, bc_elems, 4),
+                        range("dC", dC, bc_elems, 4), range("dD", dD, d_inner, 4),
+                        range("ddelta_bias", ddelta_bias, d_inner, 4),
+                        range("dh0", dh0, st_elems, 4),
+                        range("workspace", need ? workspace : nullptr,
+                              static_cast<int64_t>(need), 1)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name,
+                                            in.name);
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SS_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  ss::BwdArgs a{};
+  a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.dout = dout; a.A = A; a.D = D;
+  a.delta_bias = delta_bias; a.h0 = h0; a.dh_last = dh_last; a.du = du; a.ddelta = ddelta;
+  a.dz = z ? dz : nullptr; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
+  a.ddelta_bias = ddelta_bias; a.dh0 = dh0; a.ck = static_cast<float*>(workspace);
+  a.batch = batch; a.seqlen = seqlen; a.d_inner = d_inner;
+  a.n_cblk = (d_inner + 15) / 16;
+  a.d_state = static_cast<int32_t>(d_state);
+  a.softplus = delta_softplus ? 1 : 0;
+  if (batch * a.n_cblk > int64_t(0x7fffffff))
+    return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
+  const hipError_t e =
+      ss::launch_scan_bwd(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,6 +467,25 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
                              uint32_t flags, void* stream) {
   return decode_impl(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, out, batch,
                      d_inner, d_state, dtype, flags, stream);
+}
+
+size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                   int64_t d_state, ss_dtype dtype) {
+  (void)dtype;
+  return bwd_ws_bytes(batch, seqlen, d_inner, d_state);
+}
+
+ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      int delta_softplus, const float* h0, const void* dout,
+                      const float* dh_last, void* du, void* ddelta, void* dz, float* dA,
+                      float* dB, float* dC, float* dD, float* ddelta_bias, float* dh0,
+                      int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                      ss_dtype dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
+                      void* stream) {
+  return bwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, dout, dh_last, du,
+                  ddelta, dz, dA, dB, dC, dD, ddelta_bias, dh0, batch, seqlen, d_inner, d_state,
+                  dtype, workspace, workspace_bytes, flags, stream);
 }
 
 const char* ss_status_string(ss_status s) {

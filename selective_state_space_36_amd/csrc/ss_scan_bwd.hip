@@ -1,0 +1,364 @@
+// ss_scan_bwd.hip -- gfx950 backward of the prefill scan (first-order input term dt B u).
+//
+// Gradients by reverse-mode differentiation of the recurrence (Mamba reading guide, "Método":
+// h_t = exp(dt_t A) h_{t-1} + dt_t B_t u_t, y_t = C_t h_t; IBM explainer: D term and gate), with
+// the states recomputed instead of stored (reading guide, "Expansão de Estado Ciente de
+// Hardware": intermediate states are recomputed in the backward pass).  For one channel and
+// state n, with e_t = exp(dt_t a_n) and gy_t = dout_t silu(z_t):
+//     lam_t   = gy_t C_t + e_{t+1} lam_{t+1}                  (adjoint of h_t, run backwards)
+//     ddt_t   = sum_n lam_t (a_n e_t h_{t-1} + B_t u_t),  du_t = gy_t D + dt_t sum_n lam_t B_t
+//     dB_t   += lam_t dt_t u_t,  dC_t += gy_t h_t             (summed over channels)
+//     dA     += lam_t dt_t e_t h_{t-1},  dD += gy_t u_t,  dz_t = dout_t y_t silu'(z_t)
+//     ddelta_t = ddt_t sigmoid(delta_t + bias) (softplus'),  dbias += ddelta_t,  dh0 = e_0 lam_0.
+//
+// Work layout (as in the forward kernel): one channel per 16-lane DPP row, lane k owns state k
+// and the element work of step k of each 16-step chunk; 16 channels per 256-thread workgroup,
+// one workgroup per (16 channels, batch row).  Pass 1 runs the forward over the sequence and
+// stores each chunk's end state (workspace, a few hundred bytes per channel and chunk).  Pass 2
+// walks the chunks backwards: it recomputes the chunk's 16 states and decays from the stored
+// state into registers, computes y for the gate's derivative, then runs the adjoint backwards
+// through the 16 steps.  Sums over a channel's states go through per-wave LDS tiles (summed by
+// the owner lane of the step, as in the forward); sums over channels (dB, dC) are reduced across
+// the wave's four rows by lane shuffles and across the four waves in LDS, then added to global
+// memory with one atomic per (step, state) and workgroup; dA, dD and dbias likewise once per
+// workgroup.  The atomic sums make dA, dB, dC, dD and dbias reproducible only up to rounding
+// order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "ss_bwd.h"
+#include "ss_device.h"
+
+namespace ss {
+namespace {
+
+constexpr int kT = kBwdChunk;
+constexpr int kPRow = 336;  // floats per channel row of a partial tile (padding)
+constexpr int kPTau = 20;   // floats per step of a partial tile (padding)
+
+template <class IO, bool GATE>
+struct BwdKernel {
+  using elem = typename IO::elem;
+  static constexpr int ES = sizeof(elem);
+  static constexpr int PIECE_E = 16 / ES;        // elements per 16-byte piece
+  static constexpr int PIECES = 16 / PIECE_E;    // pieces per 16-channel tile row
+
+  struct Smem {
+    float2 bc[16][kT + 2];          // (B_t[n], C_t[n]) of the chunk
+    elem in[4][kT][16];             // u, delta, z, dout tiles [tensor][step][channel]
+    float p[4][4 * kPRow];          // per wave: partial sums over states (y, then ddt)
+    float q[4][4 * kPRow];          // per wave: partial sums over states (du)
+    float gbc[2][4][kT][16];        // per wave: dB and dC summed over the wave's channels
+  };
+
+  static __device__ __forceinline__ void run(const BwdArgs& a) {
+    __shared__ Smem sm;
+    const int64_t b = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x / a.n_cblk));
+    const int64_t d0 = __builtin_amdgcn_readfirstlane(
+        static_cast<int>((blockIdx.x - b * a.n_cblk) * 16));
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int r = lane >> 4, k = lane & 15;
+    const int cl = wave * 4 + r;
+    const int64_t D = a.d_inner, N = a.d_state, L = a.seqlen;
+    const int64_t d = d0 + cl;
+    const bool chan_ok = d < D;
+    const bool lane_ok = chan_ok && k < N;
+    const int64_t row = b * D + d;
+    const int nchunks = static_cast<int>((L + kT - 1) / kT);
+    const int last_valid = static_cast<int>(L - int64_t(nchunks - 1) * kT);
+    auto nvalid_of = [&](int c) { return c == nchunks - 1 ? last_valid : kT; };
+
+    const float a_n = lane_ok ? a.A[d * N + k] : 0.0f;
+    const float A2 = a_n * kLog2e;
+    const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
+    const float dskip = (chan_ok && a.D) ? a.D[d] : 0.0f;
+    const int64_t row0 = b * L;  // (b, 0) row of u/delta/z/dout and of B/C
+
+    // ---- tile loads: wave w loads tensor w of (u, delta, z, dout), element by element through
+    // a raw buffer sized to the chunk's valid steps (loads past the end read 0; channels past
+    // d_inner read the next row or 0 and are not used); every thread loads one (step, state) of
+    // B and C.
+    const void* tens[4] = {a.u, a.delta, a.z, a.dout};
+    const int tl_row = lane / PIECES, tl_pc = lane % PIECES;
+    const bool tl_on = lane < kT * PIECES;
+    const uint32_t tl_off =
+        tl_on ? static_cast<uint32_t>((tl_row * D + tl_pc * PIECE_E) * ES) : kOffNone;
+    const int bc_tau = tid >> 4, bc_n = tid & 15;
+    const uint32_t bc_off = bc_n < N ? static_cast<uint32_t>((bc_tau * N + bc_n) * ES) : kOffNone;
+
+    auto load_tiles = [&](int c, bool full) {
+      const int nv = nvalid_of(c);
+      const int64_t t0 = int64_t(c) * kT;
+      const uint32_t io_bytes = static_cast<uint32_t>((nv * D - d0) * ES);
+      const bool want = full || wave_u < 2;  // pass 1 needs u and delta only
+      if (want && (GATE || wave_u != 2)) {
+        const rsrc_t rt = make_buf(
+            static_cast<const char*>(tens[wave_u]) + ((row0 + t0) * D + d0) * ES, io_bytes);
+        elem v[PIECE_E];
+#pragma unroll
+        for (int e = 0; e < PIECE_E; ++e) v[e] = buf_load<elem>(rt, tl_off + e * ES);
+        if (tl_on) {
+#pragma unroll
+          for (int e = 0; e < PIECE_E; ++e) sm.in[wave_u][tl_row][tl_pc * PIECE_E + e] = v[e];
+        }
+      }
+      const uint32_t bc_bytes = static_cast<uint32_t>(nv * N * ES);
+      const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + (row0 + t0) * N * ES, bc_bytes);
+      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
+      const float bv = IO::widen(buf_load<elem>(rb, bc_off));
+      const float cv = full ? IO::widen(buf_load<elem>(rc, bc_off)) : 0.0f;
+      sm.bc[bc_n][bc_tau] = make_float2(bv, cv);
+    };
+    auto own = [&](int ten) -> float { return IO::widen(sm.in[ten][k][cl]); };
+
+    // ---- pass 1: forward, storing each chunk's end state
+    float h = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
+    float* ck_row = a.ck + (row * nchunks) * N;
+    for (int c = 0; c < nchunks; ++c) {
+      load_tiles(c, false);
+      __syncthreads();
+      const bool own_ok = chan_ok && k < nvalid_of(c);
+      const float sv = own(1) + bias;
+      float dt = a.softplus ? softplus_f(sv) : sv;
+      dt = own_ok ? dt : 0.0f;
+      const float du = own_ok ? dt * own(0) : 0.0f;
+      float4 bcv[kT / 2];
+#pragma unroll
+      for (int i = 0; i < kT / 2; ++i) bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[k][2 * i]);
+      fwd_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, h);
+      if (lane_ok) ck_row[int64_t(c) * N + k] = h;
+      __syncthreads();
+    }
+
+    // ---- pass 2: chunks backwards
+    float lam = (a.dh_last && lane_ok) ? a.dh_last[row * N + k] : 0.0f;
+    float e_next = 1.0f;
+    float ga = 0.0f, gd_acc = 0.0f, gb_acc = 0.0f;
+    for (int c = nchunks - 1; c >= 0; --c) {
+      load_tiles(c, true);
+      __syncthreads();
+      const int nv = nvalid_of(c);
+      const bool own_ok = chan_ok && k < nv;
+      const float xu = own(0);
+      const float sv = own(1) + bias;
+      float dt = a.softplus ? softplus_f(sv) : sv;
+      dt = own_ok ? dt : 0.0f;
+      const float du = own_ok ? dt * xu : 0.0f;
+      float hprev;
+      if (c > 0) hprev = lane_ok ? ck_row[int64_t(c - 1) * N + k] : 0.0f;
+      else hprev = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
+
+      float4 bcv[kT / 2];
+#pragma unroll
+      for (int i = 0; i < kT / 2; ++i) bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[k][2 * i]);
+      // recompute the chunk: states, decays and the partial sums C.h of y
+      float hh[kT], ee[kT];
+      float* pw = &sm.p[wave][r * kPRow + k];
+      rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, hprev, hh, ee, pw);
+      wave_lds_sync();
+      float y = 0.0f;
+      {
+        const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y += pr[i];
+      }
+      wave_lds_sync();
+      y = fmaf(dskip, xu, y);
+      const float g = own_ok ? own(3) : 0.0f;
+      float gy = g, gz = 0.0f;
+      if (GATE) {
+        const float zv = own(2);
+        const float sg = rcp_hw(1.0f + exp2_hw(-zv * kLog2e));
+        gy = g * zv * sg;
+        gz = g * y * sg * fmaf(zv, 1.0f - sg, 1.0f);
+      }
+      gd_acc = fmaf(gy, xu, gd_acc);
+
+      // the adjoint backwards through the chunk
+      float* qw = &sm.q[wave][r * kPRow + k];
+      rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
+                lam, e_next, ga, pw, qw, &sm.gbc[0][wave][0][0], &sm.gbc[1][wave][0][0], r, k);
+      wave_lds_sync();
+      float gdt = 0.0f, gx = 0.0f;
+      {
+        const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
+        const float* qr = &sm.q[wave][r * kPRow + k * kPTau];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          gdt += pr[i];
+          gx += qr[i];
+        }
+      }
+      if (own_ok) {
+        const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
+        gb_acc += gdelta;
+        const int64_t e = (row0 + int64_t(c) * kT + k) * D + d;
+        static_cast<elem*>(a.du)[e] = IO::from_float(fmaf(gx, dt, gy * dskip));
+        static_cast<elem*>(a.ddelta)[e] = IO::from_float(gdelta);
+        if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
+      }
+      __syncthreads();  // the wave tiles of dB and dC are complete
+      {
+        const int tau = tid >> 4, n = tid & 15;
+        const float sb = sm.gbc[0][0][tau][n] + sm.gbc[0][1][tau][n] + sm.gbc[0][2][tau][n] +
+                         sm.gbc[0][3][tau][n];
+        const float sc = sm.gbc[1][0][tau][n] + sm.gbc[1][1][tau][n] + sm.gbc[1][2][tau][n] +
+                         sm.gbc[1][3][tau][n];
+        if (tau < nv && n < N) {
+          const int64_t o = (row0 + int64_t(c) * kT + tau) * N + n;
+          atomicAdd(a.dB + o, sb);
+          atomicAdd(a.dC + o, sc);
+        }
+      }
+      __syncthreads();  // tiles are reloaded by the next chunk
+    }
+    if (lane_ok) {
+      atomicAdd(a.dA + d * N + k, ga);
+      if (a.dh0) a.dh0[row * N + k] = e_next * lam;
+    }
+    // sums over the row's 16 owner lanes
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      gd_acc += __shfl_xor(gd_acc, m, 16);
+      gb_acc += __shfl_xor(gb_acc, m, 16);
+    }
+    if (chan_ok && k == 0) {
+      if (a.dD) atomicAdd(a.dD + d, gd_acc);
+      if (a.ddelta_bias) atomicAdd(a.ddelta_bias + d, gb_acc);
+    }
+  }
+
+  // Forward step (pass 1): h <- exp(dt A) h + dt u B.
+  template <int TAU>
+  static __device__ __forceinline__ void fwd_step(const float4 (&bcv)[kT / 2], float dt, float du,
+                                                  float A2, float& h) {
+    const float4 v = bcv[TAU / 2];
+    const float bb = (TAU & 1) ? v.z : v.x;
+    h = fmaf(exp2_hw(row_bcast<TAU>(dt) * A2), h, row_bcast<TAU>(du) * bb);
+  }
+  template <int... TAUS>
+  static __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, TAUS...>,
+                                                   const float4 (&bcv)[kT / 2], float dt,
+                                                   float du, float A2, float& h) {
+    (fwd_step<TAUS>(bcv, dt, du, A2, h), ...);
+  }
+
+  // Recompute step: keep the state and the decay of every step, and the partial sum C.h.
+  template <int TAU>
+  static __device__ __forceinline__ void rec_step(const float4 (&bcv)[kT / 2], float dt, float du,
+                                                  float A2, float& h, float (&hh)[kT],
+                                                  float (&ee)[kT], float* pw) {
+    const float4 v = bcv[TAU / 2];
+    const float bb = (TAU & 1) ? v.z : v.x;
+    const float cc = (TAU & 1) ? v.w : v.y;
+    const float e = exp2_hw(row_bcast<TAU>(dt) * A2);
+    h = fmaf(e, h, row_bcast<TAU>(du) * bb);
+    hh[TAU] = h;
+    ee[TAU] = e;
+    pw[TAU * kPTau] = cc * h;
+  }
+  template <int... TAUS>
+  static __device__ __forceinline__ void rec_steps(std::integer_sequence<int, TAUS...>,
+                                                   const float4 (&bcv)[kT / 2], float dt,
+                                                   float du, float A2, float hprev,
+                                                   float (&hh)[kT], float (&ee)[kT], float* pw) {
+    float h = hprev;
+    (rec_step<TAUS>(bcv, dt, du, A2, h, hh, ee, pw), ...);
+  }
+
+  // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
+  // contributions.  Partial sums over states go to the wave tiles pw (ddt) and qw (du); dB and
+  // dC are summed over the wave's four channels by lane shuffles (xor 16, 32) and stored by row 0.
+  template <int TAU>
+  static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
+                                                  float xu, float gy, float a_n, float hprev,
+                                                  const float (&hh)[kT], const float (&ee)[kT],
+                                                  float& lam, float& e_next, float& ga, float* pw,
+                                                  float* qw, float* gbw, float* gcw, int r,
+                                                  int k) {
+    const float4 v = bcv[TAU / 2];
+    const float bb = (TAU & 1) ? v.z : v.x;
+    const float cc = (TAU & 1) ? v.w : v.y;
+    const float gyb = row_bcast<TAU>(gy);
+    lam = fmaf(e_next, lam, gyb * cc);
+    const float hp = TAU > 0 ? hh[TAU > 0 ? TAU - 1 : 0] : hprev;
+    const float rr = lam * ee[TAU] * hp;
+    ga = fmaf(row_bcast<TAU>(dt), rr, ga);
+    const float qq = lam * bb;
+    pw[TAU * kPTau] = fmaf(a_n, rr, qq * row_bcast<TAU>(xu));
+    qw[TAU * kPTau] = qq;
+    float gb = lam * row_bcast<TAU>(du);
+    float gc = gyb * hh[TAU];
+    gb += __shfl_xor(gb, 16);
+    gc += __shfl_xor(gc, 16);
+    gb += __shfl_xor(gb, 32);
+    gc += __shfl_xor(gc, 32);
+    if (r == 0) {
+      gbw[TAU * 16 + k] = gb;
+      gcw[TAU * 16 + k] = gc;
+    }
+    e_next = ee[TAU];
+  }
+  template <int... TAUS>
+  static __device__ __forceinline__ void rev_steps(std::integer_sequence<int, TAUS...>,
+                                                   const float4 (&bcv)[kT / 2], float dt,
+                                                   float du, float xu, float gy, float a_n,
+                                                   float hprev, const float (&hh)[kT],
+                                                   const float (&ee)[kT], float& lam,
+                                                   float& e_next, float& ga, float* pw, float* qw,
+                                                   float* gbw, float* gcw, int r, int k) {
+    // fold over the steps in decreasing order
+    (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, hprev, hh, ee, lam, e_next, ga, pw, qw,
+                             gbw, gcw, r, k),
+     ...);
+  }
+};
+
+template <class IO, bool GATE>
+__global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdArgs a) {
+  BwdKernel<IO, GATE>::run(a);
+}
+
+__global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    p[i] = 0.0f;
+}
+
+hipError_t zero(float* p, int64_t n, hipStream_t stream) {
+  if (!p || n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p,
+                     n);
+  return hipGetLastError();
+}
+
+template <class IO>
+void launch_io(const BwdArgs& a, hipStream_t stream) {
+  if (a.batch * a.n_cblk == 0) return;  // nothing but the zeroed sums
+  const dim3 grid(static_cast<unsigned>(a.batch * a.n_cblk)), block(kBwdThreads);
+  if (a.z)
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, false>), grid, block, 0, stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  const int64_t N = a.d_state;
+  hipError_t e;
+  if ((e = zero(a.dA, a.d_inner * N, stream)) != hipSuccess) return e;
+  if ((e = zero(a.dB, a.batch * a.seqlen * N, stream)) != hipSuccess) return e;
+  if ((e = zero(a.dC, a.batch * a.seqlen * N, stream)) != hipSuccess) return e;
+  if ((e = zero(a.dD, a.d_inner, stream)) != hipSuccess) return e;
+  if ((e = zero(a.ddelta_bias, a.d_inner, stream)) != hipSuccess) return e;
+  if (bf16) launch_io<BF16>(a, stream);
+  else launch_io<F32>(a, stream);
+  return hipGetLastError();
+}
+
+}  // namespace ss

@@ -32,6 +32,10 @@ SIGNATURES = {
     "ss_scan_fwd_conv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp,
                                 _sz, _i32, _u32, _vp]),
+    "ss_scan_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                           _i32, _vp, _sz, _u32, _vp]),
+    "ss_scan_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "ss_state_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                _i64, _i64, _i64, _i32, _vp]),
     "ss_state_update_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
@@ -198,6 +202,45 @@ def scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, del
         _ptr(h0), _ptr(h_last), _ptr(out), batch, L, d_inner, d_state, code, _ptr(workspace),
         ws_len, int(nseg or 0), SS_FLAG_ZOH_EXACT if zoh_exact else 0, _stream(stream)))
     return (out, h_last) if return_last_state else out
+
+
+def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, dh_last=None, want_dD=True, want_ddelta_bias=True, want_dh0=True,
+             workspace=None, stream=None):
+    """Gradients of scan_fwd (ss_scan_bwd) for the upstream gradient dout (same dtype and shape
+    as out) and optionally dh_last.  Returns a dict: du, ddelta, dz (io dtype; dz None without
+    z), dA, dB, dC (float32), dD, ddelta_bias, dh0 (float32, None when not wanted)."""
+    batch, L, d_inner = u.shape
+    d_state = B.shape[-1]
+    code = _dtype_code(u)
+    for name, t in (("u", u), ("delta", delta), ("z", z), ("dout", dout)):
+        _dev(t, name, u.dtype, (batch, L, d_inner))
+    for name, t in (("B", B), ("C", C)):
+        _dev(t, name, u.dtype, (batch, L, d_state))
+    _dev(A, "A", torch.float32, (d_inner, d_state))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(delta_bias, "delta_bias", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, d_state))
+    _dev(dh_last, "dh_last", torch.float32, (batch, d_inner, d_state))
+    f32 = dict(dtype=torch.float32, device=u.device)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+             dz=torch.empty_like(u) if z is not None else None,
+             dA=torch.empty((d_inner, d_state), **f32), dB=torch.empty((batch, L, d_state), **f32),
+             dC=torch.empty((batch, L, d_state), **f32),
+             dD=torch.empty((d_inner,), **f32) if want_dD else None,
+             ddelta_bias=torch.empty((d_inner,), **f32) if want_ddelta_bias else None,
+             dh0=torch.empty((batch, d_inner, d_state), **f32) if want_dh0 else None)
+    if workspace is None:
+        nbytes = int(lib().ss_scan_bwd_workspace_bytes(batch, L, d_inner, d_state, code))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=u.device) if nbytes else None
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ss_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        1 if delta_softplus else 0, _ptr(h0), _ptr(dout), _ptr(dh_last), _ptr(g["du"]),
+        _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, L, d_inner, d_state, code,
+        _ptr(workspace), ws_len, 0, _stream(stream)))
+    return g
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -117,3 +117,32 @@ def test_unknown_flag_bits_are_rejected(lib):
                                 None, 1, FAKE * 6, 2, 8, 16, ops.SS_BF16, ops.SS_FLAG_ZOH_EXACT,
                                 None)
     assert rc == ops.SS_ERR_INVALID_ARG
+
+
+def _bwd(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None,
+             bias=None, sp=1, h0=None, dout=FAKE * 6, dhl=None, du=FAKE * 7, dd=FAKE * 8,
+             dz=None, dA=FAKE * 9, dB=FAKE * 10, dC=FAKE * 11, dD=None, db=None, dh0=None,
+             batch=1, L=4, d=16, N=16, dtype=ops.SS_BF16, ws=FAKE * 12, wsb=1 << 20, flags=0)
+    a.update(kw)
+    return lib.ss_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                           a["sp"], a["h0"], a["dout"], a["dhl"], a["du"], a["dd"], a["dz"],
+                           a["dA"], a["dB"], a["dC"], a["dD"], a["db"], a["dh0"], a["batch"],
+                           a["L"], a["d"], a["N"], a["dtype"], a["ws"], a["wsb"], a["flags"],
+                           None)
+
+
+def test_backward_argument_errors_before_launch(lib):
+    assert _bwd(lib, N=32) == ops.SS_ERR_UNSUPPORTED
+    assert _bwd(lib, flags=ops.SS_FLAG_ZOH_EXACT) == ops.SS_ERR_UNSUPPORTED
+    assert _bwd(lib, z=FAKE * 13) == ops.SS_ERR_INVALID_ARG          # z without dz
+    assert b"dz" in lib.ss_last_error()
+    assert _bwd(lib, dout=None) == ops.SS_ERR_INVALID_ARG
+    assert _bwd(lib, du=FAKE) == ops.SS_ERR_INVALID_ARG              # du aliases u
+    assert b"overlaps" in lib.ss_last_error()
+    assert _bwd(lib, ws=None, wsb=0) == ops.SS_ERR_INVALID_ARG       # workspace needed
+    assert b"workspace" in lib.ss_last_error()
+    need = lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 16, ops.SS_BF16)
+    assert need == 1 * 16 * 1 * 16 * 4
+    assert _bwd(lib, wsb=need - 4) == ops.SS_ERR_INVALID_ARG
+    assert lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 17, ops.SS_BF16) == 0
