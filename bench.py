@@ -202,6 +202,28 @@ def bench_prefill(args, torch, np, ops, wl):
     ms_conv = sum(a_.elapsed_time(b_) for a_, b_ in cs) / zsteps
     log(f"prefill with fused conv front end kernel avg {ms_conv * 1e3:.1f} us")
 
+    # the backward (ss_scan_bwd) of the same layer for a random upstream gradient
+    dout = torch.randn(u.shape, device="cuda", generator=g).to(u.dtype)
+    nbw = int(ops.lib().ss_scan_bwd_workspace_bytes(w.batch, w.seqlen, w.d_inner, w.d_state,
+                                                     ops.SS_BF16 if w.io_dtype == "bf16"
+                                                     else ops.SS_F32))
+    ws_b = torch.empty(max(nbw, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(1):
+        ops.scan_bwd(u, dl, A, B, C, dout, D=D, z=z, delta_bias=db, workspace=ws_b,
+                     stream=stream)
+    torch.cuda.synchronize()
+    bsteps = max(2, args.steps // 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(bsteps):
+        ops.scan_bwd(u, dl, A, B, C, dout, D=D, z=z, delta_bias=db, workspace=ws_b,
+                     stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_bwd = e0.elapsed_time(e1) / bsteps
+    log(f"backward {ms_bwd * 1e3:.1f} us per call")
+    del ws_b
+
     # spot parity check of the benchmarked output on a few rows
     import oracle
     rows = np.array([0, 1, w.d_inner - 1, (w.batch - 1) * w.d_inner + w.d_inner // 2],
@@ -234,7 +256,7 @@ def bench_prefill(args, torch, np, ops, wl):
         e = np.abs(gc[i] - rc[0, :, 0])
         ok = ok and bool(np.all(e <= 2e-2 + 2e-2 * np.abs(rc[0, :, 0])))
         errc = max(errc, float(e.max()))
-    return (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ok,
+    return (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ms_bwd, ok,
             float(max(err.max(), errz.max(), errc)))
 
 
@@ -411,8 +433,8 @@ def main():
         return
     ops.lib()
 
-    w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ok, maxerr = bench_prefill(args, torch, np, ops,
-                                                                         wl)
+    (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ms_bwd, ok,
+     maxerr) = bench_prefill(args, torch, np, ops, wl)
     elems = w.elements
     value = elems / (ms_step * 1e-3)
     nbytes = prefill_bytes(w)
@@ -454,6 +476,11 @@ def main():
                            "note": "ss_scan_fwd_conv, width-4 causal depthwise conv + SiLU on x "
                                    "fused in; an unfused front end would write u and read it "
                                    "back (hbm_bytes_avoided)"},
+        "backward": {"us_per_call": round(ms_bwd * 1e3, 2),
+                     "elements_per_s": round(elems / (ms_bwd * 1e-3), 1),
+                     "ratio_to_forward": round(ms_bwd / ms_kernel, 2),
+                     "note": "ss_scan_bwd (forward pass storing chunk-end states + reverse pass "
+                             "recomputing each chunk), all input gradients"},
         "parity_spot_check": {"ok": ok, "max_abs_err": maxerr},
     }
     if not args.no_decode:

@@ -13,13 +13,14 @@
 //
 // Work layout (as in the forward kernel): one channel per 16-lane DPP row, lane k owns state k
 // and the element work of step k of each 16-step chunk; 16 channels per 256-thread workgroup,
-// one workgroup per (16 channels, batch row).  Pass 1 runs the forward over the sequence and
+// one workgroup per (16 channels, batch row); the next chunk's global loads are in flight while a
+// chunk is computed (LDS tiles double-buffered).  Pass 1 runs the forward over the sequence and
 // stores each chunk's end state (workspace, a few hundred bytes per channel and chunk).  Pass 2
 // walks the chunks backwards: it recomputes the chunk's 16 states and decays from the stored
 // state into registers, computes y for the gate's derivative, then runs the adjoint backwards
 // through the 16 steps.  Sums over a channel's states go through per-wave LDS tiles (summed by
 // the owner lane of the step, as in the forward); sums over channels (dB, dC) are reduced across
-// the wave's four rows by lane shuffles and across the four waves in LDS, then added to global
+// the wave's four rows by row swaps and across the four waves in LDS, then added to global
 // memory with one atomic per (step, state) and workgroup; dA, dD and dbias likewise once per
 // workgroup.  The atomic sums make dA, dB, dC, dD and dbias reproducible only up to rounding
 // order.
@@ -35,6 +36,17 @@ namespace ss {
 namespace {
 
 constexpr int kT = kBwdChunk;
+
+// Sum of x over the four 16-lane rows of the wave, in every lane (row swaps with
+// v_permlane16_swap / v_permlane32_swap: VALU only, no LDS traffic).
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
 constexpr int kPRow = 336;  // floats per channel row of a partial tile (padding)
 constexpr int kPTau = 20;   // floats per step of a partial tile (padding)
 
@@ -46,8 +58,8 @@ struct BwdKernel {
   static constexpr int PIECES = 16 / PIECE_E;    // pieces per 16-channel tile row
 
   struct Smem {
-    float2 bc[16][kT + 2];          // (B_t[n], C_t[n]) of the chunk
-    elem in[4][kT][16];             // u, delta, z, dout tiles [tensor][step][channel]
+    float2 bc[2][16][kT + 2];       // (B_t[n], C_t[n]) of the chunk, double-buffered
+    elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
     float p[4][4 * kPRow];          // per wave: partial sums over states (y, then ddt)
     float q[4][4 * kPRow];          // per wave: partial sums over states (du)
     float gbc[2][4][kT][16];        // per wave: dB and dC summed over the wave's channels
@@ -90,48 +102,67 @@ struct BwdKernel {
     const int bc_tau = tid >> 4, bc_n = tid & 15;
     const uint32_t bc_off = bc_n < N ? static_cast<uint32_t>((bc_tau * N + bc_n) * ES) : kOffNone;
 
-    auto load_tiles = [&](int c, bool full) {
+    // Global loads of chunk c go to registers (issued before the current chunk is computed) and
+    // are written to LDS buffer `buf` after it.
+    elem pv[PIECE_E];
+    float pbv = 0.0f, pcv = 0.0f;
+    auto issue = [&](int c, bool full) {
       const int nv = nvalid_of(c);
       const int64_t t0 = int64_t(c) * kT;
       const uint32_t io_bytes = static_cast<uint32_t>((nv * D - d0) * ES);
-      const bool want = full || wave_u < 2;  // pass 1 needs u and delta only
-      if (want && (GATE || wave_u != 2)) {
+      const bool want = (full || wave_u < 2) && (GATE || wave_u != 2);  // pass 1: u, delta only
+      if (want) {
         const rsrc_t rt = make_buf(
             static_cast<const char*>(tens[wave_u]) + ((row0 + t0) * D + d0) * ES, io_bytes);
-        elem v[PIECE_E];
 #pragma unroll
-        for (int e = 0; e < PIECE_E; ++e) v[e] = buf_load<elem>(rt, tl_off + e * ES);
-        if (tl_on) {
-#pragma unroll
-          for (int e = 0; e < PIECE_E; ++e) sm.in[wave_u][tl_row][tl_pc * PIECE_E + e] = v[e];
-        }
+        for (int e = 0; e < PIECE_E; ++e) pv[e] = buf_load<elem>(rt, tl_off + e * ES);
       }
       const uint32_t bc_bytes = static_cast<uint32_t>(nv * N * ES);
       const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + (row0 + t0) * N * ES, bc_bytes);
-      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
-      const float bv = IO::widen(buf_load<elem>(rb, bc_off));
-      const float cv = full ? IO::widen(buf_load<elem>(rc, bc_off)) : 0.0f;
-      sm.bc[bc_n][bc_tau] = make_float2(bv, cv);
+      pbv = IO::widen(buf_load<elem>(rb, bc_off));
+      if (full) {
+        const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
+        pcv = IO::widen(buf_load<elem>(rc, bc_off));
+      }
     };
-    auto own = [&](int ten) -> float { return IO::widen(sm.in[ten][k][cl]); };
+    auto stage = [&](int buf, bool full) {
+      const bool want = (full || wave_u < 2) && (GATE || wave_u != 2);
+      if (want && tl_on) {
+#pragma unroll
+        for (int e = 0; e < PIECE_E; ++e)
+          sm.in[buf][wave_u][tl_row][tl_pc * PIECE_E + e] = pv[e];
+      }
+      sm.bc[buf][bc_n][bc_tau] = make_float2(pbv, full ? pcv : 0.0f);
+    };
+    auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][cl]); };
 
     // ---- pass 1: forward, storing each chunk's end state
     float h = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
     float* ck_row = a.ck + (row * nchunks) * N;
-    for (int c = 0; c < nchunks; ++c) {
-      load_tiles(c, false);
+    int buf = 0;
+    if (nchunks > 0) {
+      issue(0, false);
+      stage(0, false);
       __syncthreads();
+    }
+    for (int c = 0; c < nchunks; ++c) {
+      // next: chunk c + 1 of this pass, or the last chunk for pass 2
+      const bool next_full = c + 1 == nchunks;
+      issue(next_full ? nchunks - 1 : c + 1, next_full);
       const bool own_ok = chan_ok && k < nvalid_of(c);
-      const float sv = own(1) + bias;
+      const float sv = own(buf, 1) + bias;
       float dt = a.softplus ? softplus_f(sv) : sv;
       dt = own_ok ? dt : 0.0f;
-      const float du = own_ok ? dt * own(0) : 0.0f;
+      const float du = own_ok ? dt * own(buf, 0) : 0.0f;
       float4 bcv[kT / 2];
 #pragma unroll
-      for (int i = 0; i < kT / 2; ++i) bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[k][2 * i]);
+      for (int i = 0; i < kT / 2; ++i)
+        bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k][2 * i]);
       fwd_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, h);
       if (lane_ok) ck_row[int64_t(c) * N + k] = h;
+      stage(buf ^ 1, next_full);
       __syncthreads();
+      buf ^= 1;
     }
 
     // ---- pass 2: chunks backwards
@@ -139,12 +170,11 @@ struct BwdKernel {
     float e_next = 1.0f;
     float ga = 0.0f, gd_acc = 0.0f, gb_acc = 0.0f;
     for (int c = nchunks - 1; c >= 0; --c) {
-      load_tiles(c, true);
-      __syncthreads();
+      if (c > 0) issue(c - 1, true);
       const int nv = nvalid_of(c);
       const bool own_ok = chan_ok && k < nv;
-      const float xu = own(0);
-      const float sv = own(1) + bias;
+      const float xu = own(buf, 0);
+      const float sv = own(buf, 1) + bias;
       float dt = a.softplus ? softplus_f(sv) : sv;
       dt = own_ok ? dt : 0.0f;
       const float du = own_ok ? dt * xu : 0.0f;
@@ -154,7 +184,8 @@ struct BwdKernel {
 
       float4 bcv[kT / 2];
 #pragma unroll
-      for (int i = 0; i < kT / 2; ++i) bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[k][2 * i]);
+      for (int i = 0; i < kT / 2; ++i)
+        bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k][2 * i]);
       // recompute the chunk: states, decays and the partial sums C.h of y
       float hh[kT], ee[kT];
       float* pw = &sm.p[wave][r * kPRow + k];
@@ -168,10 +199,10 @@ struct BwdKernel {
       }
       wave_lds_sync();
       y = fmaf(dskip, xu, y);
-      const float g = own_ok ? own(3) : 0.0f;
+      const float g = own_ok ? own(buf, 3) : 0.0f;
       float gy = g, gz = 0.0f;
       if (GATE) {
-        const float zv = own(2);
+        const float zv = own(buf, 2);
         const float sg = rcp_hw(1.0f + exp2_hw(-zv * kLog2e));
         gy = g * zv * sg;
         gz = g * y * sg * fmaf(zv, 1.0f - sg, 1.0f);
@@ -201,7 +232,8 @@ struct BwdKernel {
         static_cast<elem*>(a.ddelta)[e] = IO::from_float(gdelta);
         if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
       }
-      __syncthreads();  // the wave tiles of dB and dC are complete
+      if (c > 0) stage(buf ^ 1, true);
+      __syncthreads();  // the wave tiles of dB and dC, and the next chunk's tiles, are complete
       {
         const int tau = tid >> 4, n = tid & 15;
         const float sb = sm.gbc[0][0][tau][n] + sm.gbc[0][1][tau][n] + sm.gbc[0][2][tau][n] +
@@ -214,7 +246,8 @@ struct BwdKernel {
           atomicAdd(a.dC + o, sc);
         }
       }
-      __syncthreads();  // tiles are reloaded by the next chunk
+      __syncthreads();  // the dB and dC tiles are rewritten by the next chunk
+      buf ^= 1;
     }
     if (lane_ok) {
       atomicAdd(a.dA + d * N + k, ga);
@@ -272,7 +305,7 @@ struct BwdKernel {
 
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
   // contributions.  Partial sums over states go to the wave tiles pw (ddt) and qw (du); dB and
-  // dC are summed over the wave's four channels by lane shuffles (xor 16, 32) and stored by row 0.
+  // dC are summed over the wave's four channels (rows) and stored by row 0.
   template <int TAU>
   static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float xu, float gy, float a_n, float hprev,
@@ -291,12 +324,8 @@ struct BwdKernel {
     const float qq = lam * bb;
     pw[TAU * kPTau] = fmaf(a_n, rr, qq * row_bcast<TAU>(xu));
     qw[TAU * kPTau] = qq;
-    float gb = lam * row_bcast<TAU>(du);
-    float gc = gyb * hh[TAU];
-    gb += __shfl_xor(gb, 16);
-    gc += __shfl_xor(gc, 16);
-    gb += __shfl_xor(gb, 32);
-    gc += __shfl_xor(gc, 32);
+    const float gb = sum_rows(lam * row_bcast<TAU>(du));
+    const float gc = sum_rows(gyb * hh[TAU]);
     if (r == 0) {
       gbw[TAU * 16 + k] = gb;
       gcw[TAU * 16 + k] = gc;
