@@ -82,6 +82,9 @@ def _bind(lib):
     lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64,
                                     i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_scan_bwd.restype = i32
+    lib.oracle_scan2_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64,
+                                     i64, i64, i64, vp, vp, i32]
+    lib.oracle_scan2_fwd.restype = i32
     lib.oracle_state_update.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
@@ -329,3 +332,35 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
     if rc != 0:
         raise ValueError("oracle_scan_bwd rejected its arguments")
     return g
+
+
+def scan2_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+              nthreads=None):
+    """Sequential fp64 multi-head scan with a scalar transition per head (oracle_scan2_fwd).
+    x, z: (batch, L, nheads, headdim); dt: (batch, L, nheads); B, C: (batch, L, ngroups,
+    d_state) -- float32 or bf16 bits, one io dtype.  A, D, dt_bias: (nheads,) float32.  h0:
+    (batch, nheads, d_state, headdim) float64 or None.  Returns (out, h_last) in float64."""
+    x, io = _io(x, "x")
+    dt, _ = _io(dt, "dt")
+    B, _ = _io(B, "B")
+    C, _ = _io(C, "C")
+    z, _ = _io(z, "z")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _check_io([("dt", dt), ("z", z), ("B", B), ("C", C)],
+              [(batch, L, H), (batch, L, H, P), (batch, L, G, N), (batch, L, G, N)], io)
+    A = _f32(A, (H,), "A")
+    D = _f32(D, (H,), "D")
+    dt_bias = _f32(dt_bias, (H,), "dt_bias")
+    if h0 is not None:
+        h0 = np.ascontiguousarray(h0, dtype=np.float64).reshape(batch, H, N, P)
+    out = np.empty((batch, L, H, P))
+    h_last = np.empty((batch, H, N, P))
+    if nthreads is None:
+        nthreads = max(1, len(os.sched_getaffinity(0)))
+    rc = _load().oracle_scan2_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(dt_bias), int(bool(dt_softplus)), _ptr(h0), io, batch, L,
+                                  H, P, G, N, _ptr(out), _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_scan2_fwd rejected its arguments")
+    return out, h_last

@@ -372,6 +372,66 @@ int oracle_scan_bwd(const void* u, const void* delta, const float* A, const void
   return 0;
 }
 
+/*
+ * Multi-head selective scan with a scalar transition per head (the Mamba-2 form [P2: Mamba-2
+ * splits the block into heads like multi-head attention, with B and C shared by groups of heads
+ * as in grouped-query attention; P3: the diagonal transition reduced to a scalar times the
+ * identity]).  For batch b, head h (group g = h / (nheads / ngroups)), state n, head channel p:
+ *   dt_t     = softplus(dt[b,t,h] + dt_bias[h])  (or the raw sum)           [P1 S6]
+ *   hs_t[n,p] = exp(dt_t A[h]) hs_{t-1}[n,p] + dt_t B[b,t,g,n] x[b,t,h,p]   [P1 Method]
+ *   y_t[p]   = sum_n C[b,t,g,n] hs_t[n,p] + D[h] x[b,t,h,p]                 [P1, P2]
+ *   out      = y_t[p] silu(z[b,t,h,p]) when z is given                      [P2 Mamba block]
+ *   x, z : (batch, seqlen, nheads, headdim) io dtype;  dt : (batch, seqlen, nheads) io dtype
+ *   A, dt_bias, D : (nheads) f32 (dt_bias, D NULL = 0);  B, C : (batch, seqlen, ngroups, d_state)
+ *   h0, h_last : (batch, nheads, d_state, headdim) f64 (NULL = zeros / not written)
+ *   out : (batch, seqlen, nheads, headdim) f64
+ */
+int oracle_scan2_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                     const float* D, const void* z, const float* dt_bias, int dt_softplus,
+                     const double* h0, int io_dtype, int64_t batch, int64_t seqlen,
+                     int64_t nheads, int64_t headdim, int64_t ngroups, int64_t d_state,
+                     double* out, double* h_last, int nthreads) {
+  if (!x || !dt || !A || !B || !C || !out) return -1;
+  if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || ngroups < 1 || d_state < 1)
+    return -1;
+  if (nheads % ngroups != 0) return -1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return -1;
+  if (nthreads < 1) nthreads = 1;
+  const int64_t hpg = nheads / ngroups;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+  for (int64_t r = 0; r < batch * nheads; ++r) {
+    int64_t b = r / nheads, h = r % nheads, g = h / hpg;
+    double* hs = (double*)malloc(sizeof(double) * d_state * headdim);
+    if (!hs) { bad = 1; continue; }
+    for (int64_t i = 0; i < d_state * headdim; ++i) hs[i] = h0 ? h0[r * d_state * headdim + i] : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double s = rd(dt, (b * seqlen + t) * nheads + h, io_dtype) + (dt_bias ? (double)dt_bias[h] : 0.0);
+      double dtv = dt_softplus ? softplus(s) : s;
+      double decay = exp(dtv * (double)A[h]);
+      int64_t bc = ((b * seqlen + t) * ngroups + g) * d_state;
+      int64_t xo = ((b * seqlen + t) * nheads + h) * headdim;
+      for (int64_t n = 0; n < d_state; ++n) {
+        double bn = dtv * rd(B, bc + n, io_dtype);
+        for (int64_t p = 0; p < headdim; ++p)
+          hs[n * headdim + p] = decay * hs[n * headdim + p] + bn * rd(x, xo + p, io_dtype);
+      }
+      for (int64_t p = 0; p < headdim; ++p) {
+        double y = 0.0;
+        for (int64_t n = 0; n < d_state; ++n) y += rd(C, bc + n, io_dtype) * hs[n * headdim + p];
+        double xp = rd(x, xo + p, io_dtype);
+        if (D) y += (double)D[h] * xp;
+        if (z) y *= silu(rd(z, xo + p, io_dtype));
+        out[xo + p] = y;
+      }
+    }
+    if (h_last)
+      for (int64_t i = 0; i < d_state * headdim; ++i) h_last[r * d_state * headdim + i] = hs[i];
+    free(hs);
+  }
+  return bad ? -1 : 0;
+}
+
 /* Number of threads OpenMP would use by default (for reporting the CPU baseline). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -9,6 +9,7 @@ import oracle
 from tests import test_oracle_bwd as bwd_pins
 from tests import test_oracle_conv as conv_pins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_scan2 as scan2_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
 
@@ -63,11 +64,22 @@ MUTATIONS = [
     ("gate derivative without the z term",
      "        if (dz) dz[e] = dout[e] * y * sg * (1.0 + zv * (1.0 - sg));",
      "        if (dz) dz[e] = dout[e] * y * sg;"),
+    ("head reads the wrong group", "    int64_t b = r / nheads, h = r % nheads, g = h / hpg;",
+     "    int64_t b = r / nheads, h = r % nheads, g = h % ngroups;"),
+    ("multi-head decay after the input",
+     "          hs[n * headdim + p] = decay * hs[n * headdim + p] + bn * rd(x, xo + p, io_dtype);",
+     "          hs[n * headdim + p] = decay * (hs[n * headdim + p] + bn * rd(x, xo + p, io_dtype));"),
+    ("multi-head y before the update",
+     "        for (int64_t n = 0; n < d_state; ++n) y += rd(C, bc + n, io_dtype) * hs[n * headdim + p];",
+     "        for (int64_t n = 0; n < d_state; ++n) y += rd(C, bc + n, io_dtype) * hs[n * headdim + p] / decay;"),
     ("conv looks ahead", "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + ts) * d_inner + d, io_dtype);",
      "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + (ts + 1 < seqlen ? ts + 1 : ts)) * d_inner + d, io_dtype);"),
 ]
 
 PIN_CALLS = [
+    lambda: scan2_pins.test_equals_mamba1_with_constant_A_rows(False),
+    scan2_pins.test_quadratic_dual_form,
+    scan2_pins.test_group_sharing,
     lambda: bwd_pins.test_gradients_match_finite_differences(True),
     lambda: bwd_pins.test_gradients_match_finite_differences(False),
     bwd_pins.test_decay_free_linear_closed_form,
