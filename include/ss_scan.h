@@ -202,6 +202,33 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
 size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                    int64_t d_state, ss_dtype dtype);
 
+/*
+ * Multi-head scan with a scalar transition per head (the Mamba-2 form: IBM explainer, the
+ * Mamba-2 block split into heads like multi-head attention, with B and C shared by groups of
+ * heads as in grouped-query attention; Cartesia Mamba-3 post, the diagonal transition reduced to
+ * a scalar times the identity).  For batch b, head h in group g = h / (nheads / ngroups), state n
+ * and head channel p:
+ *
+ *     dt_t      = softplus(dt[b,t,h] + dt_bias[h])          (or the raw sum, softplus off)
+ *     S_t[n,p]  = exp(dt_t * A[h]) * S_{t-1}[n,p] + dt_t * B[b,t,g,n] * x[b,t,h,p]
+ *     y_t[p]    = sum_n C[b,t,g,n] * S_t[n,p] + D[h] * x[b,t,h,p]
+ *     out       = y_t[p] * silu(z[b,t,h,p])                (when z is given)
+ *
+ *   x, z, out : (batch, seqlen, nheads, headdim), io dtype; z == NULL: no gate.
+ *   dt        : (batch, seqlen, nheads), io dtype.
+ *   B, C      : (batch, seqlen, ngroups, d_state), io dtype.
+ *   A         : (nheads) float32, one transition per head.  D, dt_bias: (nheads) float32, NULL 0.
+ *   h0, h_last: (batch, nheads, d_state, headdim) float32; NULL: zeros / not written.
+ * nheads must be a multiple of ngroups (SS_ERR_INVALID_ARG); d_state outside 1..256 ->
+ * SS_ERR_UNSUPPORTED.  Empty sizes are a no-op (h_last <- h0 or zeros).  out and h_last must not
+ * overlap the inputs or each other.
+ */
+ss_status ss_scan2_fwd(const void* x, const void* dt, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       int dt_softplus, const float* h0, float* h_last, void* out,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t ngroups, int64_t d_state, ss_dtype dtype, void* stream);
+
 /* Static description of a status code. */
 const char* ss_status_string(ss_status s);
 

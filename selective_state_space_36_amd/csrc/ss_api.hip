@@ -12,6 +12,7 @@
 #include "ss_scan.h"
 #include "ss_bwd.h"
 #include "ss_launch.h"
+#include "ss_scan2.h"
 
 namespace {
 
@@ -393,6 +394,84 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   return ok();
 }
 
+ss_status scan2_impl(const void* x, const void* dt, const float* A, const void* B,
+                     const void* C, const float* D, const void* z, const float* dt_bias,
+                     int dt_softplus, const float* h0, float* h_last, void* out, int64_t batch,
+                     int64_t seqlen, int64_t nheads, int64_t headdim, int64_t ngroups,
+                     int64_t d_state, ss_dtype dtype, void* stream) {
+  int64_t es = 0;
+  if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || ngroups < 0 || d_state < 0)
+    return fail(SS_ERR_INVALID_ARG, "negative size");
+  if (d_state < 1 || d_state > 256)
+    return fail(SS_ERR_UNSUPPORTED, "d_state=%lld outside 1..256", (long long)d_state);
+  if (nheads > 0 && (ngroups < 1 || nheads % ngroups != 0))
+    return fail(SS_ERR_INVALID_ARG, "nheads=%lld is not a multiple of ngroups=%lld",
+                (long long)nheads, (long long)ngroups);
+  int64_t rows, elems, dt_elems, bc_elems, st_elems;
+  if (!mul_ok(batch, nheads, &rows) || !mul_ok(rows * seqlen, headdim, &elems) ||
+      !mul_ok(batch * seqlen, nheads, &dt_elems) ||
+      !mul_ok(batch * seqlen * ngroups, d_state, &bc_elems) ||
+      !mul_ok(rows * d_state, headdim, &st_elems) || !mul_ok(elems, 8, &elems))
+    return fail(SS_ERR_INVALID_ARG, "sizes overflow 64-bit byte offsets");
+  elems /= 8;
+  if (batch == 0 || seqlen == 0 || nheads == 0 || headdim == 0) {
+    if (h_last && st_elems > 0) {
+      if (h0 && h0 != h_last &&
+          overlap(range("h0", h0, st_elems, 4), range("h_last", h_last, st_elems, 4)))
+        return fail(SS_ERR_INVALID_ARG, "h_last overlaps h0");
+      if (h0 != h_last) {
+        const hipError_t e =
+            ss::launch_copy_state(h_last, h0, st_elems, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+      }
+    }
+    return ok();
+  }
+  // a 16-step tile of one head is addressed with 32-bit byte offsets
+  if (int64_t(ss::kScan2Chunk) * nheads * headdim * 4 >= (int64_t(1) << 31) ||
+      int64_t(ss::kScan2Chunk) * ngroups * d_state * 4 >= (int64_t(1) << 31) ||
+      seqlen > int64_t(0x7fffffff))
+    return fail(SS_ERR_UNSUPPORTED, "a 16-step tile exceeds 2 GiB (nheads * headdim or ngroups "
+                "* d_state too large) or seqlen above 2147483647");
+  if (!x || !dt || !A || !B || !C || !out)
+    return fail(SS_ERR_INVALID_ARG, "required pointer is NULL (x, dt, A, B, C and out are "
+                "required)");
+  const void* io_ptrs[] = {x, dt, B, C, z, out};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, es))
+      return fail(SS_ERR_UNSUPPORTED, "io pointer %p not aligned to its %lld-byte element", p,
+                  (long long)es);
+  const void* f_ptrs[] = {A, D, dt_bias, h0, h_last};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
+  const Range ins[] = {range("x", x, elems, es), range("dt", dt, dt_elems, es),
+                       range("z", z, elems, es), range("B", B, bc_elems, es),
+                       range("C", C, bc_elems, es), range("A", A, nheads, 4),
+                       range("D", D, nheads, 4), range("dt_bias", dt_bias, nheads, 4),
+                       range("h0", h0, st_elems, 4)};
+  const Range ro = range("out", out, elems, es);
+  const Range rh = range("h_last", h_last, st_elems, 4);
+  for (const Range& in : ins) {
+    if (overlap(ro, in)) return fail(SS_ERR_INVALID_ARG, "out overlaps %s", in.name);
+    if (overlap(rh, in)) return fail(SS_ERR_INVALID_ARG, "h_last overlaps %s", in.name);
+  }
+  if (overlap(ro, rh)) return fail(SS_ERR_INVALID_ARG, "out overlaps h_last");
+  ss::Scan2Args a{};
+  a.x = x; a.dt = dt; a.z = z; a.B = B; a.C = C; a.A = A; a.D = D; a.dt_bias = dt_bias;
+  a.h0 = h0; a.h_last = h_last; a.out = out;
+  a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.headdim = headdim;
+  a.ngroups = ngroups;
+  a.n_pblk = (headdim + ss::kScan2PBlock - 1) / ss::kScan2PBlock;
+  a.d_state = static_cast<int32_t>(d_state);
+  a.softplus = dt_softplus ? 1 : 0;
+  if (batch * nheads * a.n_pblk > int64_t(0x7fffffff))
+    return fail(SS_ERR_INVALID_ARG, "too many workgroups");
+  const hipError_t e = ss::launch_scan2(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -486,6 +565,15 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
   return bwd_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, dout, dh_last, du,
                   ddelta, dz, dA, dB, dC, dD, ddelta_bias, dh0, batch, seqlen, d_inner, d_state,
                   dtype, workspace, workspace_bytes, flags, stream);
+}
+
+ss_status ss_scan2_fwd(const void* x, const void* dt, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       int dt_softplus, const float* h0, float* h_last, void* out,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t ngroups, int64_t d_state, ss_dtype dtype, void* stream) {
+  return scan2_impl(x, dt, A, B, C, D, z, dt_bias, dt_softplus, h0, h_last, out, batch, seqlen,
+                    nheads, headdim, ngroups, d_state, dtype, stream);
 }
 
 const char* ss_status_string(ss_status s) {

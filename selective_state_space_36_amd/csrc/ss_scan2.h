@@ -1,0 +1,34 @@
+// ss_scan2.h -- host-side launch interface of the multi-head scalar-transition scan
+// (ss_scan2.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr int kScan2Threads = 256;
+constexpr int kScan2Chunk = 16;
+constexpr int kScan2PBlock = 16;  // head channels per workgroup
+
+struct Scan2Args {
+  const void* x;         // (batch, seqlen, nheads, headdim) io dtype
+  const void* dt;        // (batch, seqlen, nheads) io dtype
+  const void* z;         // (batch, seqlen, nheads, headdim) io dtype; nullptr: no gate
+  const void* B;         // (batch, seqlen, ngroups, d_state) io dtype
+  const void* C;
+  const float* A;        // (nheads)
+  const float* D;        // (nheads); nullptr: 0
+  const float* dt_bias;  // (nheads); nullptr: 0
+  const float* h0;       // (batch, nheads, d_state, headdim); nullptr: zeros
+  float* h_last;         // (batch, nheads, d_state, headdim); nullptr: not written
+  void* out;             // (batch, seqlen, nheads, headdim) io dtype
+  int64_t batch, seqlen, nheads, headdim, ngroups;
+  int64_t n_pblk;        // ceil(headdim / kScan2PBlock)
+  int32_t d_state;
+  int32_t softplus;
+};
+
+hipError_t launch_scan2(const Scan2Args& a, bool bf16, hipStream_t stream);
+
+}  // namespace ss

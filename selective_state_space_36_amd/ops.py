@@ -36,6 +36,8 @@ SIGNATURES = {
                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                            _i32, _vp, _sz, _u32, _vp]),
     "ss_scan_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
+    "ss_scan2_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+                            _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
     "ss_state_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                _i64, _i64, _i64, _i32, _vp]),
     "ss_state_update_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
@@ -241,6 +243,37 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
         _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, L, d_inner, d_state, code,
         _ptr(workspace), ws_len, 0, _stream(stream)))
     return g
+
+
+def scan2_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+              return_last_state=False, out=None, h_last=None, stream=None):
+    """Multi-head scan with a scalar transition per head (ss_scan2_fwd).
+
+    x, z: (batch, L, nheads, headdim); dt: (batch, L, nheads); B, C: (batch, L, ngroups,
+    d_state), one io dtype.  A, D, dt_bias: (nheads,) float32.  h0: (batch, nheads, d_state,
+    headdim) float32.  Returns out (and h_last when return_last_state).
+    """
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(x)
+    for name, t in (("x", x), ("z", z)):
+        _dev(t, name, x.dtype, (batch, L, H, P))
+    _dev(dt, "dt", x.dtype, (batch, L, H))
+    for name, t in (("B", B), ("C", C)):
+        _dev(t, name, x.dtype, (batch, L, G, N))
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        _dev(t, name, torch.float32, (H,))
+    _dev(h0, "h0", torch.float32, (batch, H, N, P))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype, (batch, L, H, P))
+    if return_last_state and h_last is None:
+        h_last = torch.empty((batch, H, N, P), dtype=torch.float32, device=x.device)
+    _dev(h_last, "h_last", torch.float32, (batch, H, N, P))
+    _check(lib().ss_scan2_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(dt_bias), 1 if dt_softplus else 0, _ptr(h0), _ptr(h_last),
+                              _ptr(out), batch, L, H, P, G, N, code, _stream(stream)))
+    return (out, h_last) if return_last_state else out
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,

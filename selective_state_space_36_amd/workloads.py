@@ -185,3 +185,56 @@ def make_decode(w: Workload, *, steps=None, batch=None, d_inner=None, seed=None)
     A, D, delta_bias = _params(w, kids, d_inner)
     state = normal_f32(kids[7], (batch, d_inner, w.d_state))
     return dict(state=state, u=u, delta=delta, z=z, B=B, C=C, A=A, D=D, delta_bias=delta_bias)
+
+
+@dataclasses.dataclass(frozen=True)
+class MultiHeadWorkload:
+    """A layer of the multi-head scalar-transition scan (the Mamba-2 form)."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    d_state: int
+    io_dtype: str
+    gate: bool
+    seed: int
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim
+
+
+# d_inner 5120 as 80 heads of 64 channels, one group of B/C with 128 states: the Mamba-2-shaped
+# counterpart of the 2.8B prefill layer.
+MULTIHEAD = MultiHeadWorkload("mamba2-80h-prefill", batch=4, seqlen=4096, nheads=80, headdim=64,
+                              ngroups=1, d_state=128, io_dtype="bf16", gate=True, seed=2000)
+
+
+def make_multihead(w: MultiHeadWorkload, *, batch=None, seqlen=None, nheads=None, headdim=None,
+                   ngroups=None, d_state=None, seed=None):
+    """Inputs for the multi-head scan: x, z (batch, L, H, P), dt (batch, L, H), B, C
+    (batch, L, G, N) in the io dtype, and per head A = -U[1, 16], D ~ N(1, 0.1) and dt_bias with
+    softplus(dt_bias) ~ log-uniform[1e-3, 1e-1] (float32).  Same stream discipline as
+    make_prefill: SeedSequence(seed).spawn(8) in the order x, dt, z, B, C, dt-range, D, A."""
+    batch = w.batch if batch is None else batch
+    seqlen = w.seqlen if seqlen is None else seqlen
+    H = w.nheads if nheads is None else nheads
+    P = w.headdim if headdim is None else headdim
+    G = w.ngroups if ngroups is None else ngroups
+    N = w.d_state if d_state is None else d_state
+    seed = w.seed if seed is None else seed
+    kids = np.random.SeedSequence(seed).spawn(8)
+    x = _io_cast(normal_f32(kids[0], (batch, seqlen, H, P)), w.io_dtype)
+    dt = _io_cast(normal_f32(kids[1], (batch, seqlen, H), scale=0.5), w.io_dtype)
+    z = _io_cast(normal_f32(kids[2], (batch, seqlen, H, P)), w.io_dtype) if w.gate else None
+    B = _io_cast(normal_f32(kids[3], (batch, seqlen, G, N)), w.io_dtype)
+    C = _io_cast(normal_f32(kids[4], (batch, seqlen, G, N)), w.io_dtype)
+    g_dt = np.random.Generator(np.random.PCG64(kids[5]))
+    dts = np.exp(g_dt.uniform(np.log(1e-3), np.log(1e-1), size=H))
+    dt_bias = np.log(np.expm1(dts)).astype(np.float32)
+    D = normal_f32(kids[6], (H,), scale=0.1, loc=1.0)
+    g_a = np.random.Generator(np.random.PCG64(kids[7]))
+    A = (-g_a.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    return dict(x=x, dt=dt, z=z, B=B, C=C, A=A, D=D, dt_bias=dt_bias)

@@ -1,0 +1,105 @@
+"""GPU parity of the multi-head scalar-transition scan (ss_scan2_fwd, the Mamba-2 form) against
+the fp64 oracle (oracle.scan2_fwd, pinned against the Mamba-1 oracle and the quadratic dual
+form).  Tolerances as for the prefill: 1e-4 (float32 io) and 2e-2 (bfloat16 io), elementwise."""
+import numpy as np
+import pytest
+
+import oracle
+from selective_state_space_36_amd import workloads as wl
+from tests.helpers import TOL, check_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_36_amd import ops
+    ops.lib()
+    yield
+
+
+def ops():
+    from selective_state_space_36_amd import ops as o
+    return o
+
+
+F32W = wl.MultiHeadWorkload("test-f32", 2, 50, 4, 16, 2, 16, "f32", True, 3000)
+
+
+def run2(p, *, gate=True, skip=True, h0=None, heads=None):
+    z = p["z"] if gate else None
+    D = p["D"] if skip else None
+    print(f"  scan2 case: x={p['x'].shape} N={p['B'].shape[-1]} G={p['B'].shape[2]} "
+          f"dtype={p['x'].dtype} gate={gate} h0={h0 is not None}", flush=True)
+    out, hl = ops().scan2_fwd(dev(p["x"]), dev(p["dt"]), dev(p["A"]), dev(p["B"]), dev(p["C"]),
+                              D=dev(D), z=dev(z), dt_bias=dev(p["dt_bias"]),
+                              h0=None if h0 is None else dev(h0), return_last_state=True)
+    torch.cuda.synchronize()
+    out, hl = host(out), host(hl)
+    if heads is not None:  # the oracle on a subset of heads (heads are independent)
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :, heads])
+        ro, rh = oracle.scan2_fwd(sub(p["x"]), sub(p["dt"]), p["A"][heads], p["B"], p["C"],
+                                  D=None if D is None else D[heads], z=sub(z),
+                                  dt_bias=p["dt_bias"][heads])
+        return out[:, :, heads], hl[:, heads], ro, rh
+    ro, rh = oracle.scan2_fwd(p["x"], p["dt"], p["A"], p["B"], p["C"], D=D, z=z,
+                              dt_bias=p["dt_bias"],
+                              h0=None if h0 is None else h0.astype(np.float64))
+    return out, hl, ro, rh
+
+
+@pytest.mark.parametrize("gate,skip", [(True, True), (False, False)])
+def test_small_fp32_scan2(gate, skip):
+    p = wl.make_multihead(F32W)
+    h0 = np.random.default_rng(1).standard_normal((2, 4, 16, 16)).astype(np.float32)
+    g, gh, r, rh = run2(p, gate=gate, skip=skip, h0=h0)
+    check_close(g, r, TOL["f32"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+@pytest.mark.parametrize("L,H,P,G,N", [(1, 2, 16, 1, 16), (17, 3, 20, 1, 5), (33, 4, 7, 2, 37),
+                                       (40, 2, 64, 2, 128), (20, 2, 16, 1, 256)])
+def test_ragged_fp32_scan2(L, H, P, G, N):
+    p = wl.make_multihead(F32W, batch=2, seqlen=L, nheads=H, headdim=P, ngroups=G, d_state=N,
+                          seed=L + N)
+    g, gh, r, rh = run2(p)
+    check_close(g, r, TOL["f32"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+def test_medium_bf16_scan2():
+    p = wl.make_multihead(wl.MULTIHEAD, batch=1, seqlen=512, nheads=8, seed=7)
+    g, gh, r, rh = run2(p)
+    check_close(g, r, TOL["bf16"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+def test_empty_and_invalid_scan2():
+    o = ops()
+    p = wl.make_multihead(F32W, seqlen=4)
+    with pytest.raises(o.SSError) as e:  # 4 heads are not a multiple of 3 groups
+        B3 = torch.zeros((2, 4, 3, 16), device="cuda")
+        o.scan2_fwd(dev(p["x"]), dev(p["dt"]), dev(p["A"]), B3, B3.clone())
+    assert e.value.status == o.SS_ERR_INVALID_ARG
+    # an empty sequence passes h0 through to h_last
+    h0 = torch.randn((2, 4, 16, 16), device="cuda")
+    x0 = torch.zeros((2, 0, 4, 16), device="cuda")
+    _, hl = o.scan2_fwd(x0, torch.zeros((2, 0, 4), device="cuda"), dev(p["A"]),
+                        torch.zeros((2, 0, 2, 16), device="cuda"),
+                        torch.zeros((2, 0, 2, 16), device="cuda"), h0=h0, return_last_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hl, h0)
+
+
+def test_full_size_scan2_sampled_heads():
+    """The Mamba-2-shaped layer (batch 4, L 4096, 80 heads x 64, 128 states, bf16) in the launch
+    configuration the benchmark uses, checked on a sample of heads."""
+    p = wl.make_multihead(wl.MULTIHEAD)
+    heads = np.array([0, 1, 37, 78, 79])
+    g, gh, r, rh = run2(p, heads=heads)
+    check_close(g, r, TOL["bf16"], "out (sampled heads)")
+    check_close(gh, rh, TOL["f32"], "h_last (sampled heads)")
