@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-multihead", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -357,6 +358,29 @@ def bench_decode(args, torch, np, ops, wl):
     us_hot = e0.elapsed_time(e1) * 1e3 / steps
     log(f"decode graph {us_graph:.2f} us/step, cold (8 rotating states) {us_cold:.2f} us/step, "
         f"inputs reused {us_hot:.2f} us/step")
+
+    # the step with the width-4 front end fused in (ss_state_update_conv): u is formed from
+    # the block's x (u[s] here) and a (batch, 3, d_inner) window updated in place
+    k = 4
+    rng = np.random.default_rng(44)
+    cw = torch.from_numpy((0.5 * rng.standard_normal((w.d_inner, k))).astype(np.float32)).cuda()
+    cb = torch.from_numpy((0.2 * rng.standard_normal(w.d_inner)).astype(np.float32)).cuda()
+    cs = torch.zeros((w.batch, k - 1, w.d_inner), dtype=torch.bfloat16, device="cuda")
+
+    def one_conv(s):
+        ops.state_update_conv(st, cs, u[s], cw, cb, dl[s], A, B[s], C[s], D=D, z=z[s],
+                              delta_bias=db, out=out[s], stream=stream)
+
+    for s in range(min(20, steps)):
+        one_conv(s)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(steps):
+        one_conv(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_conv = e0.elapsed_time(e1) * 1e3 / steps
+    log(f"decode with fused front end {us_conv:.2f} us/step")
     nb = decode_bytes_per_step(w)
     return dict(
         workload=w.name, batch=w.batch, d_inner=w.d_inner, d_state=w.d_state, steps=steps,
@@ -374,8 +398,58 @@ def bench_decode(args, torch, np, ops, wl):
         cold=dict(us_per_step_end_to_end=round(us_cold, 3), state_buffers=nbuf,
                   achieved_GBps=round(nb / (us_cold * 1e-6) / 1e9, 1),
                   frac=round(nb / (us_cold * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)),
+        conv_front_end=dict(us_per_step_end_to_end=round(us_conv, 3), conv_k=k,
+                            note="ss_state_update_conv: width-4 causal conv + SiLU on x and the "
+                                 "in-place window shift fused into the step"),
         note="warm: one state (41.9 MB) resident across steps, which fits the 256 MB Infinity "
              "Cache; cold: 8 states used in turn")
+
+
+def bench_multihead(args, torch, np, ops, wl):
+    """The multi-head scalar-transition scan (ss_scan2_fwd) on the Mamba-2-shaped layer."""
+    w = wl.MULTIHEAD
+    log(f"generating {w.name} inputs")
+    p = wl.make_multihead(w)
+    x, dt, z, B, C = (dev(p[k], torch, np) for k in ("x", "dt", "z", "B", "C"))
+    A, D, db = (dev(p[k], torch, np) for k in ("A", "D", "dt_bias"))
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    run = lambda: ops.scan2_fwd(x, dt, A, B, C, D=D, z=z, dt_bias=db, out=out, stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    steps = max(3, args.steps // 4)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a_, b_ in ev:
+        a_.record(stream)
+        run()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a_.elapsed_time(b_) for a_, b_ in ev) / steps
+    log(f"multi-head scan {ms * 1e3:.1f} us per call")
+    # spot parity on two heads against the oracle
+    import oracle
+    heads = np.array([0, w.nheads - 1])
+    sub = lambda a: np.ascontiguousarray(a[:, :, heads])
+    ro, _ = oracle.scan2_fwd(sub(p["x"]), sub(p["dt"]), p["A"][heads], p["B"], p["C"],
+                             D=p["D"][heads], z=sub(p["z"]), dt_bias=p["dt_bias"][heads])
+    go = out[:, :, torch.from_numpy(heads).cuda()].float().cpu().numpy().astype(np.float64)
+    err = np.abs(go - ro)
+    ok = bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ro)))
+    N, P = w.d_state, w.headdim
+    slots = w.elements * (3 * N + 10)   # per update: x.dt*B, state FMA, C.h FMA; per element ~10
+    nbytes = 3 * w.elements * 2 + w.batch * w.seqlen * w.nheads * 2 \
+        + 2 * w.batch * w.seqlen * w.ngroups * N * 2 + 3 * w.nheads * 4
+    return dict(workload=w.name, batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, headdim=P,
+                ngroups=w.ngroups, d_state=N, us_per_call=round(ms * 1e3, 2),
+                elements_per_s=round(w.elements / (ms * 1e-3), 1),
+                roofline=dict(bound="alu", achieved=round(slots / (ms * 1e-3) / 1e12, 3),
+                              peak=round(PEAK_VALU_SLOTS / 1e12, 3), unit="T VALU-slot/s",
+                              frac=round(slots / (ms * 1e-3) / PEAK_VALU_SLOTS, 4)),
+                hbm=dict(algorithmic_bytes=nbytes,
+                         achieved_GBps=round(nbytes / (ms * 1e-3) / 1e9, 1)),
+                parity_spot_check=dict(ok=ok, max_abs_err=float(err.max())))
 
 
 def cpu_baseline(args, np, w, p):
@@ -483,6 +557,8 @@ def main():
                              "recomputing each chunk), all input gradients"},
         "parity_spot_check": {"ok": ok, "max_abs_err": maxerr},
     }
+    if not args.no_multihead:
+        result["multihead"] = bench_multihead(args, torch, np, ops, wl)
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, np, ops, wl)
     if not args.no_cpu_baseline:

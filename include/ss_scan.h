@@ -229,6 +229,26 @@ ss_status ss_scan2_fwd(const void* x, const void* dt, const float* A, const void
                        int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t ngroups, int64_t d_state, ss_dtype dtype, void* stream);
 
+/*
+ * Decode with the block's front end fused in (the one-token form of ss_scan_fwd_conv): takes
+ * the block's x for this token and forms u = silu(conv_bias + sum_j conv_weight[d,j] *
+ * window[j]) over the window [conv_state (the conv_k - 1 previous inputs, oldest first), x];
+ * conv_state is then shifted in place (oldest dropped, x appended).
+ *   conv_state   : (batch, conv_k - 1, d_inner) io dtype, read and overwritten IN PLACE
+ *                  (required when conv_k > 1).
+ *   x            : (batch, d_inner) io dtype.
+ *   conv_weight, conv_bias, conv_k : as for ss_scan_fwd_conv.
+ *   the rest     : as for ss_state_update_ex.
+ * Needs d_state a multiple of 4 in 12..64 with 16-byte aligned state and A
+ * (SS_ERR_UNSUPPORTED otherwise).  conv_state must not overlap state, out or the inputs.
+ */
+ss_status ss_state_update_conv(float* state, void* conv_state, const void* x,
+                               const float* conv_weight, const float* conv_bias, int32_t conv_k,
+                               const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias,
+                               int delta_softplus, void* out, int64_t batch, int64_t d_inner,
+                               int64_t d_state, ss_dtype dtype, uint32_t flags, void* stream);
+
 /* Static description of a status code. */
 const char* ss_status_string(ss_status s);
 

@@ -250,12 +250,15 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
                       const void* B, const void* C, const float* D, const void* z,
                       const float* delta_bias, int delta_softplus, void* out, int64_t batch,
                       int64_t d_inner, int64_t d_state, ss_dtype dtype, uint32_t flags,
-                      void* stream) {
+                      void* stream, void* conv_state = nullptr, const float* conv_w = nullptr,
+                      const float* conv_b = nullptr, int32_t conv_k = 0) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (batch < 0 || d_inner < 0 || d_state < 0)
     return fail(SS_ERR_INVALID_ARG, "negative size");
+  if (conv_w && (conv_k < 1 || conv_k > 4))
+    return fail(SS_ERR_UNSUPPORTED, "conv_k=%d outside 1..4", conv_k);
   if (d_state < 1 || d_state > 64)
     return fail(SS_ERR_UNSUPPORTED, "d_state=%lld outside 1..64", (long long)d_state);
   int64_t rows, st_elems;
@@ -266,23 +269,32 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
   if (rows == 0) return ok();
   if (!state || !u || !delta || !A || !B || !C || !out)
     return fail(SS_ERR_INVALID_ARG, "required pointer is NULL (state, u, delta, A, B, C, out)");
-  const void* io_ptrs[] = {u, delta, B, C, z, out};
+  if (conv_w && conv_k > 1 && !conv_state)
+    return fail(SS_ERR_INVALID_ARG, "conv_state is NULL");
+  const void* io_ptrs[] = {u, delta, B, C, z, out, conv_w ? conv_state : nullptr};
   for (const void* p : io_ptrs)
     if (p && !aligned(p, es)) return fail(SS_ERR_UNSUPPORTED, "io pointer %p misaligned", p);
-  const void* f_ptrs[] = {state, A, D, delta_bias};
+  const void* f_ptrs[] = {state, A, D, delta_bias, conv_w, conv_b};
   for (const void* p : f_ptrs)
     if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
   const Range ins[] = {range("u", u, rows, es), range("delta", delta, rows, es),
                        range("z", z, rows, es), range("B", B, batch * d_state, es),
                        range("C", C, batch * d_state, es), range("A", A, d_inner * d_state, 4),
-                       range("D", D, d_inner, 4), range("delta_bias", delta_bias, d_inner, 4)};
+                       range("D", D, d_inner, 4), range("delta_bias", delta_bias, d_inner, 4),
+                       range("conv_w", conv_w, d_inner * conv_k, 4),
+                       range("conv_b", conv_w ? conv_b : nullptr, d_inner, 4)};
   const Range rs = range("state", state, st_elems, 4);
   const Range ro = range("out", out, rows, es);
+  const Range rcs = range("conv_state", conv_w && conv_k > 1 ? conv_state : nullptr,
+                          batch * (conv_k - 1) * d_inner, es);
   for (const Range& in : ins) {
     if (overlap(rs, in)) return fail(SS_ERR_INVALID_ARG, "state overlaps %s", in.name);
     if (overlap(ro, in)) return fail(SS_ERR_INVALID_ARG, "out overlaps %s", in.name);
+    if (overlap(rcs, in)) return fail(SS_ERR_INVALID_ARG, "conv_state overlaps %s", in.name);
   }
   if (overlap(ro, rs)) return fail(SS_ERR_INVALID_ARG, "out overlaps state");
+  if (overlap(rcs, rs) || overlap(rcs, ro))
+    return fail(SS_ERR_INVALID_ARG, "conv_state overlaps state or out");
 
   ss::DecodeArgs a{};
   a.state = state; a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C; a.A = A; a.D = D;
@@ -297,6 +309,15 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
   // the vector path addresses a batch row of the state with 32-bit byte offsets
   a.vec4 = (d_state % 4 == 0 && d_inner * d_state < (int64_t(1) << 29) && aligned(state, 16) &&
             aligned(A, 16) && aligned(B, bc_align) && aligned(C, bc_align)) ? 1 : 0;
+  if (conv_w) {
+    if (!a.vec4 || g < 4)
+      return fail(SS_ERR_UNSUPPORTED, "the fused decode front end needs d_state a multiple of 4 "
+                  "in 12..64 with 16-byte aligned state and A");
+    a.conv_state = conv_k > 1 ? conv_state : nullptr;
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    a.conv_k = conv_k;
+  }
   if ((rows * g + 255) / 256 > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many rows");
   const hipError_t e = ss::launch_decode(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
@@ -574,6 +595,18 @@ ss_status ss_scan2_fwd(const void* x, const void* dt, const float* A, const void
                        int64_t ngroups, int64_t d_state, ss_dtype dtype, void* stream) {
   return scan2_impl(x, dt, A, B, C, D, z, dt_bias, dt_softplus, h0, h_last, out, batch, seqlen,
                     nheads, headdim, ngroups, d_state, dtype, stream);
+}
+
+ss_status ss_state_update_conv(float* state, void* conv_state, const void* x,
+                               const float* conv_weight, const float* conv_bias, int32_t conv_k,
+                               const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias,
+                               int delta_softplus, void* out, int64_t batch, int64_t d_inner,
+                               int64_t d_state, ss_dtype dtype, uint32_t flags, void* stream) {
+  if (!conv_weight) return fail(SS_ERR_INVALID_ARG, "conv_weight is NULL");
+  return decode_impl(state, x, delta, A, B, C, D, z, delta_bias, delta_softplus, out, batch,
+                     d_inner, d_state, dtype, flags, stream, conv_state, conv_weight, conv_bias,
+                     conv_k);
 }
 
 const char* ss_status_string(ss_status s) {

@@ -61,6 +61,12 @@ struct DecodeArgs {
   int32_t softplus;
   int32_t vec4;            // d_state % 4 == 0 and 16-byte aligned state/A
   int32_t zoh;             // exact zero-order-hold input term instead of dt * B
+  // front end (conv_w != nullptr, vector path with lanes_per_chan >= 4 only): u holds the
+  // block's x; u = silu(causal conv over [conv_state, x] + conv_b), conv_state shifted in place
+  void* conv_state;        // (batch, conv_k - 1, d_inner) io dtype
+  const float* conv_w;     // (d_inner, conv_k)
+  const float* conv_b;     // (d_inner), nullptr: 0
+  int32_t conv_k;          // 1..4
 };
 
 // Prefill passes.  `summary` selects the first pass of a time-split scan (segments 0..nseg-2,

@@ -71,7 +71,7 @@ __device__ __forceinline__ float group_sum(float x) {
 // few shifts, and lanes past the row get an offset beyond every range: their loads return 0 and
 // their stores are dropped by the hardware range check.  Each thread takes ITEMS lanes 256
 // apart and issues all their loads before any arithmetic.
-template <class IO, bool GATE, bool ZOH, int G, int ITEMS>
+template <class IO, bool GATE, bool ZOH, bool CONV, int G, int ITEMS>
 __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs a) {
   using elem = typename IO::elem;
   using raw4 = typename Vec4In<IO>::raw;  // four io elements
@@ -91,10 +91,17 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
   // broadcasts then hand them to the whole quad.  That is 2 narrow loads per lane instead of 5,
   // and the narrow loads are what the memory pipeline spends the most instructions on.
   constexpr bool QUAD = G >= 4;
+  static_assert(!CONV || QUAD, "the front end needs a quad per channel");
   const int qq = threadIdx.x & 3;
-  const elem* aux_base = static_cast<const elem*>(
-      qq == 0 ? a.u : (qq == 1 ? a.delta : (GATE && qq == 2 ? a.z : a.u)));
-  const float* f_src = qq == 0 ? a.delta_bias : a.D;
+  // With the front end (CONV) the quad's lanes load delta / z instead, lane 2 the conv bias, and
+  // every lane one element of the 4-wide input window [conv_state (K-1 entries), x] with its tap
+  // weight; the window sum is a quad reduction.
+  const elem* aux_base =
+      CONV ? static_cast<const elem*>(qq == 0 ? a.delta : (GATE && qq == 1 ? a.z : a.delta))
+           : static_cast<const elem*>(qq == 0 ? a.u
+                                              : (qq == 1 ? a.delta
+                                                         : (GATE && qq == 2 ? a.z : a.u)));
+  const float* f_src = qq == 0 ? a.delta_bias : ((CONV && qq == 2) ? a.conv_b : a.D);
   const bool f_ok = f_src != nullptr;
   const float* f_base = f_ok ? f_src : a.A;  // any valid address; the value is then zeroed
   uint32_t so[ITEMS], io[ITEMS], fo[ITEMS], bo[ITEMS], oo[ITEMS];
@@ -123,10 +130,23 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
     const rsrc_t ro = make_buf(static_cast<elem*>(a.out) + b * D, D * ES);
     float4 hv[ITEMS], av[ITEMS];
     raw4 bv[ITEMS], cv[ITEMS];
-    elem xr[ITEMS], dr[ITEMS], zr[ITEMS];
-    float bias[ITEMS], dsk[ITEMS];
+    elem xr[ITEMS], dr[ITEMS], zr[ITEMS], wn[ITEMS];
+    float bias[ITEMS], dsk[ITEMS], wt[ITEMS];
+    const int K = CONV ? a.conv_k : 0;
+    const int jw = qq - (4 - K);  // this lane's window slot as a tap index (< 0: unused)
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
+      if (CONV) {  // window element and tap weight of this lane (unused slots: valid
+                   // addresses, values zeroed, so the loads need no branch)
+        const bool from_x = qq == 3 || jw < 0;
+        const elem* src = from_x ? static_cast<const elem*>(a.u) + b * D + dcl[i]
+                                 : static_cast<const elem*>(a.conv_state) +
+                                       (b * (K - 1) + jw) * D + dcl[i];
+        const elem v = *src;
+        const float wv = a.conv_w[int64_t(dcl[i]) * K + (jw >= 0 ? jw : 0)];
+        wn[i] = jw >= 0 ? v : elem{};
+        wt[i] = jw >= 0 ? wv : 0.0f;
+      }
       hv[i] = buf_load<float4>(rs, so[i]);
       av[i] = buf_load<float4>(rA, so[i]);
       bv[i] = buf_load<raw4>(rB, bo[i]);
@@ -145,7 +165,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       float x, s, zv = 0.0f, dskip;
-      if (QUAD) {
+      if (CONV) {
+        const float w = IO::widen(xr[i]);
+        const float f = f_ok ? bias[i] : 0.0f;
+        const float win = IO::widen(wn[i]);
+        x = silu_f(group_sum<4>(wt[i] * win) + quad_bcast<2>(f));
+        s = quad_bcast<0>(w) + quad_bcast<0>(f);
+        if (GATE) zv = quad_bcast<1>(w);
+        dskip = quad_bcast<1>(f);
+        // shift the window: slot j of the new state is the old slot j + 1 (the last one is x);
+        // the first quad of the channel writes
+        const int pos = jw - 1;
+        const uint32_t l = (blockIdx.x * ITEMS + i) * kDecodeThreads + threadIdx.x;
+        if (pos >= 0 && (l & (G - 1)) < 4 && (l >> LOG_G) < static_cast<uint32_t>(D))
+          static_cast<elem*>(a.conv_state)[(b * (K - 1) + pos) * D + dcl[i]] = wn[i];
+      } else if (QUAD) {
         const float w = IO::widen(xr[i]);
         const float f = f_ok ? bias[i] : 0.0f;
         x = quad_bcast<0>(w);
@@ -228,18 +262,26 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeAr
 
 constexpr int kItems = 1;
 
-template <class IO, bool GATE, bool ZOH, int G>
+template <class IO, bool GATE, bool ZOH, int G, bool CONV = false>
 void launch_vec(const DecodeArgs& a, hipStream_t stream) {
   const int64_t per_block = int64_t(kDecodeThreads) * kItems;
   const int64_t row_lanes = a.d_inner * G;
   const dim3 grid(static_cast<unsigned>((row_lanes + per_block - 1) / per_block),
                   static_cast<unsigned>(a.batch < 65535 ? a.batch : 65535));
-  hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, G, kItems>), grid, dim3(kDecodeThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, CONV, G, kItems>), grid,
+                     dim3(kDecodeThreads), 0, stream, a);
 }
 
 template <class IO, bool GATE, bool ZOH>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  if (a.conv_w) {  // the host admits the front end only on the vector path with G >= 4
+    switch (a.lanes_per_chan) {
+      case 4: launch_vec<IO, GATE, ZOH, 4, true>(a, stream); break;
+      case 8: launch_vec<IO, GATE, ZOH, 8, true>(a, stream); break;
+      default: launch_vec<IO, GATE, ZOH, 16, true>(a, stream); break;
+    }
+    return hipGetLastError();
+  }
   if (a.vec4) {
     switch (a.lanes_per_chan) {
       case 1: launch_vec<IO, GATE, ZOH, 1>(a, stream); break;

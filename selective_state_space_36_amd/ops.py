@@ -38,6 +38,9 @@ SIGNATURES = {
     "ss_scan_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
     "ss_scan2_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
                             _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]),
+    "ss_state_update_conv": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, ctypes.c_int, _vp, _i64, _i64, _i64, _i32, _u32,
+                                    _vp]),
     "ss_state_update": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
                                _i64, _i64, _i64, _i32, _vp]),
     "ss_state_update_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
@@ -302,4 +305,35 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _check(lib().ss_state_update_ex(*args, SS_FLAG_ZOH_EXACT, _stream(stream)))
     else:
         _check(lib().ss_state_update(*args, _stream(stream)))
+    return out
+
+
+def state_update_conv(state, conv_state, x, conv_weight, conv_bias, delta, A, B, C, D=None,
+                      z=None, delta_bias=None, delta_softplus=True, out=None, zoh_exact=False,
+                      stream=None):
+    """One decode step with the fused front end (ss_state_update_conv): state (batch, d_inner,
+    d_state) float32 and conv_state (batch, k-1, d_inner) io dtype are updated in place; x,
+    delta, z: (batch, d_inner); conv_weight (d_inner, k) float32; conv_bias (d_inner,) or None."""
+    batch, d_inner, d_state = state.shape
+    code = _dtype_code(x)
+    k = conv_weight.shape[-1]
+    _dev(state, "state", torch.float32)
+    _dev(conv_state, "conv_state", x.dtype, (batch, k - 1, d_inner))
+    for name, t in (("x", x), ("delta", delta), ("z", z)):
+        _dev(t, name, x.dtype, (batch, d_inner))
+    for name, t in (("B", B), ("C", C)):
+        _dev(t, name, x.dtype, (batch, d_state))
+    _dev(conv_weight, "conv_weight", torch.float32, (d_inner, k))
+    _dev(conv_bias, "conv_bias", torch.float32, (d_inner,))
+    _dev(A, "A", torch.float32, (d_inner, d_state))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(delta_bias, "delta_bias", torch.float32, (d_inner,))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype, (batch, d_inner))
+    _check(lib().ss_state_update_conv(
+        _ptr(state), _ptr(conv_state), _ptr(x), _ptr(conv_weight), _ptr(conv_bias), int(k),
+        _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        1 if delta_softplus else 0, _ptr(out), batch, d_inner, d_state, code,
+        SS_FLAG_ZOH_EXACT if zoh_exact else 0, _stream(stream)))
     return out
