@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libssscan.so")
 SOURCES = ["ss_api.hip", "ss_scan_fwd.hip", "ss_scan_zoh.hip", "ss_scan_conv.hip",
-           "ss_scan_conv_zoh.hip", "ss_state_update.hip", "ss_scan_bwd.hip", "ss_scan2.hip"]
+           "ss_scan_conv_zoh.hip", "ss_state_update.hip", "ss_scan_bwd.hip", "ss_scan2.hip",
+           "ss_scan2_mfma.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled (-packed-fp32-ops); the host pass warns that it

@@ -488,7 +488,10 @@ ss_status scan2_impl(const void* x, const void* dt, const float* A, const void* 
   a.softplus = dt_softplus ? 1 : 0;
   if (batch * nheads * a.n_pblk > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many workgroups");
-  const hipError_t e = ss::launch_scan2(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  const bool bf16 = dtype == SS_BF16;
+  const hipError_t e = ss::scan2_mfma_supported(a, bf16)
+                           ? ss::launch_scan2_mfma(a, static_cast<hipStream_t>(stream))
+                           : ss::launch_scan2(a, bf16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -137,6 +137,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Wait until this wave's outstanding LDS reads have returned.  A workgroup barrier orders LDS
+// writes but does not wait for reads still in flight, so a read whose value is consumed only
+// after a barrier, of memory that other waves overwrite after it, needs this before the barrier.
+__device__ __forceinline__ void lds_reads_done() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Remap the hardware
 // workgroup index so that each XCD receives one contiguous range of logical indices: logical
 // neighbours (which share cache lines of the inputs) then meet in the same L2.  A bijection on

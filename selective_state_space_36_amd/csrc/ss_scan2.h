@@ -31,4 +31,10 @@ struct Scan2Args {
 
 hipError_t launch_scan2(const Scan2Args& a, bool bf16, hipStream_t stream);
 
+// The chunked form on the matrix cores (ss_scan2_mfma.hip): bf16 io, headdim 64, d_state 64 or
+// 128, 16-byte aligned x, z, out, B and C.
+constexpr int kScan2MfmaChunk = 64;
+bool scan2_mfma_supported(const Scan2Args& a, bool bf16);
+hipError_t launch_scan2_mfma(const Scan2Args& a, hipStream_t stream);
+
 }  // namespace ss

@@ -30,14 +30,16 @@ def ops():
 F32W = wl.MultiHeadWorkload("test-f32", 2, 50, 4, 16, 2, 16, "f32", True, 3000)
 
 
-def run2(p, *, gate=True, skip=True, h0=None, heads=None):
+def run2(p, *, gate=True, skip=True, h0=None, heads=None, softplus=True):
     z = p["z"] if gate else None
     D = p["D"] if skip else None
     print(f"  scan2 case: x={p['x'].shape} N={p['B'].shape[-1]} G={p['B'].shape[2]} "
-          f"dtype={p['x'].dtype} gate={gate} h0={h0 is not None}", flush=True)
+          f"dtype={p['x'].dtype} gate={gate} skip={skip} h0={h0 is not None} "
+          f"softplus={softplus}", flush=True)
     out, hl = ops().scan2_fwd(dev(p["x"]), dev(p["dt"]), dev(p["A"]), dev(p["B"]), dev(p["C"]),
                               D=dev(D), z=dev(z), dt_bias=dev(p["dt_bias"]),
-                              h0=None if h0 is None else dev(h0), return_last_state=True)
+                              dt_softplus=softplus, h0=None if h0 is None else dev(h0),
+                              return_last_state=True)
     torch.cuda.synchronize()
     out, hl = host(out), host(hl)
     if heads is not None:  # the oracle on a subset of heads (heads are independent)
@@ -47,7 +49,7 @@ def run2(p, *, gate=True, skip=True, h0=None, heads=None):
                                   dt_bias=p["dt_bias"][heads])
         return out[:, :, heads], hl[:, heads], ro, rh
     ro, rh = oracle.scan2_fwd(p["x"], p["dt"], p["A"], p["B"], p["C"], D=D, z=z,
-                              dt_bias=p["dt_bias"],
+                              dt_bias=p["dt_bias"], dt_softplus=softplus,
                               h0=None if h0 is None else h0.astype(np.float64))
     return out, hl, ro, rh
 
@@ -76,6 +78,44 @@ def test_medium_bf16_scan2():
     g, gh, r, rh = run2(p)
     check_close(g, r, TOL["bf16"], "out")
     check_close(gh, rh, TOL["f32"], "h_last")
+
+
+# bf16 with headdim 64 and d_state 64 or 128 runs the chunked form on the matrix cores (64-step
+# chunks): sequence lengths below, at and across chunk boundaries, both state sizes, groups.
+@pytest.mark.parametrize("L,H,G,N", [(1, 2, 1, 128), (63, 2, 1, 128), (64, 3, 1, 64),
+                                     (65, 2, 2, 128), (200, 4, 2, 64), (333, 2, 1, 128)])
+def test_chunked_bf16_scan2(L, H, G, N):
+    p = wl.make_multihead(wl.MULTIHEAD, batch=2, seqlen=L, nheads=H, ngroups=G, d_state=N,
+                          seed=11 * L + N)
+    h0 = np.random.default_rng(L).standard_normal((2, H, N, 64)).astype(np.float32)
+    g, gh, r, rh = run2(p, h0=h0)
+    check_close(g, r, TOL["bf16"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+@pytest.mark.parametrize("gate,skip,softplus", [(False, False, True), (True, False, False),
+                                                (False, True, True)])
+def test_chunked_bf16_scan2_options(gate, skip, softplus):
+    """The scan isolated (no skip, no gate) shows the state path alone at the bf16 bound; without
+    softplus the raw dt (plus bias) is the step."""
+    p = wl.make_multihead(wl.MULTIHEAD, batch=1, seqlen=150, nheads=3, seed=5)
+    if not softplus:  # keep the steps positive: |dt| small around the bias's dt
+        p["dt"] = wl.f32_to_bf16_bits(np.abs(0.01 * np.random.default_rng(6).standard_normal(
+            p["dt"].shape)).astype(np.float32))
+        p["dt_bias"] = np.full_like(p["dt_bias"], 0.02)
+    g, gh, r, rh = run2(p, gate=gate, skip=skip, softplus=softplus)
+    check_close(g, r, TOL["bf16"], "out")
+    check_close(gh, rh, TOL["f32"], "h_last")
+
+
+def test_chunked_scan2_scan_part_tight():
+    """Without skip and gate the output is the scan alone; compared before the bf16 output
+    rounding matters (a tolerance of 2^-8 relative, the output's own rounding) it checks that the
+    split products keep the chunked form close to fp32."""
+    p = wl.make_multihead(wl.MULTIHEAD, batch=1, seqlen=640, nheads=2, seed=9)
+    g, gh, r, rh = run2(p, gate=False, skip=False)
+    check_close(g, r, 2.0 ** -8, "out (scan only)")
+    check_close(gh, rh, 2e-5, "h_last")
 
 
 def test_empty_and_invalid_scan2():
