@@ -75,12 +75,20 @@ __device__ __forceinline__ uint32_t highs(uint32_t a, uint32_t b) {
 // are reused within a chunk: once every wave is past the C B^T tiles and the state update, the
 // B tile holds each wave's z tile (p, t); and once a wave has read its x for the epilogue, its
 // own 16 rows of the x tile hold its output tile (t, p).
+// Column of element s in row r of a transposed tile ((p, s) for x, (n, s) for B): the eight
+// 16-byte groups of a row are XOR-permuted by (r / 8) mod 8.  The transposed stores write rows
+// 4 or 8 apart from neighbouring lanes, which would otherwise land on the same LDS banks; the
+// MFMA operand reads (16 bytes of 8 consecutive s) stay contiguous and conflict-free.
+__device__ __forceinline__ int swz(int r, int s) {
+  return (((s >> 3) ^ ((r >> 3) & 7)) << 3) | (s & 7);
+}
+
 template <int N>
 struct alignas(16) Smem2 {
   uint16_t b[kQ][N + 8];        // B of the chunk, (s, n); later: per-wave z tiles
-  uint16_t bt[N][kTP];          // B transposed, (n, s)
+  uint16_t bt[N][kTP];          // B transposed, (n, s) (swizzled)
   uint16_t c[kQ][N + 8];        // C, (t, n)
-  uint16_t xt[kP][kTP];         // x transposed, (p, s); later: per-wave output tiles
+  uint16_t xt[kP][kTP];         // x transposed, (p, s) (swizzled); later: per-wave output tiles
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
   uint16_t mlo[kQ][kTP];        // low part
   float ac[kQ];                 // c_t, the chunk's cumulative log2 decay
@@ -106,7 +114,8 @@ __device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
 }
 
 template <int N, bool GATE>
-__global__ void __launch_bounds__(256) scan2_mfma_kernel(Scan2Args a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+scan2_mfma_kernel(Scan2Args a) {
   constexpr int NT = N / 16;         // 16-row tiles of the state
   constexpr int KB = N / 32;         // 32-wide K blocks over the states
   constexpr int UNITS = 2 * N;       // (4-row, 8-state) pieces of a B or C tile
@@ -238,7 +247,7 @@ __global__ void __launch_bounds__(256) scan2_mfma_kernel(Scan2Args a) {
       for (int r = 0; r < 4; ++r) r4[r] = w == 0 ? xr[r].x : xr[r].y;
       const uint2 v = (cc & 1) ? make_uint2(highs(r4[0], r4[1]), highs(r4[2], r4[3]))
                                : make_uint2(lows(r4[0], r4[1]), lows(r4[2], r4[3]));
-      *reinterpret_cast<uint2*>(&sm.xt[4 * xp + cc][4 * xq]) = v;
+      *reinterpret_cast<uint2*>(&sm.xt[4 * xp + cc][swz(4 * xp + cc, 4 * xq)]) = v;
     }
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
@@ -260,7 +269,7 @@ __global__ void __launch_bounds__(256) scan2_mfma_kernel(Scan2Args a) {
           }
           const uint2 v = (cc & 1) ? make_uint2(highs(r4[0], r4[1]), highs(r4[2], r4[3]))
                                    : make_uint2(lows(r4[0], r4[1]), lows(r4[2], r4[3]));
-          *reinterpret_cast<uint2*>(&sm.bt[8 * nb + cc][4 * rq]) = v;
+          *reinterpret_cast<uint2*>(&sm.bt[8 * nb + cc][swz(8 * nb + cc, 4 * rq)]) = v;
         }
       }
     }
@@ -357,7 +366,7 @@ __global__ void __launch_bounds__(256) scan2_mfma_kernel(Scan2Args a) {
       for (int nt = 0; nt < NT; ++nt) S[nt] *= eEnd;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        xop[kb] = *reinterpret_cast<const Op*>(&sm.xt[p][32 * kb + 8 * g4]);
+        xop[kb] = *reinterpret_cast<const Op*>(&sm.xt[p][swz(p, 32 * kb + 8 * g4)]);
         const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4]);
         const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4 + 4]);
         const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -368,7 +377,8 @@ __global__ void __launch_bounds__(256) scan2_mfma_kernel(Scan2Args a) {
                  wlo.w[q]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const Op bt = *reinterpret_cast<const Op*>(&sm.bt[16 * nt + l16][32 * kb + 8 * g4]);
+          const Op bt = *reinterpret_cast<const Op*>(
+              &sm.bt[16 * nt + l16][swz(16 * nt + l16, 32 * kb + 8 * g4)]);
           S[nt] = mfma(bt, whi, S[nt]);
           S[nt] = mfma(bt, wlo, S[nt]);
         }
@@ -405,7 +415,7 @@ __global__ void __launch_bounds__(256) scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tb = 16 * j + 4 * g4;
-      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.xt[p][tb]);
+      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.xt[p][swz(p, tb)]);
       xs[j][0] = lo_f(xv.x);
       xs[j][1] = hi_f(xv.x);
       xs[j][2] = lo_f(xv.y);
