@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X
 # VALU issue slots per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one 64-lane wave op
 # every 4 cycles per SIMD).  Non-packed fp32 ops take one slot; v_exp_f32 takes two on gfx950.
 PEAK_VALU_SLOTS = 256 * 4 * 16 * 2.4e9
@@ -71,6 +72,7 @@ def log(msg):
 KERNEL_SOURCES = {
     "mamba2.8b-prefill": ["ss_device.h", "ss_launch.h", "ss_scan_kernel.h", "ss_scan_fwd.hip"],
     "decode-b128": ["ss_device.h", "ss_launch.h", "ss_state_update.hip"],
+    "mamba2-80h-prefill": ["ss_device.h", "ss_scan2.h", "ss_scan2_mfma.hip"],
 }
 
 
@@ -406,7 +408,9 @@ def bench_decode(args, torch, np, ops, wl):
 
 
 def bench_multihead(args, torch, np, ops, wl):
-    """The multi-head scalar-transition scan (ss_scan2_fwd) on the Mamba-2-shaped layer."""
+    """The multi-head scalar-transition scan (ss_scan2_fwd) on the Mamba-2-shaped layer: bf16
+    with headdim 64 and d_state 128 runs the chunked dual form on the matrix cores.  Its floor is
+    HBM (the algorithmic bytes at 8 TB/s); the MFMA work is reported alongside."""
     w = wl.MULTIHEAD
     log(f"generating {w.name} inputs")
     p = wl.make_multihead(w)
@@ -437,18 +441,32 @@ def bench_multihead(args, torch, np, ops, wl):
     go = out[:, :, torch.from_numpy(heads).cuda()].float().cpu().numpy().astype(np.float64)
     err = np.abs(go - ro)
     ok = bool(np.all(err <= 2e-2 + 2e-2 * np.abs(ro)))
-    N, P = w.d_state, w.headdim
-    slots = w.elements * (3 * N + 10)   # per update: x.dt*B, state FMA, C.h FMA; per element ~10
+    N, P, Q = w.d_state, w.headdim, 64
     nbytes = 3 * w.elements * 2 + w.batch * w.seqlen * w.nheads * 2 \
         + 2 * w.batch * w.seqlen * w.ngroups * N * 2 + 3 * w.nheads * 4
+    # dense products of the chunked form per (batch, head, 64-step chunk): the 10 causal 16x16
+    # tiles of C B^T (K = N) and of M X (K = 16 per tile pair), the state update B^T (w o X) and
+    # C S_in; "executed" counts the second (low-part) product of each split fp32 operand
+    chunks = w.batch * w.nheads * ((w.seqlen + Q - 1) // Q)
+    cb, mx = 10 * 16 * 16 * N * 2, 10 * 16 * 16 * 16 * 2 * P // 16
+    st, yo = 2 * N * Q * P, 2 * Q * N * P
+    flops = chunks * (cb + mx + st + yo)
+    mx_exec = 192 * 16 * P * 2  # M X runs in 32-wide K blocks: 32 + 32 + 64 + 64 per t-tile
+    flops_exec = chunks * (cb + 2 * mx_exec + 2 * st + 2 * yo)
+    sec = ms * 1e-3
     return dict(workload=w.name, batch=w.batch, seq_len=w.seqlen, nheads=w.nheads, headdim=P,
                 ngroups=w.ngroups, d_state=N, us_per_call=round(ms * 1e3, 2),
-                elements_per_s=round(w.elements / (ms * 1e-3), 1),
-                roofline=dict(bound="alu", achieved=round(slots / (ms * 1e-3) / 1e12, 3),
-                              peak=round(PEAK_VALU_SLOTS / 1e12, 3), unit="T VALU-slot/s",
-                              frac=round(slots / (ms * 1e-3) / PEAK_VALU_SLOTS, 4)),
-                hbm=dict(algorithmic_bytes=nbytes,
-                         achieved_GBps=round(nbytes / (ms * 1e-3) / 1e9, 1)),
+                elements_per_s=round(w.elements / sec, 1),
+                kernel="scan2_mfma_kernel (chunked dual form, 64-step chunks, bf16 MFMA)",
+                roofline=dict(bound="hbm", achieved=round(nbytes / sec / 1e9, 1),
+                              peak=PEAK_HBM_GBPS, unit="GB/s",
+                              frac=round(nbytes / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                              traffic=measured_traffic(w.name)),
+                mfma=dict(algorithmic_tflops=round(flops / sec / 1e12, 1),
+                          executed_tflops=round(flops_exec / sec / 1e12, 1),
+                          peak_tflops=PEAK_BF16_TFLOPS,
+                          frac_executed=round(flops_exec / sec / 1e12 / PEAK_BF16_TFLOPS, 4)),
+                hbm=dict(algorithmic_bytes=nbytes),
                 parity_spot_check=dict(ok=ok, max_abs_err=float(err.max())))
 
 
