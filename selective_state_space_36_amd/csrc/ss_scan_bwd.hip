@@ -19,9 +19,9 @@
 // walks the chunks backwards: it recomputes the chunk's 16 states and decays from the stored
 // state into registers, computes y for the gate's derivative, then runs the adjoint backwards
 // through the 16 steps.  Sums over a channel's states go through per-wave LDS tiles (summed by
-// the owner lane of the step, as in the forward); sums over channels (dB, dC) are reduced across
-// the wave's four rows by row swaps and across the four waves in LDS, then added to global
-// memory with one atomic per (step, state) and workgroup; dA, dD and dbias likewise once per
+// the owner lane of the step, as in the forward); sums over channels (dB, dC) are reduced over
+// row pairs by a row swap and over the eight pairs in LDS, then added to global memory with one
+// atomic per (step, state) and workgroup; dA, dD and dbias likewise once per
 // workgroup.  The atomic sums make dA, dB, dC, dD and dbias reproducible only up to rounding
 // order.
 #include <hip/hip_runtime.h>
@@ -37,15 +37,12 @@ namespace {
 
 constexpr int kT = kBwdChunk;
 
-// Sum of x over the four 16-lane rows of the wave, in every lane (row swaps with
-// v_permlane16_swap / v_permlane32_swap: VALU only, no LDS traffic).
-__device__ __forceinline__ float sum_rows(float x) {
+// Sum of x over row pairs (0, 1) and (2, 3) of the wave, in every lane of the pair (a row swap
+// with v_permlane16_swap: VALU only, no LDS traffic).
+__device__ __forceinline__ float sum_row_pairs(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
-                                                  false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 constexpr int kPRow = 336;  // floats per channel row of a partial tile (padding)
 constexpr int kPTau = 20;   // floats per step of a partial tile (padding)
@@ -62,7 +59,7 @@ struct BwdKernel {
     elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
     float p[4][4 * kPRow];          // per wave: partial sums over states (y, then ddt)
     float q[4][4 * kPRow];          // per wave: partial sums over states (du)
-    float gbc[2][4][kT][16];        // per wave: dB and dC summed over the wave's channels
+    float gbc[2][8][kT][16];        // per row pair: dB and dC summed over its two channels
   };
 
   static __device__ __forceinline__ void run(const BwdArgs& a) {
@@ -212,7 +209,8 @@ struct BwdKernel {
       // the adjoint backwards through the chunk
       float* qw = &sm.q[wave][r * kPRow + k];
       rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
-                lam, e_next, ga, pw, qw, &sm.gbc[0][wave][0][0], &sm.gbc[1][wave][0][0], r, k);
+                lam, e_next, ga, pw, qw, &sm.gbc[0][2 * wave + (r >> 1)][0][0],
+                &sm.gbc[1][2 * wave + (r >> 1)][0][0], r, k);
       wave_lds_sync();
       float gdt = 0.0f, gx = 0.0f;
       {
@@ -223,6 +221,7 @@ struct BwdKernel {
           gdt += pr[i];
           gx += qr[i];
         }
+        gdt = fmaf(xu, gx, gdt);  // + u_t sum_n lam B, the input term of ddt
       }
       if (own_ok) {
         const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
@@ -236,10 +235,12 @@ struct BwdKernel {
       __syncthreads();  // the wave tiles of dB and dC, and the next chunk's tiles, are complete
       {
         const int tau = tid >> 4, n = tid & 15;
-        const float sb = sm.gbc[0][0][tau][n] + sm.gbc[0][1][tau][n] + sm.gbc[0][2][tau][n] +
-                         sm.gbc[0][3][tau][n];
-        const float sc = sm.gbc[1][0][tau][n] + sm.gbc[1][1][tau][n] + sm.gbc[1][2][tau][n] +
-                         sm.gbc[1][3][tau][n];
+        float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+        for (int pr = 0; pr < 8; ++pr) {
+          sb += sm.gbc[0][pr][tau][n];
+          sc += sm.gbc[1][pr][tau][n];
+        }
         if (tau < nv && n < N) {
           const int64_t o = (row0 + int64_t(c) * kT + tau) * N + n;
           atomicAdd(a.dB + o, sb);
@@ -304,8 +305,9 @@ struct BwdKernel {
   }
 
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
-  // contributions.  Partial sums over states go to the wave tiles pw (ddt) and qw (du); dB and
-  // dC are summed over the wave's four channels (rows) and stored by row 0.
+  // contributions.  Partial sums over states go to the wave tiles pw (the A e h_prev part of ddt)
+  // and qw (lam B, which gives du and the u B part of ddt); dB and dC are summed over each pair of
+  // the wave's channels (rows) and stored by rows 0 and 2.
   template <int TAU>
   static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float xu, float gy, float a_n, float hprev,
@@ -322,11 +324,11 @@ struct BwdKernel {
     const float rr = lam * ee[TAU] * hp;
     ga = fmaf(row_bcast<TAU>(dt), rr, ga);
     const float qq = lam * bb;
-    pw[TAU * kPTau] = fmaf(a_n, rr, qq * row_bcast<TAU>(xu));
+    pw[TAU * kPTau] = a_n * rr;
     qw[TAU * kPTau] = qq;
-    const float gb = sum_rows(lam * row_bcast<TAU>(du));
-    const float gc = sum_rows(gyb * hh[TAU]);
-    if (r == 0) {
+    const float gb = sum_row_pairs(lam * row_bcast<TAU>(du));
+    const float gc = sum_row_pairs(gyb * hh[TAU]);
+    if ((r & 1) == 0) {
       gbw[TAU * 16 + k] = gb;
       gcw[TAU * 16 + k] = gc;
     }
