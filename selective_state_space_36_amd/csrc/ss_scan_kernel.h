@@ -66,6 +66,13 @@ struct ScanKernel {
   static_assert(kT * PIECES <= 64, "one 16-byte piece of a tile per lane of a wave");
   static_assert(NTEN < kWaves, "a wave left over for the output tile");
   static constexpr int BC_PER_THREAD = kT * NP / kPrefillThreads;
+  // The 16-byte pieces of row (step) k of a u/delta/z/out tile are stored XOR-permuted by
+  // (k / (8 / PIECES)) mod PIECES.  The owner lanes of steps 4 (bf16) or 2 (fp32) apart read the
+  // same column of rows that share LDS banks (rows are 32 or 64 bytes; LDS has 32 banks of 4
+  // bytes); the permutation moves half of them to the other bank set.
+  static __device__ __forceinline__ int pswz(int row) {
+    return (row / (8 / PIECES)) & (PIECES - 1);
+  }
 
   struct alignas(16) Smem {
     float2 bc[2][NP][kTileStride];  // (B_t[n], C_t[n]) per chunk
@@ -231,7 +238,7 @@ struct ScanKernel {
 #pragma unroll
       for (int i = 0; i < BC_PER_THREAD; ++i)
         sm.bc[buf][bc_n[i]][bc_tau[i]] = make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
-      if (wave_u < NTEN && tl_on) sm.in[buf][wave_u][tl_row][tl_pc] = pre.rin;
+      if (wave_u < NTEN && tl_on) sm.in[buf][wave_u][tl_row][tl_pc ^ pswz(tl_row)] = pre.rin;
     };
     // The data registers of the last output store are kept live (hold_store) until the next
     // chunk's compute is done: otherwise the allocator reuses them at once and the write to them
@@ -244,7 +251,7 @@ struct ScanKernel {
     auto store_out = [&](int buf, int ci) {
       if (!SUMMARY && wave_u == NTEN && tl_on) {
         const rsrc_t ro = io_buf(a.out, ci);
-        const uint4 v = sm.out[buf][tl_row][tl_pc];
+        const uint4 v = sm.out[buf][tl_row][tl_pc ^ pswz(tl_row)];
         if (VEC) {
           st_val = v;
           buf_store(v, ro, tl_off);
@@ -257,9 +264,11 @@ struct ScanKernel {
         }
       }
     };
+    // column of channel cl in row k of a tile (pieces permuted by pswz)
+    const int own_col = ((cl / (16 / ES)) ^ pswz(k)) * (16 / ES) + cl % (16 / ES);
     auto own_in = [&](int buf, int ten) -> float {
       const elem* t = reinterpret_cast<const elem*>(&sm.in[buf][ten][k][0]);
-      return IO::widen(t[cl]);
+      return IO::widen(t[own_col]);
     };
 
     float dt_acc = 0.0f;  // summary pass: this lane's share of sum(dt) over the segment
@@ -311,7 +320,7 @@ struct ScanKernel {
                   (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
         y = fmaf(dskip, xu, y);
         if (GATE) y *= silu_f(own_in(buf, 2));
-        reinterpret_cast<elem*>(&sm.out[buf][k][0])[cl] = IO::from_float(y);
+        reinterpret_cast<elem*>(&sm.out[buf][k][0])[own_col] = IO::from_float(y);
       }
       hold_store();
       if (has_next) stage_chunk(buf ^ 1);
