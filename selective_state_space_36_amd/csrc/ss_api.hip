@@ -407,6 +407,8 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   a.n_cblk = (d_inner + 15) / 16;
   a.d_state = static_cast<int32_t>(d_state);
   a.softplus = delta_softplus ? 1 : 0;
+  a.vec_io = (d_inner % 16 == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
+              aligned(delta, 16) && aligned(dout, 16) && (!z || aligned(z, 16))) ? 1 : 0;
   if (batch * a.n_cblk > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
   const hipError_t e =

@@ -37,6 +37,7 @@ struct BwdArgs {
   int64_t n_cblk;        // channel blocks of 16 per batch row
   int32_t d_state;
   int32_t softplus;
+  int32_t vec_io;        // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, dout
 };
 
 // Zero the accumulated outputs, then run the backward (one workgroup per 16 channels of a batch

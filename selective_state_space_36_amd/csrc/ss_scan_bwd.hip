@@ -47,14 +47,20 @@ __device__ __forceinline__ float sum_row_pairs(float x) {
 constexpr int kPRow = 336;  // floats per channel row of a partial tile (padding)
 constexpr int kPTau = 20;   // floats per step of a partial tile (padding)
 
-template <class IO, bool GATE>
+template <class IO, bool GATE, bool VEC>
 struct BwdKernel {
   using elem = typename IO::elem;
   static constexpr int ES = sizeof(elem);
   static constexpr int PIECE_E = 16 / ES;        // elements per 16-byte piece
   static constexpr int PIECES = 16 / PIECE_E;    // pieces per 16-channel tile row
+  // The 16-byte pieces of row (step) k of an input tile are stored XOR-permuted by
+  // (k / (8 / PIECES)) mod PIECES, so that the owner lanes of steps 4 (bf16) or 2 (fp32) apart
+  // do not read the same LDS banks (32 banks of 4 bytes; rows are 32 or 64 bytes).
+  static __device__ __forceinline__ int pswz(int row) {
+    return (row / (8 / PIECES)) & (PIECES - 1);
+  }
 
-  struct Smem {
+  struct alignas(16) Smem {
     float2 bc[2][16][kT + 2];       // (B_t[n], C_t[n]) of the chunk, double-buffered
     elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
     float p[4][4 * kPRow];          // per wave: partial sums over states (y, then ddt)
@@ -102,6 +108,7 @@ struct BwdKernel {
     // Global loads of chunk c go to registers (issued before the current chunk is computed) and
     // are written to LDS buffer `buf` after it.
     elem pv[PIECE_E];
+    uint4 pvv{0, 0, 0, 0};
     float pbv = 0.0f, pcv = 0.0f;
     auto issue = [&](int c, bool full) {
       const int nv = nvalid_of(c);
@@ -111,8 +118,12 @@ struct BwdKernel {
       if (want) {
         const rsrc_t rt = make_buf(
             static_cast<const char*>(tens[wave_u]) + ((row0 + t0) * D + d0) * ES, io_bytes);
+        if (VEC) {
+          pvv = buf_load<uint4>(rt, tl_off);
+        } else {
 #pragma unroll
-        for (int e = 0; e < PIECE_E; ++e) pv[e] = buf_load<elem>(rt, tl_off + e * ES);
+          for (int e = 0; e < PIECE_E; ++e) pv[e] = buf_load<elem>(rt, tl_off + e * ES);
+        }
       }
       const uint32_t bc_bytes = static_cast<uint32_t>(nv * N * ES);
       const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + (row0 + t0) * N * ES, bc_bytes);
@@ -125,13 +136,18 @@ struct BwdKernel {
     auto stage = [&](int buf, bool full) {
       const bool want = (full || wave_u < 2) && (GATE || wave_u != 2);
       if (want && tl_on) {
+        elem* dst = &sm.in[buf][wave_u][tl_row][(tl_pc ^ pswz(tl_row)) * PIECE_E];
+        if (VEC) {
+          *reinterpret_cast<uint4*>(dst) = pvv;
+        } else {
 #pragma unroll
-        for (int e = 0; e < PIECE_E; ++e)
-          sm.in[buf][wave_u][tl_row][tl_pc * PIECE_E + e] = pv[e];
+          for (int e = 0; e < PIECE_E; ++e) dst[e] = pv[e];
+        }
       }
       sm.bc[buf][bc_n][bc_tau] = make_float2(pbv, full ? pcv : 0.0f);
     };
-    auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][cl]); };
+    const int own_col = ((cl / PIECE_E) ^ pswz(k)) * PIECE_E + cl % PIECE_E;
+    auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][own_col]); };
 
     // ---- pass 1: forward, storing each chunk's end state
     float h = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
@@ -349,9 +365,9 @@ struct BwdKernel {
   }
 };
 
-template <class IO, bool GATE>
+template <class IO, bool GATE, bool VEC>
 __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdArgs a) {
-  BwdKernel<IO, GATE>::run(a);
+  BwdKernel<IO, GATE, VEC>::run(a);
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
@@ -371,10 +387,17 @@ template <class IO>
 void launch_io(const BwdArgs& a, hipStream_t stream) {
   if (a.batch * a.n_cblk == 0) return;  // nothing but the zeroed sums
   const dim3 grid(static_cast<unsigned>(a.batch * a.n_cblk)), block(kBwdThreads);
-  if (a.z)
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, false>), grid, block, 0, stream, a);
+  if (a.vec_io) {
+    if (a.z)
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (a.z)
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, false>), grid, block, 0, stream, a);
+  }
 }
 
 }  // namespace
