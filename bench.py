@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-multihead", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -500,9 +500,19 @@ def cpu_baseline(args, np, w, p):
     elems = nrows * w.seqlen * reps
     log(f"cpu oracle: {nrows} rows x {w.seqlen} steps x {reps} runs in {total:.1f} s on "
         f"{threads} threads")
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return dict(value=round(elems / total, 1), unit="elements/s", cores=threads, kind="oracle",
                 sample=f"{nrows} of {rows_all} (b,d) rows of {w.name}, all {w.seqlen} steps, "
-                       f"{reps} run(s), {total:.1f} s wall")
+                       f"{reps} run(s), {total:.1f} s wall",
+                cpu_model=model)
 
 
 def main():
