@@ -37,15 +37,20 @@ namespace {
 
 constexpr int kT = kBwdChunk;
 
-// Sum of x over row pairs (0, 1) and (2, 3) of the wave, in every lane of the pair (a row swap
-// with v_permlane16_swap: VALU only, no LDS traffic).
-__device__ __forceinline__ float sum_row_pairs(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+// Sums over the row pairs (0, 1) and (2, 3) of the wave of two quantities at once: x in rows 0
+// and 2 of the result, y in rows 1 and 3.  v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second, leaving (x0, y0, x2, y2) and (x1, y1, x3, y3).
+__device__ __forceinline__ float sum_row_pairs2(float x, float y) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false,
                                                   false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 constexpr int kPRow = 336;  // floats per channel row of a partial tile (padding)
 constexpr int kPTau = 20;   // floats per step of a partial tile (padding)
+// dB and dC partial tiles: 8 row pairs x kBwdChunk steps x 16 states each; the dC half starts 16
+// floats after the dB half so that rows 0 and 1 of a wave, which write the two halves with one
+// instruction, use different LDS banks.
+constexpr int kGcOff = 8 * kBwdChunk * 16 + 16;
 
 template <class IO, bool GATE, bool VEC>
 struct BwdKernel {
@@ -65,7 +70,7 @@ struct BwdKernel {
     elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
     float p[4][4 * kPRow];          // per wave: partial sums over states (y, then ddt)
     float q[4][4 * kPRow];          // per wave: partial sums over states (du)
-    float gbc[2][8][kT][16];        // per row pair: dB and dC summed over its two channels
+    float gbc[kGcOff + 8 * kT * 16];  // per row pair: dB, then dC, summed over its channels
   };
 
   static __device__ __forceinline__ void run(const BwdArgs& a) {
@@ -224,9 +229,9 @@ struct BwdKernel {
 
       // the adjoint backwards through the chunk
       float* qw = &sm.q[wave][r * kPRow + k];
+      float* gbc_w = &sm.gbc[(r & 1) * kGcOff + (2 * wave + (r >> 1)) * kT * 16];
       rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
-                lam, e_next, ga, pw, qw, &sm.gbc[0][2 * wave + (r >> 1)][0][0],
-                &sm.gbc[1][2 * wave + (r >> 1)][0][0], r, k);
+                lam, e_next, ga, pw, qw, gbc_w, k);
       wave_lds_sync();
       float gdt = 0.0f, gx = 0.0f;
       {
@@ -254,8 +259,8 @@ struct BwdKernel {
         float sb = 0.0f, sc = 0.0f;
 #pragma unroll
         for (int pr = 0; pr < 8; ++pr) {
-          sb += sm.gbc[0][pr][tau][n];
-          sc += sm.gbc[1][pr][tau][n];
+          sb += sm.gbc[(pr * kT + tau) * 16 + n];
+          sc += sm.gbc[kGcOff + (pr * kT + tau) * 16 + n];
         }
         if (tau < nv && n < N) {
           const int64_t o = (row0 + int64_t(c) * kT + tau) * N + n;
@@ -323,14 +328,13 @@ struct BwdKernel {
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
   // contributions.  Partial sums over states go to the wave tiles pw (the A e h_prev part of ddt)
   // and qw (lam B, which gives du and the u B part of ddt); dB and dC are summed over each pair of
-  // the wave's channels (rows) and stored by rows 0 and 2.
+  // the wave's channels (rows) together, rows 0 and 2 storing dB and rows 1 and 3 dC (gw).
   template <int TAU>
   static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float xu, float gy, float a_n, float hprev,
                                                   const float (&hh)[kT], const float (&ee)[kT],
                                                   float& lam, float& e_next, float& ga, float* pw,
-                                                  float* qw, float* gbw, float* gcw, int r,
-                                                  int k) {
+                                                  float* qw, float* gw, int k) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
@@ -342,12 +346,7 @@ struct BwdKernel {
     const float qq = lam * bb;
     pw[TAU * kPTau] = a_n * rr;
     qw[TAU * kPTau] = qq;
-    const float gb = sum_row_pairs(lam * row_bcast<TAU>(du));
-    const float gc = sum_row_pairs(gyb * hh[TAU]);
-    if ((r & 1) == 0) {
-      gbw[TAU * 16 + k] = gb;
-      gcw[TAU * 16 + k] = gc;
-    }
+    gw[TAU * 16 + k] = sum_row_pairs2(lam * row_bcast<TAU>(du), gyb * hh[TAU]);
     e_next = ee[TAU];
   }
   template <int... TAUS>
@@ -357,10 +356,10 @@ struct BwdKernel {
                                                    float hprev, const float (&hh)[kT],
                                                    const float (&ee)[kT], float& lam,
                                                    float& e_next, float& ga, float* pw, float* qw,
-                                                   float* gbw, float* gcw, int r, int k) {
+                                                   float* gw, int k) {
     // fold over the steps in decreasing order
     (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, hprev, hh, ee, lam, e_next, ga, pw, qw,
-                             gbw, gcw, r, k),
+                             gw, k),
      ...);
   }
 };
