@@ -226,6 +226,30 @@ def bench_prefill(args, torch, np, ops, wl):
     ms_bwd = e0.elapsed_time(e1) / bsteps
     log(f"backward {ms_bwd * 1e3:.1f} us per call")
     del ws_b
+    # the training path: the forward saving its chunk-end states (ss_scan_fwd_states), then the
+    # backward taking them (SS_FLAG_STATES_GIVEN) instead of rerunning the forward
+    st_buf = torch.empty((w.batch, w.d_inner, (w.seqlen + 15) // 16, w.d_state),
+                         dtype=torch.float32, device="cuda")
+    st_out = torch.empty_like(u)
+    fwd_s = lambda: ops.scan_fwd_states(u, dl, A, B, C, D=D, z=z, delta_bias=db, out=st_out,
+                                        states=st_buf, workspace=ws, stream=stream)
+    bwd_s = lambda: ops.scan_bwd(u, dl, A, B, C, dout, D=D, z=z, delta_bias=db, states=st_buf,
+                                 stream=stream)
+    fwd_s()
+    bwd_s()
+    torch.cuda.synchronize()
+    times = {}
+    for name, fn in (("fwd", fwd_s), ("bwd", bwd_s)):
+        e0.record(stream)
+        for _ in range(bsteps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / bsteps
+    train = dict(ms_fwd_states=times["fwd"], ms_bwd_states=times["bwd"])
+    log(f"forward saving states {times['fwd'] * 1e3:.1f} us, backward given them "
+        f"{times['bwd'] * 1e3:.1f} us")
+    del st_buf, st_out
 
     # spot parity check of the benchmarked output on a few rows
     import oracle
@@ -259,7 +283,7 @@ def bench_prefill(args, torch, np, ops, wl):
         e = np.abs(gc[i] - rc[0, :, 0])
         ok = ok and bool(np.all(e <= 2e-2 + 2e-2 * np.abs(rc[0, :, 0])))
         errc = max(errc, float(e.max()))
-    return (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ms_bwd, ok,
+    return (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ms_bwd, train, ok,
             float(max(err.max(), errz.max(), errc)))
 
 
@@ -535,7 +559,7 @@ def main():
         return
     ops.lib()
 
-    (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ms_bwd, ok,
+    (w, p, ms_step, ms_kernel, ms_zoh, ms_conv, ms_bwd, train, ok,
      maxerr) = bench_prefill(args, torch, np, ops, wl)
     elems = w.elements
     value = elems / (ms_step * 1e-3)
@@ -582,7 +606,13 @@ def main():
                      "elements_per_s": round(elems / (ms_bwd * 1e-3), 1),
                      "ratio_to_forward": round(ms_bwd / ms_kernel, 2),
                      "note": "ss_scan_bwd (forward pass storing chunk-end states + reverse pass "
-                             "recomputing each chunk), all input gradients"},
+                             "recomputing each chunk), all input gradients",
+                     "with_saved_states": {
+                         "forward_us": round(train["ms_fwd_states"] * 1e3, 2),
+                         "backward_us": round(train["ms_bwd_states"] * 1e3, 2),
+                         "note": "ss_scan_fwd_states (the forward also writing the 335 MB of "
+                                 "chunk-end states) then ss_scan_bwd with SS_FLAG_STATES_GIVEN "
+                                 "(no forward pass of its own)"}},
         "parity_spot_check": {"ok": ok, "max_abs_err": maxerr},
     }
     if not args.no_multihead:

@@ -53,14 +53,18 @@ typedef enum {
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 
 /*
- * Option bits of the _ex entry points (any other bit -> SS_ERR_UNSUPPORTED).
- *   SS_FLAG_ZOH_EXACT: the input term uses the exact zero-order-hold discretisation of the
- *     continuous system (reading guide, "Método": B_bar = (dt A)^-1 (exp(dt A) - I) dt B, which
- *     for the diagonal A is B_bar[n] = (exp(dt A[d,n]) - 1) / A[d,n] * B[n], and dt * B[n] where
- *     A[d,n] == 0) in place of the first-order dt * B[n] of the default (aivaro.ru, section 3).
- *     A_bar = exp(dt A) either way.  It costs a few more operations per state update.
+ * Option bits (an entry point given a bit it does not take -> SS_ERR_UNSUPPORTED).
+ *   SS_FLAG_ZOH_EXACT (prefill and decode): the input term uses the exact zero-order-hold
+ *     discretisation of the continuous system (reading guide, "Método": B_bar =
+ *     (dt A)^-1 (exp(dt A) - I) dt B, which for the diagonal A is B_bar[n] =
+ *     (exp(dt A[d,n]) - 1) / A[d,n] * B[n], and dt * B[n] where A[d,n] == 0) in place of the
+ *     first-order dt * B[n] of the default (aivaro.ru, section 3).  A_bar = exp(dt A) either
+ *     way.  It costs a few more operations per state update.
+ *   SS_FLAG_STATES_GIVEN (ss_scan_bwd only): the workspace already holds the chunk-end states
+ *     of these inputs, as written by ss_scan_fwd_states; the backward then skips its own
+ *     forward pass.
  */
-enum { SS_FLAG_ZOH_EXACT = 1 };
+enum { SS_FLAG_ZOH_EXACT = 1, SS_FLAG_STATES_GIVEN = 2 };
 
 /*
  * Prefill: the whole sequence in one call.
@@ -109,6 +113,28 @@ ss_status ss_scan_fwd_ex(const void* u, const void* delta, const float* A, const
 
 size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                       int64_t d_state, ss_dtype dtype, int32_t nseg);
+
+/*
+ * Prefill that also saves the state after every 16-step chunk, for a later backward (the
+ * reading guide, "Expansão de Estado Ciente de Hardware", keeps intermediate states out of
+ * memory and recomputes them in the backward pass; the chunk-end states are the points the
+ * recomputation restarts from).  As ss_scan_fwd (first-order input term), plus:
+ *   states : (batch, d_inner, ceil(seqlen / 16), d_state) float32, written: states[b,d,c,:] is
+ *            the state after step min(16 c + 15, seqlen - 1).  Caller-owned, of
+ *            ss_scan_fwd_states_bytes() bytes; it must not overlap the inputs, out, h_last or
+ *            the workspace.  With d_state <= 16 it is exactly the workspace ss_scan_bwd takes
+ *            with SS_FLAG_STATES_GIVEN.
+ */
+ss_status ss_scan_fwd_states(const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* delta_bias, int delta_softplus, const float* h0,
+                             float* h_last, void* out, float* states, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the states ss_scan_fwd_states writes for this shape (0 for an empty problem). */
+size_t ss_scan_fwd_states_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                int64_t d_state);
 
 /*
  * Prefill with the block's front end fused in: instead of u the call takes the block's x and
@@ -198,7 +224,10 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
                       ss_dtype dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
                       void* stream);
 
-/* Workspace bytes ss_scan_bwd needs for this shape (0 for an empty problem or d_state > 16). */
+/* Workspace bytes ss_scan_bwd needs for this shape (0 for an empty problem or d_state > 16).
+ * With flags SS_FLAG_STATES_GIVEN the workspace is read, not written: it must hold the states
+ * ss_scan_fwd_states wrote for the same u, delta, A, B, delta_bias, delta_softplus, h0, sizes
+ * and dtype (C, D and z do not enter the states). */
 size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                    int64_t d_state, ss_dtype dtype);
 

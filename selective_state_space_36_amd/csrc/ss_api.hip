@@ -97,9 +97,9 @@ ss_status check_dtype(ss_dtype dt, int64_t* esize) {
   return fail(SS_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
 }
 
-ss_status check_flags(uint32_t flags) {
-  if (flags & ~uint32_t(SS_FLAG_ZOH_EXACT))
-    return fail(SS_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags & ~uint32_t(SS_FLAG_ZOH_EXACT));
+ss_status check_flags(uint32_t flags, uint32_t allowed = SS_FLAG_ZOH_EXACT) {
+  if (flags & ~allowed)
+    return fail(SS_ERR_UNSUPPORTED, "flag bits 0x%x not taken here", flags & ~allowed);
   return SS_OK;
 }
 
@@ -110,7 +110,7 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
                     void* workspace, size_t workspace_bytes, int32_t nseg_req, bool forced,
                     uint32_t flags, void* stream, const float* conv_w = nullptr,
                     const float* conv_b = nullptr, const void* x_prev = nullptr,
-                    int32_t conv_k = 0) {
+                    int32_t conv_k = 0, float* states = nullptr) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
@@ -179,6 +179,19 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
     if (overlap(rh, in)) return fail(SS_ERR_INVALID_ARG, "h_last overlaps %s", in.name);
   }
   if (overlap(ro, rh)) return fail(SS_ERR_INVALID_ARG, "out overlaps h_last");
+  const int64_t nct = (seqlen + ss::kChunk - 1) / ss::kChunk;
+  int64_t st_count = 0;
+  if (states) {
+    if (!aligned(states, 4)) return fail(SS_ERR_UNSUPPORTED, "states pointer misaligned");
+    if (!mul_ok(rows, nct, &st_count) || !mul_ok(st_count, d_state * 4, &st_count))
+      return fail(SS_ERR_INVALID_ARG, "states size overflows");
+    st_count /= 4;
+    const Range rs = range("states", states, st_count, 4);
+    for (const Range& in : ins)
+      if (overlap(rs, in)) return fail(SS_ERR_INVALID_ARG, "states overlaps %s", in.name);
+    if (overlap(rs, ro) || overlap(rs, rh))
+      return fail(SS_ERR_INVALID_ARG, "states overlaps out or h_last");
+  }
 
   // time split
   int32_t want = forced && nseg_req > 0 ? nseg_req : auto_nseg(batch, seqlen, d_inner);
@@ -229,7 +242,11 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
       if (overlap(rw, in)) return fail(SS_ERR_INVALID_ARG, "workspace overlaps %s", in.name);
     if (overlap(rw, ro) || overlap(rw, rh))
       return fail(SS_ERR_INVALID_ARG, "workspace overlaps an output");
+    if (states && overlap(rw, range("states", states, st_count, 4)))
+      return fail(SS_ERR_INVALID_ARG, "workspace overlaps states");
   }
+  a.states = states;
+  a.states_chunks = nct;
   const int64_t ncb = batch * a.n_cblk;
   if (ncb * nseg > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
@@ -342,7 +359,8 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
                    size_t workspace_bytes, uint32_t flags, void* stream) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
-  if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
+  if (check_flags(flags, SS_FLAG_ZOH_EXACT | SS_FLAG_STATES_GIVEN) != SS_OK)
+    return SS_ERR_UNSUPPORTED;
   if (flags & SS_FLAG_ZOH_EXACT)
     return fail(SS_ERR_UNSUPPORTED, "the backward implements the first-order input term only");
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
@@ -409,6 +427,7 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   a.softplus = delta_softplus ? 1 : 0;
   a.vec_io = (d_inner % 16 == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
               aligned(delta, 16) && aligned(dout, 16) && (!z || aligned(z, 16))) ? 1 : 0;
+  a.states_given = (flags & SS_FLAG_STATES_GIVEN) ? 1 : 0;
   if (batch * a.n_cblk > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
   const hipError_t e =
@@ -541,6 +560,29 @@ size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_i
   int32_t n;
   segments(seqlen, nseg > 0 ? nseg : auto_nseg(batch, seqlen, d_inner), &seg_len, &n);
   return ws_bytes(batch, d_inner, d_state, n);
+}
+
+ss_status ss_scan_fwd_states(const void* u, const void* delta, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* delta_bias, int delta_softplus, const float* h0,
+                             float* h_last, void* out, float* states, int64_t batch,
+                             int64_t seqlen, int64_t d_inner, int64_t d_state, ss_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!states && batch > 0 && seqlen > 0 && d_inner > 0)
+    return fail(SS_ERR_INVALID_ARG, "states is NULL");
+  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, 0, false, 0,
+                   stream, nullptr, nullptr, nullptr, 0, states);
+}
+
+size_t ss_scan_fwd_states_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                int64_t d_state) {
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
+  int64_t n;
+  if (!mul_ok(batch * d_inner, (seqlen + ss::kChunk - 1) / ss::kChunk, &n) ||
+      !mul_ok(n, d_state * 4, &n))
+    return 0;
+  return static_cast<size_t>(n);
 }
 
 ss_status ss_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias,

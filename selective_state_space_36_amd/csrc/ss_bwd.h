@@ -38,6 +38,7 @@ struct BwdArgs {
   int32_t d_state;
   int32_t softplus;
   int32_t vec_io;        // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, dout
+  int32_t states_given;  // ck already holds the chunk-end states: skip the forward pass
 };
 
 // Zero the accumulated outputs, then run the backward (one workgroup per 16 channels of a batch

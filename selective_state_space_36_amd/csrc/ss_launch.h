@@ -42,6 +42,9 @@ struct ScanArgs {
   const float* conv_b;  // (d_inner), nullptr: 0
   const void* x_prev;   // (batch, conv_k - 1, d_inner) io dtype: x before t = 0; nullptr: 0
   int32_t conv_k;       // 1..4
+  // chunk-end states (ss_scan_fwd_states): (batch, d_inner, states_chunks, d_state); nullptr: none
+  float* states;
+  int64_t states_chunks;  // ceil(seqlen / kChunk)
 };
 
 struct DecodeArgs {

@@ -154,16 +154,23 @@ struct BwdKernel {
     const int own_col = ((cl / PIECE_E) ^ pswz(k)) * PIECE_E + cl % PIECE_E;
     auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][own_col]); };
 
-    // ---- pass 1: forward, storing each chunk's end state
+    // ---- pass 1: forward, storing each chunk's end state (skipped when the caller's forward
+    // saved them: then only the last chunk is staged for pass 2)
     float h = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
     float* ck_row = a.ck + (row * nchunks) * N;
     int buf = 0;
-    if (nchunks > 0) {
+    if (a.states_given) {
+      if (nchunks > 0) {
+        issue(nchunks - 1, true);
+        stage(0, true);
+        __syncthreads();
+      }
+    } else if (nchunks > 0) {
       issue(0, false);
       stage(0, false);
       __syncthreads();
     }
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = 0; c < (a.states_given ? 0 : nchunks); ++c) {
       // next: chunk c + 1 of this pass, or the last chunk for pass 2
       const bool next_full = c + 1 == nchunks;
       issue(next_full ? nchunks - 1 : c + 1, next_full);

@@ -115,6 +115,11 @@ struct ScanKernel {
     }
     const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
     const float dskip = (!SUMMARY && chan_ok && a.D) ? a.D[d] : 0.0f;
+    // saved chunk-end states: this lane's state n = k of row (b, d), from the segment's first
+    // chunk on (the output pass carries the true state across segments)
+    float* st_lane = (!SUMMARY && a.states && chan_ok)
+                         ? a.states + (row * a.states_chunks + t_begin / kT) * a.d_state + k
+                         : nullptr;
 
     // Front end (CONV): tap weights of a 4-wide window ending at this lane's step, split by
     // whether the tap's step lies in this chunk (cw_cur) or the previous one (cw_prev), and the
@@ -307,6 +312,12 @@ struct ScanKernel {
       if (SUMMARY) dt_acc += dt;
 
       chunk_steps(sm, buf, dt, du, A2, h, wave, r, k);
+      if (!SUMMARY && a.states && st_lane) {
+        float* p = st_lane + int64_t(ci) * a.d_state;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          if (k + 16 * j < a.d_state) p[16 * j] = h[j];
+      }
 
       if (!SUMMARY) {
         wave_lds_sync();

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libssscan.so")
 SS_OK, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_ERR_HIP = 0, 1, 2, 3
 SS_F32, SS_BF16 = 0, 1
 SS_FLAG_ZOH_EXACT = 1
+SS_FLAG_STATES_GIVEN = 2
 
 # Every symbol declared in include/ss_scan.h, with its ctypes signature.
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -29,6 +30,9 @@ SIGNATURES = {
     "ss_scan_fwd_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
                               _vp, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32, _u32, _vp]),
     "ss_scan_fwd_ex_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
+    "ss_scan_fwd_states": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                  _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "ss_scan_fwd_states_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "ss_scan_fwd_conv": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp,
                                 _sz, _i32, _u32, _vp]),
@@ -209,12 +213,55 @@ def scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, del
     return (out, h_last) if return_last_state else out
 
 
+def scan_fwd_states(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                    h0=None, return_last_state=False, out=None, h_last=None, states=None,
+                    workspace=None, stream=None):
+    """Prefill that also saves the state after every 16-step chunk (ss_scan_fwd_states), for
+    scan_bwd(..., states=...).  Arguments as for scan_fwd; states: (batch, d_inner,
+    ceil(L / 16), d_state) float32 or None (allocated here).  Returns (out, states), or
+    (out, states, h_last) with return_last_state."""
+    batch, L, d_inner = u.shape
+    d_state = B.shape[-1]
+    code = _dtype_code(u)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        _dev(t, name, u.dtype, (batch, L, d_inner))
+    for name, t in (("B", B), ("C", C)):
+        _dev(t, name, u.dtype, (batch, L, d_state))
+    _dev(A, "A", torch.float32, (d_inner, d_state))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(delta_bias, "delta_bias", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, d_state))
+    if out is None:
+        out = torch.empty_like(u)
+    _dev(out, "out", u.dtype, (batch, L, d_inner))
+    if return_last_state and h_last is None:
+        h_last = torch.empty((batch, d_inner, d_state), dtype=torch.float32, device=u.device)
+    _dev(h_last, "h_last", torch.float32, (batch, d_inner, d_state))
+    nct = (L + 15) // 16
+    if states is None:
+        states = torch.empty((batch, d_inner, nct, d_state), dtype=torch.float32,
+                             device=u.device)
+    _dev(states, "states", torch.float32, (batch, d_inner, nct, d_state))
+    if workspace is None:
+        nbytes = workspace_bytes(batch, L, d_inner, d_state, u.dtype, None)
+        workspace = (torch.empty(nbytes, dtype=torch.uint8, device=u.device) if nbytes
+                     else None)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ss_scan_fwd_states(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        1 if delta_softplus else 0, _ptr(h0), _ptr(h_last), _ptr(out), _ptr(states), batch, L,
+        d_inner, d_state, code, _ptr(workspace), ws_len, _stream(stream)))
+    return (out, states, h_last) if return_last_state else (out, states)
+
+
 def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
              h0=None, dh_last=None, want_dD=True, want_ddelta_bias=True, want_dh0=True,
-             workspace=None, stream=None):
+             workspace=None, states=None, stream=None):
     """Gradients of scan_fwd (ss_scan_bwd) for the upstream gradient dout (same dtype and shape
     as out) and optionally dh_last.  Returns a dict: du, ddelta, dz (io dtype; dz None without
-    z), dA, dB, dC (float32), dD, ddelta_bias, dh0 (float32, None when not wanted)."""
+    z), dA, dB, dC (float32), dD, ddelta_bias, dh0 (float32, None when not wanted).
+    states: the chunk-end states scan_fwd_states saved for these inputs (then the backward skips
+    its own forward pass: SS_FLAG_STATES_GIVEN); workspace is ignored then."""
     batch, L, d_inner = u.shape
     d_state = B.shape[-1]
     code = _dtype_code(u)
@@ -235,7 +282,11 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
              dD=torch.empty((d_inner,), **f32) if want_dD else None,
              ddelta_bias=torch.empty((d_inner,), **f32) if want_ddelta_bias else None,
              dh0=torch.empty((batch, d_inner, d_state), **f32) if want_dh0 else None)
-    if workspace is None:
+    flags = 0
+    if states is not None:
+        _dev(states, "states", torch.float32, (batch, d_inner, (L + 15) // 16, d_state))
+        workspace, flags = states, SS_FLAG_STATES_GIVEN
+    elif workspace is None:
         nbytes = int(lib().ss_scan_bwd_workspace_bytes(batch, L, d_inner, d_state, code))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=u.device) if nbytes else None
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -244,7 +295,7 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
         1 if delta_softplus else 0, _ptr(h0), _ptr(dout), _ptr(dh_last), _ptr(g["du"]),
         _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
         _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, L, d_inner, d_state, code,
-        _ptr(workspace), ws_len, 0, _stream(stream)))
+        _ptr(workspace), ws_len, flags, _stream(stream)))
     return g
 
 

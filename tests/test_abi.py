@@ -146,3 +146,34 @@ def test_backward_argument_errors_before_launch(lib):
     assert need == 1 * 16 * 1 * 16 * 4
     assert _bwd(lib, wsb=need - 4) == ops.SS_ERR_INVALID_ARG
     assert lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 17, ops.SS_BF16) == 0
+
+
+def _fwd_states(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None,
+             bias=None, sp=1, h0=None, hl=None, out=FAKE * 6, states=FAKE * 7, batch=1, L=33,
+             d=16, N=16, dtype=ops.SS_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.ss_scan_fwd_states(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                  a["bias"], a["sp"], a["h0"], a["hl"], a["out"], a["states"],
+                                  a["batch"], a["L"], a["d"], a["N"], a["dtype"], a["ws"],
+                                  a["wsb"], None)
+
+
+def test_saved_states_argument_errors_before_launch(lib):
+    assert lib.ss_scan_fwd_states_bytes(1, 33, 16, 16) == 16 * 3 * 16 * 4
+    assert lib.ss_scan_fwd_states_bytes(2, 16, 8, 40) == 2 * 8 * 1 * 40 * 4
+    assert lib.ss_scan_fwd_states_bytes(1, 0, 16, 16) == 0
+    assert _fwd_states(lib, states=None) == ops.SS_ERR_INVALID_ARG
+    assert b"states" in lib.ss_last_error()
+    assert _fwd_states(lib, states=FAKE * 6 + 64) == ops.SS_ERR_INVALID_ARG  # inside out
+    assert b"states overlaps" in lib.ss_last_error()
+    assert _fwd_states(lib, states=FAKE * 7 + 2) == ops.SS_ERR_UNSUPPORTED   # misaligned
+    assert _fwd_states(lib, N=65) == ops.SS_ERR_UNSUPPORTED
+    assert _fwd_states(lib, L=0, states=None) == ops.SS_OK                   # empty: no-op
+    # the forward does not take the backward's flag; the backward takes it and still checks
+    rc = lib.ss_scan_fwd_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, None, None, None, 1,
+                            None, None, FAKE * 6, 1, 16, 8, 16, ops.SS_BF16, None, 0, 0,
+                            ops.SS_FLAG_STATES_GIVEN, None)
+    assert rc == ops.SS_ERR_UNSUPPORTED and b"flag" in lib.ss_last_error()
+    assert _bwd(lib, flags=ops.SS_FLAG_STATES_GIVEN, dout=None) == ops.SS_ERR_INVALID_ARG
+    assert _bwd(lib, flags=ops.SS_FLAG_STATES_GIVEN, ws=None, wsb=0) == ops.SS_ERR_INVALID_ARG
