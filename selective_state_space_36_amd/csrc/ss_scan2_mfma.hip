@@ -17,9 +17,9 @@
 // the state in registers; wave w owns head channels 16w..16w+15 (one 16-column tile of S, X and
 // Y), so the state never leaves the wave.  The 10 causal 16x16 tiles of C B^T are shared: each
 // wave computes some of them, applies the mask and decays, and writes the split products to LDS.
-// Per chunk the workgroup stages B (row-major and transposed), C, x and z (transposed) in LDS
-// from 16-byte / 8-byte global loads issued one chunk ahead, and writes its outputs through a
-// per-wave LDS tile as 16-byte stores.
+// Per chunk the workgroup stages B (row-major and transposed), C and x (transposed) in LDS from
+// 16-byte / 8-byte global loads issued one chunk ahead; each wave transposes its own z tile into
+// LDS once the B tile is free, and writes its outputs through an LDS tile as 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -240,7 +240,7 @@ scan2_mfma_kernel(Scan2Args a) {
     __syncthreads();  // the previous chunk's LDS reads are done
     // ---- stage the chunk in LDS
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {  // x, z transposed: (p, 4 consecutive steps) per write
+    for (int cc = 0; cc < 4; ++cc) {  // x transposed: (p, 4 consecutive steps) per write
       const int w = cc >> 1;
       uint32_t r4[4];
 #pragma unroll

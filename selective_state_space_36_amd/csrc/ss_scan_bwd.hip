@@ -15,15 +15,17 @@
 // and the element work of step k of each 16-step chunk; 16 channels per 256-thread workgroup,
 // one workgroup per (16 channels, batch row); the next chunk's global loads are in flight while a
 // chunk is computed (LDS tiles double-buffered).  Pass 1 runs the forward over the sequence and
-// stores each chunk's end state (workspace, a few hundred bytes per channel and chunk).  Pass 2
+// stores each chunk's end state (workspace, 4 d_state bytes per channel and chunk); when the
+// caller's forward already saved them (ss_scan_fwd_states), pass 1 is skipped.  Pass 2
 // walks the chunks backwards: it recomputes the chunk's 16 states and decays from the stored
 // state into registers, computes y for the gate's derivative, then runs the adjoint backwards
 // through the 16 steps.  Sums over a channel's states go through per-wave LDS tiles (summed by
 // the owner lane of the step, as in the forward); sums over channels (dB, dC) are reduced over
-// row pairs by a row swap and over the eight pairs in LDS, then added to global memory with one
-// atomic per (step, state) and workgroup; dA, dD and dbias likewise once per
-// workgroup.  The atomic sums make dA, dB, dC, dD and dbias reproducible only up to rounding
-// order.
+// row pairs by a row swap (dB and dC in one swap) and over the eight pairs in LDS, then added to
+// global memory with one atomic per (step, state) and workgroup; dA, dD and dbias likewise once
+// per workgroup.  The atomic sums make dA, dB, dC, dD and dbias reproducible only up to rounding
+// order.  u/delta/z/dout tiles move as 16-byte pieces when the channel blocks are whole, with
+// the pieces of each tile row permuted by step against LDS bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
