@@ -241,4 +241,22 @@ def test_full_size_workload_sampled(index):
     r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
                             delta_bias=p["delta_bias"], rows=rows)
     check_close(g, r, TOL["bf16"], f"{w.name} out")
-    check_close(gh, rh, TOL["bf16"], f"{w.name} h_last")
+    # the state is float32 from exact bf16 inputs: the 130M and 2.8B layers meet the float32
+    # bound; the 1M-step layer carries its state through 2^20 steps and is held to the bf16 one
+    h_tol = TOL["f32"] if index < 3 else TOL["bf16"]
+    check_close(gh, rh, h_tol, f"{w.name} h_last")
+
+    # the scan isolated (no skip term, no gate): out is C.h alone, which D.u would otherwise
+    # dominate
+    print(f"  running {w.name} without D and z ...", flush=True)
+    out, h_last = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]),
+                                 dev(p["C"]), delta_bias=dev(p["delta_bias"]),
+                                 return_last_state=True)
+    torch.cuda.synchronize()
+    g = host(out[torch.from_numpy(b_idx).cuda(), :, torch.from_numpy(d_idx).cuda()])
+    gh = host(h_last.reshape(-1, w.d_state)[torch.from_numpy(rows).cuda()])
+    del out, h_last
+    r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
+                            delta_bias=p["delta_bias"], rows=rows)
+    check_close(g, r, TOL["bf16"], f"{w.name} out (scan isolated)")
+    check_close(gh, rh, h_tol, f"{w.name} h_last (scan isolated)")
