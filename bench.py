@@ -594,6 +594,15 @@ def main():
                      "kernel_us": round(ms_kernel * 1e3, 2)},
         "hbm": {"algorithmic_bytes": nbytes, "achieved_GBps": round(hbm_gbps, 1),
                 "peak_GBps": PEAK_HBM_GBPS, "frac": round(hbm_gbps / PEAK_HBM_GBPS, 4)},
+        # transcendentals: one v_exp_f32 per update, and per element 2 for softplus (exp, log)
+        # and 2 for silu (exp, rcp); v_exp_f32 issues at half the VALU rate
+        "exp": {"per_update": 1,
+                "per_element": w.d_state + (4 if w.gate else 2),
+                "exp_per_s": round(elems * (w.d_state + (2 if w.gate else 1))
+                                   / (ms_kernel * 1e-3), 1),
+                "exp_peak_per_s": PEAK_VALU_SLOTS / 2,
+                "exp_frac": round(elems * (w.d_state + (2 if w.gate else 1))
+                                  / (ms_kernel * 1e-3) / (PEAK_VALU_SLOTS / 2), 4)},
         "zoh_exact": {"kernel_us": round(ms_zoh * 1e3, 2),
                       "elements_per_s": round(elems / (ms_zoh * 1e-3), 1),
                       "note": "same layer with the exact zero-order-hold input term; its extra "
