@@ -239,8 +239,13 @@ struct BwdKernel {
       // the adjoint backwards through the chunk
       float* qw = &sm.q[wave][r * kPRow + k];
       float* gbc_w = &sm.gbc[(r & 1) * kGcOff + (2 * wave + (r >> 1)) * kT * 16];
+      float xb[kT], yc[kT];
       rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
-                lam, e_next, ga, pw, qw, gbc_w, k);
+                lam, e_next, ga, pw, qw, xb, yc);
+      // dB and dC of each step, summed over channel pairs (independent of one another, so the
+      // row swaps of different steps overlap)
+#pragma unroll
+      for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = sum_row_pairs2(xb[t], yc[t]);
       wave_lds_sync();
       float gdt = 0.0f, gx = 0.0f;
       {
@@ -337,13 +342,14 @@ struct BwdKernel {
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
   // contributions.  Partial sums over states go to the wave tiles pw (the A e h_prev part of ddt)
   // and qw (lam B, which gives du and the u B part of ddt); dB and dC are summed over each pair of
-  // the wave's channels (rows) together, rows 0 and 2 storing dB and rows 1 and 3 dC (gw).
+  // the wave's channels (rows) after the chain (xb, yc), rows 0 and 2 storing dB and rows 1
+  // and 3 dC.
   template <int TAU>
   static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float xu, float gy, float a_n, float hprev,
                                                   const float (&hh)[kT], const float (&ee)[kT],
                                                   float& lam, float& e_next, float& ga, float* pw,
-                                                  float* qw, float* gw, int k) {
+                                                  float* qw, float (&xb)[kT], float (&yc)[kT]) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
@@ -355,7 +361,8 @@ struct BwdKernel {
     const float qq = lam * bb;
     pw[TAU * kPTau] = a_n * rr;
     qw[TAU * kPTau] = qq;
-    gw[TAU * 16 + k] = sum_row_pairs2(lam * row_bcast<TAU>(du), gyb * hh[TAU]);
+    xb[TAU] = lam * row_bcast<TAU>(du);  // this channel's dB and dC terms, summed over
+    yc[TAU] = gyb * hh[TAU];             // channel pairs after the chain
     e_next = ee[TAU];
   }
   template <int... TAUS>
@@ -365,10 +372,10 @@ struct BwdKernel {
                                                    float hprev, const float (&hh)[kT],
                                                    const float (&ee)[kT], float& lam,
                                                    float& e_next, float& ga, float* pw, float* qw,
-                                                   float* gw, int k) {
+                                                   float (&xb)[kT], float (&yc)[kT]) {
     // fold over the steps in decreasing order
     (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, hprev, hh, ee, lam, e_next, ga, pw, qw,
-                             gw, k),
+                             xb, yc),
      ...);
   }
 };
