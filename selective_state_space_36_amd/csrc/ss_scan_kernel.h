@@ -52,8 +52,16 @@ namespace {
 constexpr int kWaves = kPrefillThreads / 64;
 constexpr int kT = kChunk;               // steps per chunk (= lanes per row)
 constexpr int kTileStride = kT + 2;      // float2 slots per state row of the B/C tile (padding)
-constexpr int kPRow = 336;               // floats per channel row of the partial tile (padding)
-constexpr int kPTau = 20;                // floats per step of the partial tile (padding)
+// Per-wave tile of the values the lanes hand to the owner lanes: channel row r at r * kPRow,
+// step slot s at s * kPTau, lane k at k; odd rows keep step t in slot t ^ kPSwap.  Chosen by
+// measurement on gfx950 (LDS bank-conflict counter over the tile's own access patterns): with
+// this layout both the owners' 16-byte reads and the paired 4-byte writes of two steps are
+// conflict-free, while rows 336 floats apart (no swap) conflict on the reads and rows 320 apart
+// conflict on the writes (swap 0 or 4) or on the reads (swap 4).
+constexpr int kPRow = 320;               // floats per channel row of the partial tile
+constexpr int kPSwap = 12;               // odd rows: step t in slot t ^ kPSwap
+constexpr int kPTau = 20;                // floats per step slot of the partial tile (padding)
+constexpr int kSRow = 20;                // floats per row of the split B and C tiles (padding)
 static_assert(kT == 16, "one chunk step per row lane");
 
 template <class IO, int NL, bool GATE, bool SUMMARY, bool VEC, bool ZOH, bool CONV>
@@ -66,6 +74,11 @@ struct ScanKernel {
   static_assert(kT * PIECES <= 64, "one 16-byte piece of a tile per lane of a wave");
   static_assert(NTEN < kWaves, "a wave left over for the output tile");
   static constexpr int BC_PER_THREAD = kT * NP / kPrefillThreads;
+  // d_state <= 16 (one state per lane): the lanes hand their states h_t[n] to the owner lane of
+  // step t, which forms C_t . h_t with 16 FMAs, instead of each lane multiplying by C_t[n] and
+  // the owner adding 16 products (31 instructions per chunk -> 17).  Wider states keep the
+  // per-lane partial sums: their states would not fit the per-wave tile.
+  static constexpr bool FOLD = NL == 1 && !SUMMARY;
   // The 16-byte pieces of row (step) k of a u/delta/z/out tile are stored XOR-permuted by
   // (k / (8 / PIECES)) mod PIECES.  The owner lanes of steps 4 (bf16) or 2 (fp32) apart read the
   // same column of rows that share LDS banks (rows are 32 or 64 bytes; LDS has 32 banks of 4
@@ -74,11 +87,18 @@ struct ScanKernel {
     return (row / (8 / PIECES)) & (PIECES - 1);
   }
 
-  struct alignas(16) Smem {
+  struct PairTile {
     float2 bc[2][NP][kTileStride];  // (B_t[n], C_t[n]) per chunk
+  };
+  struct SplitTile {
+    float b[2][kT][kSRow];  // B_t[n] per chunk, row n (read by the lane of state n)
+    float c[2][kT][kSRow];  // C_t[n] per chunk, row t (read by the owner lane of step t)
+  };
+  struct alignas(16) Smem {
+    std::conditional_t<FOLD, SplitTile, PairTile> bt;
     uint4 in[2][NTEN][kT][PIECES];  // raw u, delta, z tiles per chunk
     uint4 out[2][kT][PIECES];       // raw output tile per chunk
-    float p[kWaves][4 * kPRow];     // per-wave partial sums [row][step][lane]
+    float p[kWaves][4 * kPRow];     // per-wave partial sums or states [row][step][lane]
   };
 
   static __device__ __forceinline__ void run(const ScanArgs& a) {
@@ -241,8 +261,15 @@ struct ScanKernel {
     };
     auto stage_chunk = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < BC_PER_THREAD; ++i)
-        sm.bc[buf][bc_n[i]][bc_tau[i]] = make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
+      for (int i = 0; i < BC_PER_THREAD; ++i) {
+        if constexpr (FOLD) {
+          sm.bt.b[buf][bc_n[i]][bc_tau[i]] = IO::widen(pre.rb[i]);
+          sm.bt.c[buf][bc_tau[i]][bc_n[i]] = IO::widen(pre.rc[i]);
+        } else {
+          sm.bt.bc[buf][bc_n[i]][bc_tau[i]] =
+              make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
+        }
+      }
       if (wave_u < NTEN && tl_on) sm.in[buf][wave_u][tl_row][tl_pc ^ pswz(tl_row)] = pre.rin;
     };
     // The data registers of the last output store are kept live (hold_store) until the next
@@ -321,14 +348,42 @@ struct ScanKernel {
 
       if (!SUMMARY) {
         wave_lds_sync();
-        const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
+        const float* pr = &sm.p[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
         const float4 q0 = *reinterpret_cast<const float4*>(pr + 0);
         const float4 q1 = *reinterpret_cast<const float4*>(pr + 4);
         const float4 q2 = *reinterpret_cast<const float4*>(pr + 8);
         const float4 q3 = *reinterpret_cast<const float4*>(pr + 12);
-        wave_lds_sync();
-        float y = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w))) +
-                  (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
+        float y;
+        if constexpr (FOLD) {
+          // q holds h_t[0..15] of this lane's step t = k; C_t is row k of the C tile (the four
+          // channels of the wave read the same row)
+          const float* cr = &sm.bt.c[buf][k][0];
+          const float4 c0 = *reinterpret_cast<const float4*>(cr + 0);
+          const float4 c1 = *reinterpret_cast<const float4*>(cr + 4);
+          const float4 c2 = *reinterpret_cast<const float4*>(cr + 8);
+          const float4 c3 = *reinterpret_cast<const float4*>(cr + 12);
+          wave_lds_sync();
+          float y0 = c0.x * q0.x, y1 = c2.x * q2.x;
+          y0 = fmaf(c0.y, q0.y, y0);
+          y1 = fmaf(c2.y, q2.y, y1);
+          y0 = fmaf(c0.z, q0.z, y0);
+          y1 = fmaf(c2.z, q2.z, y1);
+          y0 = fmaf(c0.w, q0.w, y0);
+          y1 = fmaf(c2.w, q2.w, y1);
+          y0 = fmaf(c1.x, q1.x, y0);
+          y1 = fmaf(c3.x, q3.x, y1);
+          y0 = fmaf(c1.y, q1.y, y0);
+          y1 = fmaf(c3.y, q3.y, y1);
+          y0 = fmaf(c1.z, q1.z, y0);
+          y1 = fmaf(c3.z, q3.z, y1);
+          y0 = fmaf(c1.w, q1.w, y0);
+          y1 = fmaf(c3.w, q3.w, y1);
+          y = y0 + y1;
+        } else {
+          wave_lds_sync();
+          y = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w))) +
+              (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
+        }
         y = fmaf(dskip, xu, y);
         if (GATE) y *= silu_f(own_in(buf, 2));
         reinterpret_cast<elem*>(&sm.out[buf][k][0])[own_col] = IO::from_float(y);
@@ -391,7 +446,8 @@ struct ScanKernel {
   }
 
   // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
-  // (B, C) pairs for this lane's states, two steps per float4.
+  // (B, C) pairs for this lane's states, two steps per float4 (with FOLD: B only, four steps per
+  // float4, and the lane stores its new state instead of C_t[n] h_t[n]).
   template <int TAU>
   static __device__ __forceinline__ void step(Smem& sm, const float4 (&bcv)[NL][kT / 2],
                                               float dt, float du, const float (&A2)[NL],
@@ -401,16 +457,29 @@ struct ScanKernel {
     float p = 0.0f;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const float4 v = bcv[j][TAU / 2];
-      const float bb = (TAU & 1) ? v.z : v.x;
-      const float cc = (TAU & 1) ? v.w : v.y;
+      float bb, cc = 0.0f;
+      if constexpr (FOLD) {
+        const float4 v = bcv[j][TAU / 4];
+        bb = (TAU & 3) == 0 ? v.x : ((TAU & 3) == 1 ? v.y : ((TAU & 3) == 2 ? v.z : v.w));
+      } else {
+        const float4 v = bcv[j][TAU / 2];
+        bb = (TAU & 1) ? v.z : v.x;
+        cc = (TAU & 1) ? v.w : v.y;
+      }
       const float y = dtb * A2[j];
       const float e = exp2_hw(y);
       const float inc = ZOH ? (dub * bb) * zoh_gain(e, y) : dub * bb;
       h[j] = fmaf(e, h[j], inc);
-      p = (j == 0) ? cc * h[j] : fmaf(cc, h[j], p);
+      if constexpr (FOLD)
+        p = h[j];
+      else if constexpr (!SUMMARY)
+        p = (j == 0) ? cc * h[j] : fmaf(cc, h[j], p);
     }
-    if (!SUMMARY) sm.p[wave][r * kPRow + TAU * kPTau + k] = p;
+    if (!SUMMARY) {
+      // slot TAU ^ kPSwap on odd rows
+      const int flip = ((TAU ^ kPSwap) - TAU) * (r & 1) * kPTau;
+      sm.p[wave][r * kPRow + k + flip + TAU * kPTau] = p;
+    }
   }
 
   template <int... TAUS>
@@ -428,10 +497,17 @@ struct ScanKernel {
                                                      int wave, int r, int k) {
     float4 bcv[NL][kT / 2];
 #pragma unroll
-    for (int j = 0; j < NL; ++j)
+    for (int j = 0; j < NL; ++j) {
+      if constexpr (FOLD) {
 #pragma unroll
-      for (int i = 0; i < kT / 2; ++i)
-        bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k + 16 * j][2 * i]);
+        for (int i = 0; i < kT / 4; ++i)
+          bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bt.b[buf][k][4 * i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kT / 2; ++i)
+          bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bt.bc[buf][k + 16 * j][2 * i]);
+      }
+    }
     steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, h, wave, r, k);
   }
 };
