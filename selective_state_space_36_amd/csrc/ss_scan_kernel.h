@@ -317,8 +317,22 @@ struct ScanKernel {
       const bool has_next = ci + 1 < nchunks;
       if (has_next) load_chunk(ci + 1);
 
-      const bool own_ok = chan_ok && k < nvalid_of(ci);
+      // Every LDS read of the chunk is issued here, in the order the results are needed (LDS
+      // returns them in order): this lane's u and delta for the element work, the B column of its
+      // states for the steps, z for the gate, the C row of its step for the output sum.
       float xu = own_in(buf, 0);
+      const float sraw = own_in(buf, 1);
+      float4 bcv[NL][kT / 2];
+      read_b(sm, buf, k, bcv);
+      const float zraw = (GATE && !SUMMARY) ? own_in(buf, 2) : 0.0f;
+      float4 cv[4];
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cv[i] = *reinterpret_cast<const float4*>(&sm.bt.c[buf][k][4 * i]);
+      }
+
+      const bool own_ok = chan_ok && k < nvalid_of(ci);
       if (CONV) {  // xu holds x_t here; u_t = silu(conv)
         const float xc = xu;
         float acc = fmaf(cw_own, xc, cbias);
@@ -331,14 +345,15 @@ struct ScanKernel {
         xprev = xc;
         xu = silu_f(acc);
       }
-      const float sv = own_in(buf, 1) + bias;
-      float dt = a.softplus ? softplus_f(sv) : sv;
+      const float sv = sraw + bias;
+      const float sp = softplus_f(sv);  // computed either way: a select, not a branch
+      float dt = a.softplus ? sp : sv;
       dt = own_ok ? dt : 0.0f;  // steps past the end leave h unchanged
       // exact hold: the input term is (dt u / ln 2) B_t[n] (2^y - 1) / y with y = dt A[n] log2(e)
       const float du = own_ok ? (ZOH ? dt * xu * (1.0f / kLn2) : dt * xu) : 0.0f;
       if (SUMMARY) dt_acc += dt;
 
-      chunk_steps(sm, buf, dt, du, A2, h, wave, r, k);
+      steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, h, wave, r, k);
       if (!SUMMARY && a.states && st_lane) {
         float* p = st_lane + int64_t(ci) * a.d_state;
 #pragma unroll
@@ -355,13 +370,9 @@ struct ScanKernel {
         const float4 q3 = *reinterpret_cast<const float4*>(pr + 12);
         float y;
         if constexpr (FOLD) {
-          // q holds h_t[0..15] of this lane's step t = k; C_t is row k of the C tile (the four
+          // q holds h_t[0..15] of this lane's step t = k; cv is C_t (row k of the C tile; the four
           // channels of the wave read the same row)
-          const float* cr = &sm.bt.c[buf][k][0];
-          const float4 c0 = *reinterpret_cast<const float4*>(cr + 0);
-          const float4 c1 = *reinterpret_cast<const float4*>(cr + 4);
-          const float4 c2 = *reinterpret_cast<const float4*>(cr + 8);
-          const float4 c3 = *reinterpret_cast<const float4*>(cr + 12);
+          const float4 c0 = cv[0], c1 = cv[1], c2 = cv[2], c3 = cv[3];
           wave_lds_sync();
           float y0 = c0.x * q0.x, y1 = c2.x * q2.x;
           y0 = fmaf(c0.y, q0.y, y0);
@@ -385,7 +396,7 @@ struct ScanKernel {
               (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
         }
         y = fmaf(dskip, xu, y);
-        if (GATE) y *= silu_f(own_in(buf, 2));
+        if (GATE) y *= silu_f(zraw);
         reinterpret_cast<elem*>(&sm.out[buf][k][0])[own_col] = IO::from_float(y);
       }
       hold_store();
@@ -490,12 +501,10 @@ struct ScanKernel {
     (step<TAUS>(sm, bcv, dt, du, A2, h, wave, r, k), ...);
   }
 
-  // The 16 recurrence steps of one chunk.  The B/C tile reads are issued together up front
-  // (16-byte reads, two steps each) so that the steps themselves are pure VALU work.
-  static __device__ __forceinline__ void chunk_steps(Smem& sm, int buf, float dt, float du,
-                                                     const float (&A2)[NL], float (&h)[NL],
-                                                     int wave, int r, int k) {
-    float4 bcv[NL][kT / 2];
+  // The B (with FOLD) or (B, C) tile entries of this lane's states for the 16 steps of a chunk,
+  // read as 16-byte pieces so that the steps themselves are pure VALU work.
+  static __device__ __forceinline__ void read_b(const Smem& sm, int buf, int k,
+                                                float4 (&bcv)[NL][kT / 2]) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       if constexpr (FOLD) {
@@ -508,7 +517,6 @@ struct ScanKernel {
           bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bt.bc[buf][k + 16 * j][2 * i]);
       }
     }
-    steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, h, wave, r, k);
   }
 };
 
