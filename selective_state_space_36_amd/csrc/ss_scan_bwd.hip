@@ -47,8 +47,19 @@ __device__ __forceinline__ float sum_row_pairs2(float x, float y) {
                                                   false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
-constexpr int kPRow = 336;  // floats per channel row of a partial tile (padding)
-constexpr int kPTau = 20;   // floats per step of a partial tile (padding)
+// Partial tiles: channel row r at r * kPRow, step slot s at s * kPTau, lane k at k; odd rows keep
+// step t in slot t ^ kPSwap.  With this layout the owners' 16-byte reads and the paired 4-byte
+// writes of two steps are both free of LDS bank conflicts on gfx950 (measured with the
+// bank-conflict counter; rows 336 floats apart conflict on the reads, rows 320 apart without the
+// swap on the writes).
+constexpr int kPRow = 320;  // floats per channel row of a partial tile
+constexpr int kPTau = 20;   // floats per step slot of a partial tile (padding)
+constexpr int kPSwap = 12;  // odd rows: step t in slot t ^ kPSwap
+// Offset of step TAU's slot from slot TAU, for a row of parity ODD.
+template <int TAU>
+__device__ __forceinline__ int pslot_shift(int odd) {
+  return ((TAU ^ kPSwap) - TAU) * kPTau * odd;
+}
 // dB and dC partial tiles: 8 row pairs x kBwdChunk steps x 16 states each; the dC half starts 16
 // floats after the dB half so that rows 0 and 1 of a wave, which write the two halves with one
 // instruction, use different LDS banks.
@@ -216,11 +227,11 @@ struct BwdKernel {
       // recompute the chunk: states, decays and the partial sums C.h of y
       float hh[kT], ee[kT];
       float* pw = &sm.p[wave][r * kPRow + k];
-      rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, hprev, hh, ee, pw);
+      rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, hprev, hh, ee, pw, r & 1);
       wave_lds_sync();
       float y = 0.0f;
       {
-        const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
+        const float* pr = &sm.p[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
 #pragma unroll
         for (int i = 0; i < 16; ++i) y += pr[i];
       }
@@ -241,7 +252,7 @@ struct BwdKernel {
       float* gbc_w = &sm.gbc[(r & 1) * kGcOff + (2 * wave + (r >> 1)) * kT * 16];
       float xb[kT], yc[kT];
       rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
-                lam, e_next, ga, pw, qw, xb, yc);
+                lam, e_next, ga, pw, qw, xb, yc, r & 1);
       // dB and dC of each step, summed over channel pairs (independent of one another, so the
       // row swaps of different steps overlap)
 #pragma unroll
@@ -249,8 +260,8 @@ struct BwdKernel {
       wave_lds_sync();
       float gdt = 0.0f, gx = 0.0f;
       {
-        const float* pr = &sm.p[wave][r * kPRow + k * kPTau];
-        const float* qr = &sm.q[wave][r * kPRow + k * kPTau];
+        const float* pr = &sm.p[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
+        const float* qr = &sm.q[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           gdt += pr[i];
@@ -320,7 +331,7 @@ struct BwdKernel {
   template <int TAU>
   static __device__ __forceinline__ void rec_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float A2, float& h, float (&hh)[kT],
-                                                  float (&ee)[kT], float* pw) {
+                                                  float (&ee)[kT], float* pw, int odd) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
@@ -328,15 +339,16 @@ struct BwdKernel {
     h = fmaf(e, h, row_bcast<TAU>(du) * bb);
     hh[TAU] = h;
     ee[TAU] = e;
-    pw[TAU * kPTau] = cc * h;
+    pw[TAU * kPTau + pslot_shift<TAU>(odd)] = cc * h;
   }
   template <int... TAUS>
   static __device__ __forceinline__ void rec_steps(std::integer_sequence<int, TAUS...>,
                                                    const float4 (&bcv)[kT / 2], float dt,
                                                    float du, float A2, float hprev,
-                                                   float (&hh)[kT], float (&ee)[kT], float* pw) {
+                                                   float (&hh)[kT], float (&ee)[kT], float* pw,
+                                                   int odd) {
     float h = hprev;
-    (rec_step<TAUS>(bcv, dt, du, A2, h, hh, ee, pw), ...);
+    (rec_step<TAUS>(bcv, dt, du, A2, h, hh, ee, pw, odd), ...);
   }
 
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
@@ -349,7 +361,8 @@ struct BwdKernel {
                                                   float xu, float gy, float a_n, float hprev,
                                                   const float (&hh)[kT], const float (&ee)[kT],
                                                   float& lam, float& e_next, float& ga, float* pw,
-                                                  float* qw, float (&xb)[kT], float (&yc)[kT]) {
+                                                  float* qw, float (&xb)[kT], float (&yc)[kT],
+                                                  int odd) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
@@ -359,8 +372,8 @@ struct BwdKernel {
     const float rr = lam * ee[TAU] * hp;
     ga = fmaf(row_bcast<TAU>(dt), rr, ga);
     const float qq = lam * bb;
-    pw[TAU * kPTau] = a_n * rr;
-    qw[TAU * kPTau] = qq;
+    pw[TAU * kPTau + pslot_shift<TAU>(odd)] = a_n * rr;
+    qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qq;
     xb[TAU] = lam * row_bcast<TAU>(du);  // this channel's dB and dC terms, summed over
     yc[TAU] = gyb * hh[TAU];             // channel pairs after the chain
     e_next = ee[TAU];
@@ -372,10 +385,10 @@ struct BwdKernel {
                                                    float hprev, const float (&hh)[kT],
                                                    const float (&ee)[kT], float& lam,
                                                    float& e_next, float& ga, float* pw, float* qw,
-                                                   float (&xb)[kT], float (&yc)[kT]) {
+                                                   float (&xb)[kT], float (&yc)[kT], int odd) {
     // fold over the steps in decreasing order
     (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, hprev, hh, ee, lam, e_next, ga, pw, qw,
-                             xb, yc),
+                             xb, yc, odd),
      ...);
   }
 };
