@@ -60,10 +60,12 @@ template <int TAU>
 __device__ __forceinline__ int pslot_shift(int odd) {
   return ((TAU ^ kPSwap) - TAU) * kPTau * odd;
 }
-// dB and dC partial tiles: 8 row pairs x kBwdChunk steps x 16 states each; the dC half starts 16
-// floats after the dB half so that rows 0 and 1 of a wave, which write the two halves with one
-// instruction, use different LDS banks.
-constexpr int kGcOff = 8 * kBwdChunk * 16 + 16;
+// Once the owner lanes of a wave have read their sums, the wave's partial tiles hold its dB and dC
+// tiles: per row pair (rows 0-1, 2-3) kBwdChunk steps x 16 states, dB at pair * 256 and dC
+// kGcOff further (16 floats past a multiple of 32, so that rows 0 and 1, which write dB and dC
+// with one instruction, use different LDS banks).  Sharing the space keeps the workgroup at
+// 49.7 KB of LDS: three workgroups per CU.
+constexpr int kGcOff = 2 * kBwdChunk * 16 + 16;
 
 template <class IO, bool GATE, bool VEC>
 struct BwdKernel {
@@ -81,10 +83,11 @@ struct BwdKernel {
   struct alignas(16) Smem {
     float2 bc[2][16][kT + 2];       // (B_t[n], C_t[n]) of the chunk, double-buffered
     elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
-    float p[4][4 * kPRow];          // per wave: partial sums over states (y, then ddt)
-    float q[4][4 * kPRow];          // per wave: partial sums over states (du)
-    float gbc[kGcOff + 8 * kT * 16];  // per row pair: dB, then dC, summed over its channels
+    // per wave: partial sums over states, p (y, then ddt) at 0 and q (du) at 4 * kPRow; after
+    // the owner sums, the dB and dC tiles of the wave's row pairs
+    float pq[4][2 * 4 * kPRow];
   };
+  static_assert(kGcOff + 2 * kT * 16 <= 2 * 4 * kPRow, "dB/dC tiles inside the partial tiles");
 
   static __device__ __forceinline__ void run(const BwdArgs& a) {
     __shared__ Smem sm;
@@ -226,12 +229,12 @@ struct BwdKernel {
         bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k][2 * i]);
       // recompute the chunk: states, decays and the partial sums C.h of y
       float hh[kT], ee[kT];
-      float* pw = &sm.p[wave][r * kPRow + k];
+      float* pw = &sm.pq[wave][r * kPRow + k];
       rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, hprev, hh, ee, pw, r & 1);
       wave_lds_sync();
       float y = 0.0f;
       {
-        const float* pr = &sm.p[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
+        const float* pr = &sm.pq[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
 #pragma unroll
         for (int i = 0; i < 16; ++i) y += pr[i];
       }
@@ -248,20 +251,22 @@ struct BwdKernel {
       gd_acc = fmaf(gy, xu, gd_acc);
 
       // the adjoint backwards through the chunk
-      float* qw = &sm.q[wave][r * kPRow + k];
-      float* gbc_w = &sm.gbc[(r & 1) * kGcOff + (2 * wave + (r >> 1)) * kT * 16];
+      float* qw = &sm.pq[wave][4 * kPRow + r * kPRow + k];
+      float* gbc_w = &sm.pq[wave][(r & 1) * kGcOff + (r >> 1) * kT * 16];
       float xb[kT], yc[kT];
       rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
                 lam, e_next, ga, pw, qw, xb, yc, r & 1);
       // dB and dC of each step, summed over channel pairs (independent of one another, so the
-      // row swaps of different steps overlap)
+      // row swaps of different steps overlap); stored below, over the partial tiles
+      float gpair[kT];
 #pragma unroll
-      for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = sum_row_pairs2(xb[t], yc[t]);
+      for (int t = 0; t < kT; ++t) gpair[t] = sum_row_pairs2(xb[t], yc[t]);
       wave_lds_sync();
       float gdt = 0.0f, gx = 0.0f;
       {
-        const float* pr = &sm.p[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
-        const float* qr = &sm.q[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
+        const int own_slot = r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau;
+        const float* pr = &sm.pq[wave][own_slot];
+        const float* qr = &sm.pq[wave][4 * kPRow + own_slot];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           gdt += pr[i];
@@ -269,6 +274,9 @@ struct BwdKernel {
         }
         gdt = fmaf(xu, gx, gdt);  // + u_t sum_n lam B, the input term of ddt
       }
+      wave_lds_sync();  // every lane of the wave has its sums: the tiles take dB and dC
+#pragma unroll
+      for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = gpair[t];
       if (own_ok) {
         const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
         gb_acc += gdelta;
@@ -284,8 +292,8 @@ struct BwdKernel {
         float sb = 0.0f, sc = 0.0f;
 #pragma unroll
         for (int pr = 0; pr < 8; ++pr) {
-          sb += sm.gbc[(pr * kT + tau) * 16 + n];
-          sc += sm.gbc[kGcOff + (pr * kT + tau) * 16 + n];
+          sb += sm.pq[pr >> 1][((pr & 1) * kT + tau) * 16 + n];
+          sc += sm.pq[pr >> 1][kGcOff + ((pr & 1) * kT + tau) * 16 + n];
         }
         if (tau < nv && n < N) {
           const int64_t o = (row0 + int64_t(c) * kT + tau) * N + n;
