@@ -235,7 +235,7 @@ def bench_prefill(args, torch, np, ops, wl):
     del ws_b
     # the training path: the forward saving its chunk-end states (ss_scan_fwd_states), then the
     # backward taking them (SS_FLAG_STATES_GIVEN) instead of rerunning the forward
-    st_buf = torch.empty((w.batch, w.d_inner, (w.seqlen + 15) // 16, w.d_state),
+    st_buf = torch.empty((w.batch, (w.seqlen + 15) // 16, w.d_inner, w.d_state),
                          dtype=torch.float32, device="cuda")
     st_out = torch.empty_like(u)
     fwd_s = lambda: ops.scan_fwd_states(u, dl, A, B, C, D=D, z=z, delta_bias=db, out=st_out,

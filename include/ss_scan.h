@@ -119,7 +119,7 @@ size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_i
  * reading guide, "Expansão de Estado Ciente de Hardware", keeps intermediate states out of
  * memory and recomputes them in the backward pass; the chunk-end states are the points the
  * recomputation restarts from).  As ss_scan_fwd (first-order input term), plus:
- *   states : (batch, d_inner, ceil(seqlen / 16), d_state) float32, written: states[b,d,c,:] is
+ *   states : (batch, ceil(seqlen / 16), d_inner, d_state) float32, written: states[b,c,d,:] is
  *            the state after step min(16 c + 15, seqlen - 1).  Caller-owned, of
  *            ss_scan_fwd_states_bytes() bytes; it must not overlap the inputs, out, h_last or
  *            the workspace.  With d_state <= 16 it is exactly the workspace ss_scan_bwd takes
@@ -209,7 +209,7 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
  *                       D / bias, also when D or delta_bias is NULL, i.e. 0).
  *   dh0               : (batch, d_inner, d_state) float32, written when non-NULL.
  *   workspace         : device scratch of ss_scan_bwd_workspace_bytes() bytes (the chunk-end
- *                       states, batch * d_inner * ceil(seqlen / 16) * d_state floats), required
+ *                       states, (batch, ceil(seqlen / 16), d_inner, d_state) floats), required
  *                       when that is non-zero; SS_ERR_INVALID_ARG if smaller.
  * dA, dB, dC, dD and ddelta_bias are sums formed with float atomics: they are reproducible up
  * to rounding order only.  d_state above 16 and SS_FLAG_ZOH_EXACT -> SS_ERR_UNSUPPORTED.

@@ -173,7 +173,10 @@ struct BwdKernel {
     // ---- pass 1: forward, storing each chunk's end state (skipped when the caller's forward
     // saved them: then only the last chunk is staged for pass 2)
     float h = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
-    float* ck_row = a.ck + (row * nchunks) * N;
+    // chunk-end states, (batch, chunk, d_inner, d_state): the wave's four channels of a chunk are
+    // 256 contiguous bytes
+    float* ck_lane = a.ck + ((b * nchunks) * D + d) * N + k;
+    const int64_t ck_chunk = D * N;
     int buf = 0;
     if (a.states_given) {
       if (nchunks > 0) {
@@ -200,8 +203,9 @@ struct BwdKernel {
       for (int i = 0; i < kT / 2; ++i)
         bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k][2 * i]);
       fwd_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, h);
-      if (lane_ok) ck_row[int64_t(c) * N + k] = h;
       stage(buf ^ 1, next_full);
+      // stored after the staging (whose wait for the loads would also wait for this store)
+      if (lane_ok) ck_lane[int64_t(c) * ck_chunk] = h;
       __syncthreads();
       buf ^= 1;
     }
@@ -220,7 +224,7 @@ struct BwdKernel {
       dt = own_ok ? dt : 0.0f;
       const float du = own_ok ? dt * xu : 0.0f;
       float hprev;
-      if (c > 0) hprev = lane_ok ? ck_row[int64_t(c - 1) * N + k] : 0.0f;
+      if (c > 0) hprev = lane_ok ? ck_lane[int64_t(c - 1) * ck_chunk] : 0.0f;
       else hprev = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
 
       float4 bcv[kT / 2];

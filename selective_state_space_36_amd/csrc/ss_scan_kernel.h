@@ -135,10 +135,13 @@ struct ScanKernel {
     }
     const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
     const float dskip = (!SUMMARY && chan_ok && a.D) ? a.D[d] : 0.0f;
-    // saved chunk-end states: this lane's state n = k of row (b, d), from the segment's first
-    // chunk on (the output pass carries the true state across segments)
+    // saved chunk-end states, (batch, chunk, d_inner, d_state): this lane's state n = k of
+    // channel d, from the segment's first chunk on (the output pass carries the true state across
+    // segments).  The four channels of a wave fill 256 contiguous bytes per chunk.
+    const int64_t st_chunk = a.d_inner * a.d_state;  // floats per chunk
     float* st_lane = (!SUMMARY && a.states && chan_ok)
-                         ? a.states + (row * a.states_chunks + t_begin / kT) * a.d_state + k
+                         ? a.states + ((b * a.states_chunks + t_begin / kT) * a.d_inner + d) *
+                                          a.d_state + k
                          : nullptr;
 
     // Front end (CONV): tap weights of a 4-wide window ending at this lane's step, split by
@@ -354,12 +357,6 @@ struct ScanKernel {
       if (SUMMARY) dt_acc += dt;
 
       steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, h, wave, r, k);
-      if (!SUMMARY && a.states && st_lane) {
-        float* p = st_lane + int64_t(ci) * a.d_state;
-#pragma unroll
-        for (int j = 0; j < NL; ++j)
-          if (k + 16 * j < a.d_state) p[16 * j] = h[j];
-      }
 
       if (!SUMMARY) {
         wave_lds_sync();
@@ -401,6 +398,14 @@ struct ScanKernel {
       }
       hold_store();
       if (has_next) stage_chunk(buf ^ 1);
+      // The chunk-end state goes out after the staging: a wait for the next chunk's loads also
+      // waits for stores issued before it, and this one then has a whole chunk to complete.
+      if (!SUMMARY && a.states && st_lane) {
+        float* p = st_lane + int64_t(ci) * st_chunk;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          if (k + 16 * j < a.d_state) p[16 * j] = h[j];
+      }
       __syncthreads();
       store_out(buf, ci);
     };

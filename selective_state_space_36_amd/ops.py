@@ -217,8 +217,8 @@ def scan_fwd_states(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_so
                     h0=None, return_last_state=False, out=None, h_last=None, states=None,
                     workspace=None, stream=None):
     """Prefill that also saves the state after every 16-step chunk (ss_scan_fwd_states), for
-    scan_bwd(..., states=...).  Arguments as for scan_fwd; states: (batch, d_inner,
-    ceil(L / 16), d_state) float32 or None (allocated here).  Returns (out, states), or
+    scan_bwd(..., states=...).  Arguments as for scan_fwd; states: (batch, ceil(L / 16),
+    d_inner, d_state) float32 or None (allocated here).  Returns (out, states), or
     (out, states, h_last) with return_last_state."""
     batch, L, d_inner = u.shape
     d_state = B.shape[-1]
@@ -239,9 +239,9 @@ def scan_fwd_states(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_so
     _dev(h_last, "h_last", torch.float32, (batch, d_inner, d_state))
     nct = (L + 15) // 16
     if states is None:
-        states = torch.empty((batch, d_inner, nct, d_state), dtype=torch.float32,
+        states = torch.empty((batch, nct, d_inner, d_state), dtype=torch.float32,
                              device=u.device)
-    _dev(states, "states", torch.float32, (batch, d_inner, nct, d_state))
+    _dev(states, "states", torch.float32, (batch, nct, d_inner, d_state))
     if workspace is None:
         nbytes = workspace_bytes(batch, L, d_inner, d_state, u.dtype, None)
         workspace = (torch.empty(nbytes, dtype=torch.uint8, device=u.device) if nbytes
@@ -284,7 +284,7 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
              dh0=torch.empty((batch, d_inner, d_state), **f32) if want_dh0 else None)
     flags = 0
     if states is not None:
-        _dev(states, "states", torch.float32, (batch, d_inner, (L + 15) // 16, d_state))
+        _dev(states, "states", torch.float32, (batch, (L + 15) // 16, d_inner, d_state))
         workspace, flags = states, SS_FLAG_STATES_GIVEN
     elif workspace is None:
         nbytes = int(lib().ss_scan_bwd_workspace_bytes(batch, L, d_inner, d_state, code))

@@ -51,16 +51,16 @@ def check_states(p, h0, *, gate=True):
     # saving the states does not change the outputs
     assert torch.equal(out_s, out_p) and torch.equal(hl, hl_p)
     nct = (L + 15) // 16
-    assert tuple(states.shape) == (batch, D, nct, N)
+    assert tuple(states.shape) == (batch, nct, D, N)
     st = host(states)
-    check_close(st[:, :, -1, :], host(hl), 0.0, "last saved state == h_last")
+    check_close(st[:, -1, :, :], host(hl), 0.0, "last saved state == h_last")
     for c in sorted({0, 1, nct // 2, nct - 2, nct - 1} & set(range(nct))):
         n = min(16 * (c + 1), L)
         q = prefix(p, n)
         _, ref_h = oracle.scan_fwd(q["u"], q["delta"], q["A"], q["B"], q["C"], D=q["D"],
                                    z=q["z"] if gate else None, delta_bias=q["delta_bias"],
                                    h0=None if h0 is None else h0.astype(np.float64))
-        check_close(st[:, :, c, :], ref_h, TOL["f32"], f"state after chunk {c} (step {n - 1})")
+        check_close(st[:, c, :, :], ref_h, TOL["f32"], f"state after chunk {c} (step {n - 1})")
     return states
 
 
@@ -126,7 +126,7 @@ def test_saved_states_full_size_sampled():
                                       delta_bias=dev(p["delta_bias"]))
     torch.cuda.synchronize()
     rows = np.array([0, 17, w.d_inner - 1, 3 * w.d_inner + 2500], dtype=np.int64)
-    st = host(states).reshape(w.batch * w.d_inner, -1, w.d_state)
+    st = np.moveaxis(host(states), 1, 2).reshape(w.batch * w.d_inner, -1, w.d_state)
     for c in (0, 100, 255):
         q = prefix(p, 16 * (c + 1))
         _, ref_h = oracle.scan_fwd(q["u"], q["delta"], q["A"], q["B"], q["C"], D=q["D"],
