@@ -281,6 +281,8 @@ struct BwdKernel {
       wave_lds_sync();  // every lane of the wave has its sums: the tiles take dB and dC
 #pragma unroll
       for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = gpair[t];
+      // the next chunk's tiles first: its wait for the loads would also wait for the stores below
+      if (c > 0) stage(buf ^ 1, true);
       if (own_ok) {
         const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
         gb_acc += gdelta;
@@ -289,7 +291,6 @@ struct BwdKernel {
         static_cast<elem*>(a.ddelta)[e] = IO::from_float(gdelta);
         if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
       }
-      if (c > 0) stage(buf ^ 1, true);
       __syncthreads();  // the wave tiles of dB and dC, and the next chunk's tiles, are complete
       {
         const int tau = tid >> 4, n = tid & 15;
