@@ -3,8 +3,8 @@
 Prints ONE JSON line.  A step is one prefill call (ss_scan_fwd) on the Mamba-2.8B-shaped layer
 (batch 4, L 4096, d_inner 5120, d_state 16, bf16 io, silu gate, fp32 state) with inputs resident
 in HBM; `value` is B*L*D elements per second over K timed steps.  The same line carries:
-  * roofline: the prefill kernel against the VALU issue rate (it is arithmetic-bound on gfx950,
-    see DESIGN.md), with the HBM view alongside;
+  * roofline: the prefill kernel against the VALU issue rate (on gfx950 its 115 VALU slots per
+    element take longer than its 8 bytes of HBM traffic), with the HBM view alongside;
   * decode: the batch-128 single-token step (ss_state_update) run 1000 times back to back over
     pre-generated inputs: end-to-end us/step, kernel-only us/step and state GB/s;
   * cpu_baseline: the fp64 C oracle timed on this host's cores on a bounded sample of rows.
@@ -552,8 +552,9 @@ def cpu_baseline(args, np, w, p):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (each box has "
-              "one MI355X; see DESIGN.md for how the scan would shard)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the scan "
+              "is measured on one MI355X; a multi-GPU run would split batch rows or channel "
+              "blocks across GPUs with no communication inside the scan)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
