@@ -28,8 +28,11 @@
 //     through LDS and double-buffered so that the next chunk's loads are in flight while the
 //     current chunk is computed.  The tiles are addressed as raw buffers sized to the valid
 //     steps, so the hardware range check handles the sequence tail.
-//   * The row's 16 partial sums C_t[n] h_t[n] go through a per-wave LDS tile; the owner lane of
-//     step t adds them up.  No atomics: results are bitwise reproducible.
+//   * The output sum over states goes through a per-wave LDS tile: with d_state <= 16 the lanes
+//     store their states h_t[n] and the owner lane of step t forms C_t . h_t itself (16 FMAs,
+//     C_t read as a row of the C tile); with wider states the lanes store partial sums over
+//     their own states and the owner adds them up.  No atomics: results are bitwise
+//     reproducible.
 //   * Long sequences with few channels are cut into time segments.  A summary pass computes each
 //     segment's end state from a zero start and the sum of its dt; the output pass then starts
 //     segment s from h0 carried through segments 0..s-1 with h <- exp(A sum dt) h + h_end, the
