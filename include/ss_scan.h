@@ -210,7 +210,9 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
  *   dh0               : (batch, d_inner, d_state) float32, written when non-NULL.
  *   workspace         : device scratch of ss_scan_bwd_workspace_bytes() bytes (the chunk-end
  *                       states, (batch, ceil(seqlen / 16), d_inner, d_state) floats), required
- *                       when that is non-zero; SS_ERR_INVALID_ARG if smaller.
+ *                       when that is non-zero; SS_ERR_INVALID_ARG if smaller.  Without
+ *                       SS_FLAG_STATES_GIVEN the call first writes them there with a forward
+ *                       pass (a launch of its own on the stream), then runs the reverse pass.
  * dA, dB, dC, dD and ddelta_bias are sums formed with float atomics: they are reproducible up
  * to rounding order only.  d_state above 16 and SS_FLAG_ZOH_EXACT -> SS_ERR_UNSUPPORTED.
  * Outputs must not overlap inputs, each other or the workspace.

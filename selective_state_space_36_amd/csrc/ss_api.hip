@@ -427,11 +427,30 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   a.softplus = delta_softplus ? 1 : 0;
   a.vec_io = (d_inner % 16 == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
               aligned(delta, 16) && aligned(dout, 16) && (!z || aligned(z, 16))) ? 1 : 0;
-  a.states_given = (flags & SS_FLAG_STATES_GIVEN) ? 1 : 0;
   if (batch * a.n_cblk > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
-  const hipError_t e =
-      ss::launch_scan_bwd(a, dtype == SS_BF16, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!(flags & SS_FLAG_STATES_GIVEN) && batch * seqlen * d_inner > 0) {
+    // The forward pass that stores the chunk-end states runs as the prefill kernel's summary
+    // instance in its states-only form (no segment buffers): the same recurrence at the
+    // prefill's occupancy, five waves per SIMD against the backward kernel's three.
+    ss::ScanArgs f{};
+    f.u = u; f.delta = delta; f.B = B; f.C = C; f.A = A; f.delta_bias = delta_bias; f.h0 = h0;
+    f.batch = batch; f.seqlen = seqlen; f.d_inner = d_inner;
+    segments(seqlen, 1, &f.seg_len, &f.nseg);
+    f.n_cblk = (d_inner + ss::kChanPerWG - 1) / ss::kChanPerWG;
+    f.d_state = static_cast<int32_t>(d_state);
+    f.softplus = a.softplus;
+    f.vec_io = (d_inner % ss::kChanPerWG == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
+                aligned(delta, 16)) ? 1 : 0;
+    f.states = static_cast<float*>(workspace);
+    f.states_chunks = (seqlen + ss::kChunk - 1) / ss::kChunk;
+    f.n_wg = batch * f.n_cblk;
+    const hipError_t ef = ss::launch_scan(f, dtype == SS_BF16, /*summary=*/true, st);
+    if (ef != hipSuccess)
+      return fail(SS_ERR_HIP, "backward forward-pass launch failed: %s", hipGetErrorString(ef));
+  }
+  const hipError_t e = ss::launch_scan_bwd(a, dtype == SS_BF16, st);
   if (e != hipSuccess) return fail(SS_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -32,17 +32,16 @@ struct BwdArgs {
   float* dD;             // nullptr: not computed; accumulated
   float* ddelta_bias;    // nullptr: not computed; accumulated
   float* dh0;            // nullptr: not written
-  float* ck;             // workspace: (batch, d_inner, nchunks, d_state) chunk-end states
+  const float* ck;       // workspace: (batch, nchunks, d_inner, d_state) chunk-end states
   int64_t batch, seqlen, d_inner;
   int64_t n_cblk;        // channel blocks of 16 per batch row
   int32_t d_state;
   int32_t softplus;
   int32_t vec_io;        // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, dout
-  int32_t states_given;  // ck already holds the chunk-end states: skip the forward pass
 };
 
-// Zero the accumulated outputs, then run the backward (one workgroup per 16 channels of a batch
-// row: a forward pass storing chunk-end states, then the reverse pass).
+// Zero the accumulated outputs, then run the reverse pass (one workgroup per 16 channels of a
+// batch row) from the chunk-end states in ck.
 hipError_t launch_scan_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace ss

@@ -26,8 +26,11 @@ struct ScanArgs {
   const float* h0;     // nullptr: zeros
   float* h_last;       // nullptr: not written
   void* out;
-  float* seg_h;        // (nseg-1, batch, d_inner, d_state): local end state of each segment
-  float* seg_dt;       // (nseg-1, batch, d_inner): sum of dt over each segment
+  // summary pass: (nseg-1, batch, d_inner, d_state) local end state and (nseg-1, batch, d_inner)
+  // sum of dt of each segment; seg_h == nullptr selects the states-only pass instead (one
+  // segment, from h0, writing every chunk-end state to `states` and nothing else)
+  float* seg_h;
+  float* seg_dt;
   int64_t batch, seqlen, d_inner;
   int64_t seg_len;     // multiple of kChunk
   int64_t n_cblk;      // channel blocks per batch row = ceil(d_inner / kChanPerWG)
@@ -42,7 +45,7 @@ struct ScanArgs {
   const float* conv_b;  // (d_inner), nullptr: 0
   const void* x_prev;   // (batch, conv_k - 1, d_inner) io dtype: x before t = 0; nullptr: 0
   int32_t conv_k;       // 1..4
-  // chunk-end states (ss_scan_fwd_states): (batch, d_inner, states_chunks, d_state); nullptr: none
+  // chunk-end states: (batch, states_chunks, d_inner, d_state); nullptr: none
   float* states;
   int64_t states_chunks;  // ceil(seqlen / kChunk)
 };

@@ -14,9 +14,9 @@
 // Work layout (as in the forward kernel): one channel per 16-lane DPP row, lane k owns state k
 // and the element work of step k of each 16-step chunk; 16 channels per 256-thread workgroup,
 // one workgroup per (16 channels, batch row); the next chunk's global loads are in flight while a
-// chunk is computed (LDS tiles double-buffered).  Pass 1 runs the forward over the sequence and
-// stores each chunk's end state (workspace, 4 d_state bytes per channel and chunk); when the
-// caller's forward already saved them (ss_scan_fwd_states), pass 1 is skipped.  Pass 2
+// chunk is computed (LDS tiles double-buffered).  The kernel starts from the chunk-end states in
+// the workspace (4 d_state bytes per channel and chunk), saved by the caller's forward
+// (ss_scan_fwd_states) or, before this launch, by the prefill kernel's states-only pass.  It
 // walks the chunks backwards: it recomputes the chunk's 16 states and decays from the stored
 // state into registers, computes y for the gate's derivative, then runs the adjoint backwards
 // through the 16 steps.  Sums over a channel's states go through per-wave LDS tiles (summed by
@@ -131,12 +131,11 @@ struct BwdKernel {
     elem pv[PIECE_E];
     uint4 pvv{0, 0, 0, 0};
     float pbv = 0.0f, pcv = 0.0f;
-    auto issue = [&](int c, bool full) {
+    auto issue = [&](int c) {
       const int nv = nvalid_of(c);
       const int64_t t0 = int64_t(c) * kT;
       const uint32_t io_bytes = static_cast<uint32_t>((nv * D - d0) * ES);
-      const bool want = (full || wave_u < 2) && (GATE || wave_u != 2);  // pass 1: u, delta only
-      if (want) {
+      if (GATE || wave_u != 2) {  // uniform: z only with the gate
         const rsrc_t rt = make_buf(
             static_cast<const char*>(tens[wave_u]) + ((row0 + t0) * D + d0) * ES, io_bytes);
         if (VEC) {
@@ -149,14 +148,11 @@ struct BwdKernel {
       const uint32_t bc_bytes = static_cast<uint32_t>(nv * N * ES);
       const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + (row0 + t0) * N * ES, bc_bytes);
       pbv = IO::widen(buf_load<elem>(rb, bc_off));
-      if (full) {
-        const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
-        pcv = IO::widen(buf_load<elem>(rc, bc_off));
-      }
+      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
+      pcv = IO::widen(buf_load<elem>(rc, bc_off));
     };
-    auto stage = [&](int buf, bool full) {
-      const bool want = (full || wave_u < 2) && (GATE || wave_u != 2);
-      if (want && tl_on) {
+    auto stage = [&](int buf) {
+      if ((GATE || wave_u != 2) && tl_on) {
         elem* dst = &sm.in[buf][wave_u][tl_row][(tl_pc ^ pswz(tl_row)) * PIECE_E];
         if (VEC) {
           *reinterpret_cast<uint4*>(dst) = pvv;
@@ -165,49 +161,20 @@ struct BwdKernel {
           for (int e = 0; e < PIECE_E; ++e) dst[e] = pv[e];
         }
       }
-      sm.bc[buf][bc_n][bc_tau] = make_float2(pbv, full ? pcv : 0.0f);
+      sm.bc[buf][bc_n][bc_tau] = make_float2(pbv, pcv);
     };
     const int own_col = ((cl / PIECE_E) ^ pswz(k)) * PIECE_E + cl % PIECE_E;
     auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][own_col]); };
 
-    // ---- pass 1: forward, storing each chunk's end state (skipped when the caller's forward
-    // saved them: then only the last chunk is staged for pass 2)
-    float h = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
     // chunk-end states, (batch, chunk, d_inner, d_state): the wave's four channels of a chunk are
     // 256 contiguous bytes
-    float* ck_lane = a.ck + ((b * nchunks) * D + d) * N + k;
+    const float* ck_lane = a.ck + ((b * nchunks) * D + d) * N + k;
     const int64_t ck_chunk = D * N;
     int buf = 0;
-    if (a.states_given) {
-      if (nchunks > 0) {
-        issue(nchunks - 1, true);
-        stage(0, true);
-        __syncthreads();
-      }
-    } else if (nchunks > 0) {
-      issue(0, false);
-      stage(0, false);
+    if (nchunks > 0) {  // the last chunk first
+      issue(nchunks - 1);
+      stage(0);
       __syncthreads();
-    }
-    for (int c = 0; c < (a.states_given ? 0 : nchunks); ++c) {
-      // next: chunk c + 1 of this pass, or the last chunk for pass 2
-      const bool next_full = c + 1 == nchunks;
-      issue(next_full ? nchunks - 1 : c + 1, next_full);
-      const bool own_ok = chan_ok && k < nvalid_of(c);
-      const float sv = own(buf, 1) + bias;
-      float dt = a.softplus ? softplus_f(sv) : sv;
-      dt = own_ok ? dt : 0.0f;
-      const float du = own_ok ? dt * own(buf, 0) : 0.0f;
-      float4 bcv[kT / 2];
-#pragma unroll
-      for (int i = 0; i < kT / 2; ++i)
-        bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k][2 * i]);
-      fwd_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, h);
-      stage(buf ^ 1, next_full);
-      // stored after the staging (whose wait for the loads would also wait for this store)
-      if (lane_ok) ck_lane[int64_t(c) * ck_chunk] = h;
-      __syncthreads();
-      buf ^= 1;
     }
 
     // ---- pass 2: chunks backwards
@@ -215,7 +182,7 @@ struct BwdKernel {
     float e_next = 1.0f;
     float ga = 0.0f, gd_acc = 0.0f, gb_acc = 0.0f;
     for (int c = nchunks - 1; c >= 0; --c) {
-      if (c > 0) issue(c - 1, true);
+      if (c > 0) issue(c - 1);
       const int nv = nvalid_of(c);
       const bool own_ok = chan_ok && k < nv;
       const float xu = own(buf, 0);
@@ -282,7 +249,7 @@ struct BwdKernel {
 #pragma unroll
       for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = gpair[t];
       // the next chunk's tiles first: its wait for the loads would also wait for the stores below
-      if (c > 0) stage(buf ^ 1, true);
+      if (c > 0) stage(buf ^ 1);
       if (own_ok) {
         const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
         gb_acc += gdelta;
@@ -323,21 +290,6 @@ struct BwdKernel {
       if (a.dD) atomicAdd(a.dD + d, gd_acc);
       if (a.ddelta_bias) atomicAdd(a.ddelta_bias + d, gb_acc);
     }
-  }
-
-  // Forward step (pass 1): h <- exp(dt A) h + dt u B.
-  template <int TAU>
-  static __device__ __forceinline__ void fwd_step(const float4 (&bcv)[kT / 2], float dt, float du,
-                                                  float A2, float& h) {
-    const float4 v = bcv[TAU / 2];
-    const float bb = (TAU & 1) ? v.z : v.x;
-    h = fmaf(exp2_hw(row_bcast<TAU>(dt) * A2), h, row_bcast<TAU>(du) * bb);
-  }
-  template <int... TAUS>
-  static __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, TAUS...>,
-                                                   const float4 (&bcv)[kT / 2], float dt,
-                                                   float du, float A2, float& h) {
-    (fwd_step<TAUS>(bcv, dt, du, A2, h), ...);
   }
 
   // Recompute step: keep the state and the decay of every step, and the partial sum C.h.

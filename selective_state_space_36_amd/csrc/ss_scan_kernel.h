@@ -142,7 +142,9 @@ struct ScanKernel {
     // channel d, from the segment's first chunk on (the output pass carries the true state across
     // segments).  The four channels of a wave fill 256 contiguous bytes per chunk.
     const int64_t st_chunk = a.d_inner * a.d_state;  // floats per chunk
-    float* st_lane = (!SUMMARY && a.states && chan_ok)
+    // the states-only pass (a summary launch without segment buffers) saves them as well
+    const bool states_only = SUMMARY && a.seg_h == nullptr;
+    float* st_lane = ((!SUMMARY || states_only) && a.states && chan_ok)
                          ? a.states + ((b * a.states_chunks + t_begin / kT) * a.d_inner + d) *
                                           a.d_state + k
                          : nullptr;
@@ -172,7 +174,7 @@ struct ScanKernel {
                          (b * (K - 1) + (K - 1) + tp) * a.d_inner + d);
     }
 
-    if (!SUMMARY) {
+    if (!SUMMARY || states_only) {
       // Initial state of this segment: h0 carried through the summaries of segments 0..seg-1.
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
@@ -403,7 +405,7 @@ struct ScanKernel {
       if (has_next) stage_chunk(buf ^ 1);
       // The chunk-end state goes out after the staging: a wait for the next chunk's loads also
       // waits for stores issued before it, and this one then has a whole chunk to complete.
-      if (!SUMMARY && a.states && st_lane) {
+      if ((!SUMMARY || states_only) && a.states && st_lane) {
         float* p = st_lane + int64_t(ci) * st_chunk;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
@@ -439,7 +441,7 @@ struct ScanKernel {
     }
     __builtin_amdgcn_s_setprio(0);
 
-    if (SUMMARY) {
+    if (SUMMARY && !states_only) {
       // segment summary: local end state and the row's total dt
       float sdt = dt_acc;
       sdt += __shfl_xor(sdt, 1, 16);
