@@ -127,13 +127,16 @@ struct ScanKernel {
     const int64_t t_begin = seg * a.seg_len;
     const int64_t t_end = (t_begin + a.seg_len < a.seqlen) ? t_begin + a.seg_len : a.seqlen;
 
-    // Per-lane constants: A scaled by log2(e) so that exp(dt A) = 2^(dt A2).
-    float A2[NL], h[NL];
+    // Per-lane constants: A scaled by log2(e) so that exp(dt A) = 2^(dt A2), and (exact hold
+    // only) 1 / A, 0 where A = 0.
+    float A2[NL], ia[NL], h[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int n = k + 16 * j;
       const bool ok = chan_ok && n < a.d_state;
-      A2[j] = ok ? a.A[d * a.d_state + n] * kLog2e : 0.0f;
+      const float an = ok ? a.A[d * a.d_state + n] : 0.0f;
+      A2[j] = an * kLog2e;
+      ia[j] = (ZOH && an != 0.0f) ? 1.0f / an : 0.0f;
       h[j] = 0.0f;
     }
     const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
@@ -357,11 +360,11 @@ struct ScanKernel {
       const float sp = softplus_f(sv);  // computed either way: a select, not a branch
       float dt = a.softplus ? sp : sv;
       dt = own_ok ? dt : 0.0f;  // steps past the end leave h unchanged
-      // exact hold: the input term is (dt u / ln 2) B_t[n] (2^y - 1) / y with y = dt A[n] log2(e)
-      const float du = own_ok ? (ZOH ? dt * xu * (1.0f / kLn2) : dt * xu) : 0.0f;
+      // exact hold: the input term is u B_t[n] times the gain of hold_gain
+      const float du = own_ok ? (ZOH ? xu : dt * xu) : 0.0f;
       if (SUMMARY) dt_acc += dt;
 
-      steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, h, wave, r, k);
+      steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, ia, h, wave, r, k);
 
       if (!SUMMARY) {
         wave_lds_sync();
@@ -467,12 +470,28 @@ struct ScanKernel {
   }
 
   // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
+  // Exact-hold gain (exp(dt A) - 1) / A, from e = 2^y with y = dt A log2(e) and ia = 1 / A (0
+  // where A = 0).  For |y| < 1/8 it is dt R(y), R(y) = (2^y - 1) / (y ln 2) = sum_k (y ln 2)^k /
+  // (k + 1)! cut after k = 4 (the rest is below 7e-9 relative there): no cancellation in 2^y - 1
+  // and no division.  Elsewhere it is (e - 1) / A as one fused multiply-add; there |e - 1| >=
+  // 0.083, so the 1-ulp error of e is at most 1.5e-6 of the difference.  e = 0 (large negative y)
+  // gives -1 / A; A = 0 gives dt.
+  static __device__ __forceinline__ float hold_gain(float e, float y, float dt, float ia) {
+    float q = 1.9236258e-3f;
+    q = fmaf(q, y, 1.3876027e-2f);
+    q = fmaf(q, y, 8.0075502e-2f);
+    q = fmaf(q, y, 3.4657359e-1f);
+    q = fmaf(q, y, 1.0f);
+    return fabsf(y) < 0.125f ? dt * q : fmaf(e, ia, -ia);
+  }
+
   // (B, C) pairs for this lane's states, two steps per float4 (with FOLD: B only, four steps per
   // float4, and the lane stores its new state instead of C_t[n] h_t[n]).
   template <int TAU>
   static __device__ __forceinline__ void step(Smem& sm, const float4 (&bcv)[NL][kT / 2],
                                               float dt, float du, const float (&A2)[NL],
-                                              float (&h)[NL], int wave, int r, int k) {
+                                              const float (&ia)[NL], float (&h)[NL], int wave,
+                                              int r, int k) {
     const float dtb = row_bcast<TAU>(dt);
     const float dub = row_bcast<TAU>(du);
     float p = 0.0f;
@@ -489,7 +508,7 @@ struct ScanKernel {
       }
       const float y = dtb * A2[j];
       const float e = exp2_hw(y);
-      const float inc = ZOH ? (dub * bb) * zoh_gain(e, y) : dub * bb;
+      const float inc = ZOH ? (dub * bb) * hold_gain(e, y, dtb, ia[j]) : dub * bb;
       h[j] = fmaf(e, h[j], inc);
       if constexpr (FOLD)
         p = h[j];
@@ -506,9 +525,10 @@ struct ScanKernel {
   template <int... TAUS>
   static __device__ __forceinline__ void steps(std::integer_sequence<int, TAUS...>, Smem& sm,
                                                const float4 (&bcv)[NL][kT / 2], float dt,
-                                               float du, const float (&A2)[NL], float (&h)[NL],
-                                               int wave, int r, int k) {
-    (step<TAUS>(sm, bcv, dt, du, A2, h, wave, r, k), ...);
+                                               float du, const float (&A2)[NL],
+                                               const float (&ia)[NL], float (&h)[NL], int wave,
+                                               int r, int k) {
+    (step<TAUS>(sm, bcv, dt, du, A2, ia, h, wave, r, k), ...);
   }
 
   // The B (with FOLD) or (B, C) tile entries of this lane's states for the 16 steps of a chunk,

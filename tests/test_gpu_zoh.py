@@ -128,6 +128,44 @@ def test_mixed_A_covers_every_branch():
     check_close(gh, rh, TOL["f32"], "h_last")
 
 
+def test_hold_gain_elementwise_accuracy():
+    """One step from a zero state with u = B = C = 1 and one state per channel: each output is the
+    exact-hold gain (exp(dt A) - 1) / A of its channel itself.  4096 channels span dt A from -1e4
+    to +1 (A = 0, tiny and large |A|, exp(dt A) underflowing to 0) and put dt A log2(e) just
+    inside and just outside the kernel's series cut-off at +-1/8; each gain must match the fp64
+    oracle to 3e-6 relative, the accuracy the fp32 evaluation is built for."""
+    rng = np.random.default_rng(123)
+    D = 4096
+    A = -np.exp(rng.uniform(np.log(1e-4), np.log(100.0), size=D))
+    dt = np.exp(rng.uniform(np.log(1e-6), np.log(100.0), size=D))
+    A[:64] = 0.0
+    A[64:128] = rng.uniform(1e-3, 1.0, size=64)  # growth: dt A <= 1 below
+    dt[64:128] = rng.uniform(1e-3, 1.0, size=64)
+    ycut = 0.125 * np.log(2.0)  # |dt A| at the cut-off
+    for i, f in enumerate((0.999, 0.9999, 1.0001, 1.001)):
+        sl = slice(128 + 64 * i, 192 + 64 * i)
+        dt[sl] = rng.uniform(0.01, 10.0, size=64)
+        A[sl] = -f * ycut / dt[sl]
+        A[sl][::2] *= -1.0  # both signs of y
+    A = A.astype(np.float32)
+    dt = dt.astype(np.float32)
+    u = np.ones((1, 1, D), np.float32)
+    delta = dt.reshape(1, 1, D)
+    ones = np.ones((1, 1, 1), np.float32)
+    print(f"  hold gain case: D={D}", flush=True)
+    out = ops().scan_fwd(dev(u), dev(delta), dev(A.reshape(D, 1)), dev(ones), dev(ones),
+                         delta_softplus=False, zoh_exact=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.scan_fwd(u, delta, A.reshape(D, 1), ones, ones, delta_softplus=False,
+                             zoh_exact=True)
+    got = host(out)[0, 0].astype(np.float64)
+    want = ref[0, 0]
+    rel = np.abs(got - want) / np.abs(want)
+    i = int(np.argmax(rel))
+    assert rel.max() <= 3e-6, (f"worst gain at channel {i}: dt={dt[i]!r} A={A[i]!r} got "
+                                f"{got[i]!r} want {want[i]!r} rel {rel[i]:.3g}")
+
+
 def test_decode_zoh_matches_oracle_and_prefill():
     """Decode steps under the exact hold match the oracle step by step, and L decode steps
     reproduce the exact-hold prefill of the same sequence."""
