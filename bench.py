@@ -615,7 +615,8 @@ def main():
         "zoh_exact": {"kernel_us": round(ms_zoh * 1e3, 2),
                       "elements_per_s": round(elems / (ms_zoh * 1e-3), 1),
                       "note": "same layer with the exact zero-order-hold input term; its extra "
-                              "per-update work (series or (2^y-1)/y) is not in the slot count"},
+                              "per-update work (a series or (2^y-1)/A, a compare, a select) "
+                              "is not in the slot count"},
         "conv_front_end": {"kernel_us": round(ms_conv * 1e3, 2),
                            "elements_per_s": round(elems / (ms_conv * 1e-3), 1),
                            "hbm_bytes_avoided": 2 * elems * (2 if w.io_dtype == "bf16" else 4),

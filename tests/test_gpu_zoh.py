@@ -166,6 +166,31 @@ def test_hold_gain_elementwise_accuracy():
                                 f"{got[i]!r} want {want[i]!r} rel {rel[i]:.3g}")
 
 
+def test_full_size_zoh_sampled():
+    """The 2.8B-shaped layer (batch 4, L 4096, d_inner 5120, bf16, gate) under the exact hold, in
+    the launch configuration the benchmark times: sampled rows against the oracle."""
+    from tests.test_gpu_scan import _sample_rows
+    w = wl.WORKLOADS[2]
+    print(f"  generating {w.name} ...", flush=True)
+    p = wl.make_prefill(w)
+    print(f"  running {w.name} with the exact hold ...", flush=True)
+    out, h_last = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]),
+                                 dev(p["C"]), D=dev(p["D"]), z=dev(p["z"]),
+                                 delta_bias=dev(p["delta_bias"]), return_last_state=True,
+                                 zoh_exact=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.batch, w.d_inner, 16, seed=5)
+    b_idx, d_idx = rows // w.d_inner, rows % w.d_inner
+    g = host(out[torch.from_numpy(b_idx).cuda(), :, torch.from_numpy(d_idx).cuda()])
+    gh = host(h_last.reshape(-1, w.d_state)[torch.from_numpy(rows).cuda()])
+    del out, h_last
+    print(f"  oracle on {len(rows)} rows x {w.seqlen} steps ...", flush=True)
+    r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+                            delta_bias=p["delta_bias"], zoh_exact=True, rows=rows)
+    check_close(g, r, TOL["bf16"], f"{w.name} exact-hold out")
+    check_close(gh, rh, TOL["f32"], f"{w.name} exact-hold h_last")
+
+
 def test_decode_zoh_matches_oracle_and_prefill():
     """Decode steps under the exact hold match the oracle step by step, and L decode steps
     reproduce the exact-hold prefill of the same sequence."""
