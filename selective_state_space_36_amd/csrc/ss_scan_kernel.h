@@ -365,6 +365,14 @@ struct ScanKernel {
       if (SUMMARY) dt_acc += dt;
 
       steps(std::make_integer_sequence<int, kT>{}, sm, bcv, dt, du, A2, ia, h, wave, r, k);
+      if constexpr (SUMMARY) {
+        // The summary's steps store nothing, so the compiler would sink their arithmetic past
+        // the next chunk's staging (a branch) while the row broadcasts, which cannot move across
+        // control flow, stay above it; in different blocks the broadcasts are not folded into
+        // the multiplies (32 extra moves per chunk).  Using the states here keeps them together.
+#pragma unroll
+        for (int j = 0; j < NL; ++j) asm volatile("" ::"v"(h[j]));
+      }
 
       if (!SUMMARY) {
         wave_lds_sync();
