@@ -477,7 +477,6 @@ struct ScanKernel {
     }
   }
 
-  // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
   // Exact-hold gain (exp(dt A) - 1) / A, from e = 2^y with y = dt A log2(e) and ia = 1 / A (0
   // where A = 0).  For |y| < 1/8 it is dt R(y), R(y) = (2^y - 1) / (y ln 2) = sum_k (y ln 2)^k /
   // (k + 1)! cut after k = 4 (the rest is below 7e-9 relative there): no cancellation in 2^y - 1
@@ -493,6 +492,7 @@ struct ScanKernel {
     return fabsf(y) < 0.125f ? dt * q : fmaf(e, ia, -ia);
   }
 
+  // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
   // (B, C) pairs for this lane's states, two steps per float4 (with FOLD: B only, four steps per
   // float4, and the lane stores its new state instead of C_t[n] h_t[n]).
   template <int TAU>
