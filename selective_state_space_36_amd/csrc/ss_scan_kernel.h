@@ -82,6 +82,8 @@ struct ScanKernel {
   // the owner adding 16 products (31 instructions per chunk -> 17).  Wider states keep the
   // per-lane partial sums: their states would not fit the per-wave tile.
   static constexpr bool FOLD = NL == 1 && !SUMMARY;
+  // One state per lane: B and C in tiles of their own (a summary pass stages only B).
+  static constexpr bool SPLIT = NL == 1;
   // The 16-byte pieces of row (step) k of a u/delta/z/out tile are stored XOR-permuted by
   // (k / (8 / PIECES)) mod PIECES.  The owner lanes of steps 4 (bf16) or 2 (fp32) apart read the
   // same column of rows that share LDS banks (rows are 32 or 64 bytes; LDS has 32 banks of 4
@@ -98,7 +100,7 @@ struct ScanKernel {
     float c[2][kT][kSRow];  // C_t[n] per chunk, row t (read by the owner lane of step t)
   };
   struct alignas(16) Smem {
-    std::conditional_t<FOLD, SplitTile, PairTile> bt;
+    std::conditional_t<SPLIT, SplitTile, PairTile> bt;
     uint4 in[2][NTEN][kT][PIECES];  // raw u, delta, z tiles per chunk
     uint4 out[2][kT][PIECES];       // raw output tile per chunk
     float p[kWaves][4 * kPRow];     // per-wave partial sums or states [row][step][lane]
@@ -273,9 +275,9 @@ struct ScanKernel {
     auto stage_chunk = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < BC_PER_THREAD; ++i) {
-        if constexpr (FOLD) {
+        if constexpr (SPLIT) {
           sm.bt.b[buf][bc_n[i]][bc_tau[i]] = IO::widen(pre.rb[i]);
-          sm.bt.c[buf][bc_tau[i]][bc_n[i]] = IO::widen(pre.rc[i]);
+          if constexpr (!SUMMARY) sm.bt.c[buf][bc_tau[i]][bc_n[i]] = IO::widen(pre.rc[i]);
         } else {
           sm.bt.bc[buf][bc_n[i]][bc_tau[i]] =
               make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
@@ -493,8 +495,8 @@ struct ScanKernel {
   }
 
   // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
-  // (B, C) pairs for this lane's states, two steps per float4 (with FOLD: B only, four steps per
-  // float4, and the lane stores its new state instead of C_t[n] h_t[n]).
+  // (B, C) pairs for this lane's states, two steps per float4 (with one state per lane: B only,
+  // four steps per float4; with FOLD the lane stores its new state instead of C_t[n] h_t[n]).
   template <int TAU>
   static __device__ __forceinline__ void step(Smem& sm, const float4 (&bcv)[NL][kT / 2],
                                               float dt, float du, const float (&A2)[NL],
@@ -506,7 +508,7 @@ struct ScanKernel {
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       float bb, cc = 0.0f;
-      if constexpr (FOLD) {
+      if constexpr (SPLIT) {
         const float4 v = bcv[j][TAU / 4];
         bb = (TAU & 3) == 0 ? v.x : ((TAU & 3) == 1 ? v.y : ((TAU & 3) == 2 ? v.z : v.w));
       } else {
@@ -539,13 +541,13 @@ struct ScanKernel {
     (step<TAUS>(sm, bcv, dt, du, A2, ia, h, wave, r, k), ...);
   }
 
-  // The B (with FOLD) or (B, C) tile entries of this lane's states for the 16 steps of a chunk,
-  // read as 16-byte pieces so that the steps themselves are pure VALU work.
+  // The B (one state per lane) or (B, C) tile entries of this lane's states for the 16 steps of
+  // a chunk, read as 16-byte pieces so that the steps themselves are pure VALU work.
   static __device__ __forceinline__ void read_b(const Smem& sm, int buf, int k,
                                                 float4 (&bcv)[NL][kT / 2]) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      if constexpr (FOLD) {
+      if constexpr (SPLIT) {
 #pragma unroll
         for (int i = 0; i < kT / 4; ++i)
           bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bt.b[buf][k][4 * i]);
