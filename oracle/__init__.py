@@ -79,8 +79,8 @@ def _bind(lib):
                                         i32, i64, i64, i64, vp, i64, vp, i32]
     lib.oracle_conv_silu.argtypes = [vp, vp, vp, vp, i64, i32, i64, i64, i64, vp]
     lib.oracle_conv_silu.restype = i32
-    lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64,
-                                    i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i64, i64,
+                                    i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
     lib.oracle_scan_bwd.restype = i32
     lib.oracle_scan2_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64,
                                      i64, i64, i64, vp, vp, i32]
@@ -294,11 +294,13 @@ def conv_step(conv_state, x, w, b=None):
 
 
 def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
-             h0=None, dh_last=None):
-    """fp64 gradients of scan_fwd (first-order discretisation) for upstream gradients dout
-    (batch, L, d_inner) and dh_last (batch, d_inner, d_state) or None.  Inputs as for scan_fwd
-    (u in the io dtype).  Returns a dict with du, ddelta, dz (None without z), dA, dB, dC, dD,
-    ddelta_bias, dh0 -- float64 arrays shaped like the corresponding inputs."""
+             h0=None, dh_last=None, zoh_exact=False, nthreads=None):
+    """fp64 gradients of scan_fwd (first-order input term, or the exact ZOH one with zoh_exact)
+    for upstream gradients dout (batch, L, d_inner) and dh_last (batch, d_inner, d_state) or
+    None.  Inputs as for scan_fwd (u in the io dtype).  Returns a dict with du, ddelta, dz (None
+    without z), dA, dB, dC, dD, ddelta_bias, dh0 -- float64 arrays shaped like the
+    corresponding inputs.  Rows run on nthreads OpenMP threads (default: every core this
+    process may use); the sums over rows are added in a fixed order for a given count."""
     delta, dt = _io(delta, "delta")
     u, udt = _io_u(u, dt)
     if udt != dt:
@@ -324,11 +326,14 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
              dA=np.empty((d_inner, d_state)), dB=np.empty((batch, L, d_state)),
              dC=np.empty((batch, L, d_state)), dD=np.empty(d_inner),
              ddelta_bias=np.empty(d_inner), dh0=np.empty((batch, d_inner, d_state)))
+    if nthreads is None:
+        nthreads = max(1, len(os.sched_getaffinity(0)))
     rc = _load().oracle_scan_bwd(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-        int(bool(delta_softplus)), _ptr(h0), dt, batch, L, d_inner, d_state, _ptr(dout),
-        _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]),
-        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]))
+        int(bool(delta_softplus)), _ptr(h0), int(bool(zoh_exact)), dt, batch, L, d_inner,
+        d_state, _ptr(dout), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]),
+        _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]),
+        _ptr(g["dh0"]), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_scan_bwd rejected its arguments")
     return g

@@ -1,9 +1,10 @@
 """GPU parity of the backward entry point (ss_scan_bwd) against the fp64 oracle's reverse-mode
 gradients (oracle.scan_bwd, itself pinned by finite differences).
 
-Comparison per gradient tensor: |gpu - oracle| <= tol * (|oracle| + rms(oracle)), with
-tol = 1e-3 for float32 results (the recurrences and the sums over channels and steps run in
-float32) and 2e-2 for results stored in bfloat16 (du, ddelta, dz with bf16 io)."""
+Comparison per gradient element, in the same form as the forward's: |gpu - oracle| <=
+tol + tol * |oracle|, with tol = 1e-3 for float32 results (the recurrences and the sums over
+channels and steps run in float32) and 2e-2 for results stored in bfloat16 (du, ddelta, dz with
+bf16 io)."""
 import numpy as np
 import pytest
 
@@ -31,17 +32,17 @@ def ops():
 
 
 def check_grad(got, ref, tol, what):
+    """Elementwise |got - ref| <= tol + tol * |ref|."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     err = np.abs(got - ref)
-    bound = tol * (np.abs(ref) + rms) + 1e-30
+    bound = tol + tol * np.abs(ref)
     bad = ~(err <= bound)
     if bad.any():
         i = np.unravel_index(np.argmax(err / bound), err.shape)
-        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside tol={tol} (rms "
-                             f"{rms:.3e}); worst at {tuple(int(v) for v in i)}: got {got[i]!r} "
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside atol=rtol={tol}; "
+                             f"worst at {tuple(int(v) for v in i)}: got {got[i]!r} "
                              f"want {ref[i]!r}")
 
 
@@ -154,32 +155,3 @@ def test_invalid_bwd_arguments():
     with pytest.raises(o.SSError) as e:
         o.scan_bwd(*args, g_out, workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
     assert e.value.status == o.SS_ERR_INVALID_ARG
-
-
-def test_full_size_bwd_sampled_channels():
-    """The 2.8B-shaped layer (batch 4, L 4096, d_inner 5120) through the backward; the
-    per-channel gradients (du, ddelta, dz, dA, dD, ddelta_bias, dh0) are checked on a sample of
-    channels (block edges and random ones) against the oracle run on those channels alone, which
-    is exact because channels are independent.  dB and dC sum over all channels and are covered
-    at the smaller sizes above."""
-    w = wl.WORKLOADS[2]
-    p = wl.make_prefill(w)
-    rng = np.random.default_rng(5)
-    g_out = wl.f32_to_bf16_bits(rng.standard_normal(p["u"].shape).astype(np.float32))
-    g = ops().scan_bwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"]),
-                       dev(g_out), D=dev(p["D"]), z=dev(p["z"]), delta_bias=dev(p["delta_bias"]))
-    torch.cuda.synchronize()
-    chans = np.unique(np.concatenate([np.arange(0, 17), np.arange(w.d_inner - 17, w.d_inner),
-                                      rng.integers(0, w.d_inner, size=30)])).astype(np.int64)
-    print(f"  bwd full size, {len(chans)} sampled channels", flush=True)
-    sub = lambda x: np.ascontiguousarray(x[:, :, chans])
-    ref = oracle.scan_bwd(sub(p["u"]), sub(p["delta"]), p["A"][chans], p["B"], p["C"],
-                          wl_f64(sub(g_out)), D=p["D"][chans], z=sub(p["z"]),
-                          delta_bias=p["delta_bias"][chans])
-    ct = torch.from_numpy(chans).cuda()
-    for key in ("du", "ddelta", "dz"):
-        check_grad(host(g[key][:, :, ct]), ref[key], 2e-2, key)
-    check_grad(host(g["dA"][ct]), ref["dA"], 1e-3, "dA")
-    check_grad(host(g["dD"][ct]), ref["dD"], 1e-3, "dD")
-    check_grad(host(g["ddelta_bias"][ct]), ref["ddelta_bias"], 1e-3, "ddelta_bias")
-    check_grad(host(g["dh0"][:, ct]), ref["dh0"], 1e-3, "dh0")

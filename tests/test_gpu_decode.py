@@ -134,20 +134,6 @@ def test_decode_invalid_arguments():
     assert e.value.status == o.SS_ERR_INVALID_ARG
 
 
-def test_decode_full_size_sampled():
-    """The batch-128 decode workload at full size for 50 consecutive steps (the bench times
-    1000): every step's output checked on sampled rows, and the final state on them."""
-    w = wl.WORKLOADS[4]
-    d = wl.make_decode(w, steps=50)
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([
-        np.arange(0, 16), np.arange(w.d_inner - 16, w.d_inner + 16),
-        (w.batch - 1) * w.d_inner + np.arange(w.d_inner - 16, w.d_inner),
-        rng.integers(0, w.batch * w.d_inner, size=2000)])).astype(np.int64)
-    print(f"  decode full size, {len(rows)} sampled rows", flush=True)
-    _decode_steps(d, 50, rows=rows)
-
-
 def test_decode_graph_replays_match_eager():
     """Decode steps captured into a HIP graph (as the benchmark's graph line does): each of
     several replays, with eager work and synchronisation between them, matches the same steps

@@ -1,0 +1,210 @@
+"""GPU parity on the five stated workloads at their full sizes, every output element compared
+with the fp64 oracle, in the launch configuration the benchmark times.
+
+* the Mamba-130M- and Mamba-2.8B-shaped prefills: every (b, t, d) output and every final state,
+  gated with the skip term, and with the scan isolated (no D, no z: out = C.h alone, which the
+  D.u term would otherwise dominate);
+* the 2^20-step layer: all 1536 rows, streamed through the oracle in channel blocks so that
+  its fp64 output never exceeds about 1 GB at a time;
+* the batch-128 decode: all 1000 steps, every step's output on every row, the final state on
+  every row;
+* the backward of the 2.8B-shaped layer: every gradient at full size (the sums over channels
+  dB, dC included) against the oracle's reverse mode.
+
+Bars (elementwise |gpu - oracle| <= tol + tol * |oracle|): out 2e-2 (bf16 io); the float32
+state 1e-4 where the state runs at most 4096 steps, 2e-2 on the 2^20-step layer.  Each test
+prints the achieved maximum errors.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from selective_state_space_36_amd import workloads as wl
+from tests.helpers import TOL, dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_36_amd import ops
+    ops.lib()  # raises if the HIP library is missing: no silent fallback
+    yield
+
+
+def ops():
+    from selective_state_space_36_amd import ops as o
+    return o
+
+
+class Errors:
+    """Elementwise check |got - want| <= tol + tol*|want| over blocks, keeping the worst errors."""
+
+    def __init__(self, what, tol):
+        self.what, self.tol = what, tol
+        self.max_abs = 0.0
+        self.max_rel = 0.0      # |got - want| / |want| over elements with |want| >= 1e-3
+        self.worst = 0.0        # max of err / bound (<= 1 passes)
+        self.n = 0
+
+    def add(self, got, want, where=""):
+        got = np.asarray(got, dtype=np.float64)
+        want = np.asarray(want, dtype=np.float64)
+        assert got.shape == want.shape, (self.what, got.shape, want.shape)
+        err = np.subtract(got, want)
+        np.abs(err, out=err)
+        bound = np.abs(want)
+        big = bound >= 1e-3
+        if big.any():
+            self.max_rel = max(self.max_rel, float((err[big] / bound[big]).max()))
+        bound *= self.tol
+        bound += self.tol
+        ratio = err / bound
+        self.n += err.size
+        if err.size:
+            self.max_abs = max(self.max_abs, float(err.max()))
+            w = float(ratio.max())            # NaN propagates and fails the check below
+            self.worst = max(self.worst, w) if w == w else float("nan")
+            if not w <= 1.0:
+                bad = ~(ratio <= 1.0)
+                i = np.unravel_index(np.argmax(np.where(bad, np.inf, ratio)), err.shape)
+                raise AssertionError(
+                    f"{self.what}{where}: {int(bad.sum())} of {bad.size} elements outside "
+                    f"atol=rtol={self.tol}; worst at {tuple(int(v) for v in i)}: got "
+                    f"{got[i]!r} want {want[i]!r}")
+
+    def report(self):
+        print(f"  {self.what}: {self.n} elements, max abs err {self.max_abs:.3e}, max rel err "
+              f"{self.max_rel:.3e} (|ref| >= 1e-3), worst err/bound {self.worst:.3f} at "
+              f"tol {self.tol}", flush=True)
+
+
+def _to_gpu(p):
+    return {k: (dev(v) if isinstance(v, np.ndarray) else None) for k, v in p.items()}
+
+
+def _prefill_full(index, block):
+    """Run the stated prefill workload whole (gated, then scan isolated) and compare every row
+    in channel blocks of `block` against the oracle on those rows."""
+    w = wl.WORKLOADS[index]
+    print(f"  generating {w.name} ({w.batch} x {w.seqlen} x {w.d_inner})", flush=True)
+    p = wl.make_prefill(w)
+    g = _to_gpu(p)
+    h_tol = TOL["f32"] if w.seqlen <= 4096 else TOL["bf16"]
+    for gated in (True, False):
+        label = "gated" if gated else "scan isolated"
+        print(f"  {w.name} {label}: GPU", flush=True)
+        out, h_last = ops().scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"],
+                                     D=g["D"] if gated else None, z=g["z"] if gated else None,
+                                     delta_bias=g["delta_bias"], return_last_state=True)
+        torch.cuda.synchronize()
+        e_out = Errors(f"{w.name} {label} out", TOL["bf16"])
+        e_h = Errors(f"{w.name} {label} h_last", h_tol)
+        for b in range(w.batch):
+            for d0 in range(0, w.d_inner, block):
+                d1 = min(w.d_inner, d0 + block)
+                rows = (b * w.d_inner + np.arange(d0, d1)).astype(np.int64)
+                r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
+                                        D=p["D"] if gated else None,
+                                        z=p["z"] if gated else None,
+                                        delta_bias=p["delta_bias"], rows=rows)
+                got = out[b, :, d0:d1].float().t().contiguous().cpu().numpy()
+                e_out.add(got, r, f" (b={b}, d={d0}..{d1 - 1})")
+                del got, r
+                e_h.add(h_last[b, d0:d1].cpu().numpy(), rh, f" (b={b}, d={d0}..{d1 - 1})")
+        e_out.report()
+        e_h.report()
+        del out, h_last
+    del g
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("index", [1, 2])
+def test_full_prefill_every_row(index):
+    _prefill_full(index, block=1024)
+
+
+@pytest.mark.timeout(1200)
+def test_full_long_prefill_every_row():
+    """The 2^20-step layer: one call, the state carried over every step (the automatic time
+    split runs its summary and output passes), all 1536 rows compared."""
+    _prefill_full(3, block=128)
+
+
+@pytest.mark.timeout(900)
+def test_full_decode_all_steps():
+    """The batch-128 decode workload: 1000 consecutive in-place steps, every step's output on
+    every (b, d) and the final state on every row, against the oracle's fp64 state advanced
+    step by step."""
+    w = wl.WORKLOADS[4]
+    print(f"  generating {w.decode_steps} decode steps", flush=True)
+    d = wl.make_decode(w)
+    steps = w.decode_steps
+    st = dev(d["state"])
+    u, dl, z, B, C = (dev(d[k]) for k in ("u", "delta", "z", "B", "C"))
+    A, D, db = dev(d["A"]), dev(d["D"]), dev(d["delta_bias"])
+    outs = torch.empty((steps, w.batch, w.d_inner), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    print("  1000 GPU steps", flush=True)
+    for s in range(steps):
+        ops().state_update(st, u[s], dl[s], A, B[s], C[s], D=D, z=z[s], delta_bias=db,
+                           out=outs[s], stream=stream)
+    torch.cuda.synchronize()
+    st_ref = d["state"].astype(np.float64)
+    e_out = Errors("decode out (every step)", TOL["bf16"])
+    print("  1000 oracle steps", flush=True)
+    for s in range(steps):
+        ref = oracle.state_update(st_ref, d["u"][s], d["delta"][s], d["A"], d["B"][s],
+                                  d["C"][s], D=d["D"], z=d["z"][s], delta_bias=d["delta_bias"])
+        e_out.add(outs[s].float().cpu().numpy(), ref, f" (step {s})")
+        if s % 250 == 249:
+            print(f"    step {s + 1} ok", flush=True)
+    e_out.report()
+    e_st = Errors("decode final state", TOL["f32"])
+    e_st.add(st.cpu().numpy(), st_ref)
+    e_st.report()
+
+
+@pytest.mark.timeout(900)
+def test_full_backward_every_gradient():
+    """The backward of the 2.8B-shaped layer for a seeded upstream gradient: every element of
+    every gradient against the oracle's reverse mode over the whole layer, including dB and dC
+    (each entry a sum over all 5120 channels) and dA, dD, ddelta_bias (sums over batch and
+    steps).  Bound, elementwise: |gpu - ref| <= tol + tol * |ref|, tol = 2e-2 for the
+    bf16-stored du, ddelta, dz and 1e-3 for the float32 ones."""
+    w = wl.WORKLOADS[2]
+    print(f"  generating {w.name}", flush=True)
+    p = wl.make_prefill(w)
+    rng = np.random.default_rng(5)
+    g_out = wl.f32_to_bf16_bits(rng.standard_normal(p["u"].shape).astype(np.float32))
+    g = _to_gpu(p)
+    print("  GPU backward", flush=True)
+    gr = ops().scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dev(g_out), D=g["D"],
+                        z=g["z"], delta_bias=g["delta_bias"])
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu().numpy() for k, v in gr.items() if v is not None}
+    del gr, g
+    torch.cuda.empty_cache()
+    print("  oracle backward", flush=True)
+    ref = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
+                          wl.bf16_bits_to_f32(g_out).astype(np.float64), D=p["D"], z=p["z"],
+                          delta_bias=p["delta_bias"])
+    for key in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        tol = 2e-2 if key in ("du", "ddelta", "dz") else 1e-3
+        want = ref[key]
+        err = np.abs(got[key].astype(np.float64) - want)
+        bound = tol + tol * np.abs(want)
+        ratio = float((err / bound).max())
+        print(f"  {key}: {want.size} elements, max abs err {err.max():.3e}, max |ref| "
+              f"{np.abs(want).max():.3e}, worst err/bound {ratio:.3f} at tol {tol}", flush=True)
+        bad = ~(err <= bound)
+        if bad.any():
+            i = np.unravel_index(np.argmax(err / bound), err.shape)
+            raise AssertionError(f"{key}: {int(bad.sum())} of {bad.size} outside; worst at "
+                                 f"{tuple(int(v) for v in i)}: got {got[key][i]!r} want "
+                                 f"{want[i]!r}")

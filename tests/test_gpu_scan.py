@@ -204,59 +204,3 @@ def test_invalid_arguments_raise():
         o.scan_fwd(u, d, A, B, C, nseg=4, workspace=torch.empty(16, dtype=torch.uint8,
                                                                   device="cuda"))
     assert e.value.status == o.SS_ERR_INVALID_ARG
-
-
-# ------------------------------------------------------------------------------------------
-# full-size workloads, in the launch configuration the benchmark times; sampled rows
-# ------------------------------------------------------------------------------------------
-def _sample_rows(batch, d_inner, k, seed):
-    """Rows covering every batch index, both ends of the channel range and random interior
-    channels (each row is one independent recurrence, so the check on it is exact)."""
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for b in range(batch):
-        for d in (0, 1, 15, 16, d_inner // 2, d_inner - 17, d_inner - 1):
-            rows.add(b * d_inner + d)
-    rows.update(rng.integers(0, batch * d_inner, size=k).tolist())
-    return np.array(sorted(rows), dtype=np.int64)
-
-
-@pytest.mark.parametrize("index", [1, 2, 3])
-def test_full_size_workload_sampled(index):
-    w = wl.WORKLOADS[index]
-    print(f"  generating {w.name} ...", flush=True)
-    p = wl.make_prefill(w)
-    print(f"  running {w.name} on the GPU ...", flush=True)
-    out, h_last = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]),
-                                 dev(p["C"]), D=dev(p["D"]), z=dev(p["z"]),
-                                 delta_bias=dev(p["delta_bias"]), return_last_state=True)
-    torch.cuda.synchronize()
-    rows = _sample_rows(w.batch, w.d_inner, 24 if index < 3 else 6, seed=index)
-    b_idx, d_idx = rows // w.d_inner, rows % w.d_inner
-    g = out[torch.from_numpy(b_idx).cuda(), :, torch.from_numpy(d_idx).cuda()]
-    g = host(g)
-    gh = host(h_last.reshape(-1, w.d_state)[torch.from_numpy(rows).cuda()])
-    del out, h_last
-    print(f"  oracle on {len(rows)} rows x {w.seqlen} steps ...", flush=True)
-    r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
-                            delta_bias=p["delta_bias"], rows=rows)
-    check_close(g, r, TOL["bf16"], f"{w.name} out")
-    # the state is float32 from exact bf16 inputs: the 130M and 2.8B layers meet the float32
-    # bound; the 1M-step layer carries its state through 2^20 steps and is held to the bf16 one
-    h_tol = TOL["f32"] if index < 3 else TOL["bf16"]
-    check_close(gh, rh, h_tol, f"{w.name} h_last")
-
-    # the scan isolated (no skip term, no gate): out is C.h alone, which D.u would otherwise
-    # dominate
-    print(f"  running {w.name} without D and z ...", flush=True)
-    out, h_last = ops().scan_fwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]),
-                                 dev(p["C"]), delta_bias=dev(p["delta_bias"]),
-                                 return_last_state=True)
-    torch.cuda.synchronize()
-    g = host(out[torch.from_numpy(b_idx).cuda(), :, torch.from_numpy(d_idx).cuda()])
-    gh = host(h_last.reshape(-1, w.d_state)[torch.from_numpy(rows).cuda()])
-    del out, h_last
-    r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
-                            delta_bias=p["delta_bias"], rows=rows)
-    check_close(g, r, TOL["bf16"], f"{w.name} out (scan isolated)")
-    check_close(gh, rh, h_tol, f"{w.name} h_last (scan isolated)")

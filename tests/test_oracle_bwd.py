@@ -22,13 +22,14 @@ def _case(rng, batch=2, L=6, D=3, N=4, gate=True, skip=True, bias=True):
     return c, w_out, w_h
 
 
-def _loss(c, w_out, w_h, softplus=True):
+def _loss(c, w_out, w_h, softplus=True, zoh=False):
     out, h = oracle.scan_fwd(c["u"], c["delta"], c["A"], c["B"], c["C"], D=c["D"], z=c["z"],
-                             delta_bias=c["delta_bias"], delta_softplus=softplus, h0=c["h0"])
+                             delta_bias=c["delta_bias"], delta_softplus=softplus, h0=c["h0"],
+                             zoh_exact=zoh)
     return float(np.sum(w_out * out) + np.sum(w_h * h))
 
 
-def _fd(c, key, w_out, w_h, softplus=True):
+def _fd(c, key, w_out, w_h, softplus=True, zoh=False):
     """Central difference of the loss in every element of c[key].  The perturbed values are
     rounded to the input's dtype, so the difference quotient divides by the step actually taken
     (it differs from 2H only where x +- H crosses a power of two)."""
@@ -42,7 +43,7 @@ def _fd(c, key, w_out, w_h, softplus=True):
             xs.append(float(pert[idx]))
             c2 = dict(c)
             c2[key] = pert
-            vals.append(_loss(c2, w_out, w_h, softplus))
+            vals.append(_loss(c2, w_out, w_h, softplus, zoh))
         grad[idx] = (vals[0] - vals[1]) / (xs[0] - xs[1])
     return grad
 
@@ -63,6 +64,57 @@ def test_gradients_match_finite_differences(softplus):
     for key, gk in KEYS:
         fd = _fd(c, key, w_out, w_h, softplus)
         np.testing.assert_allclose(g[gk], fd, rtol=1e-6, atol=1e-7, err_msg=gk)
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+def test_exact_zoh_gradients_match_finite_differences(softplus):
+    """The exact zero-order-hold input term (exp(dt a) - 1) / a * B: its derivatives in dt and a
+    enter ddelta, du, dB and dA; finite differences of the exact-ZOH forward oracle pin them."""
+    rng = np.random.default_rng(11 + softplus)
+    c, w_out, w_h = _case(rng)
+    if not softplus:
+        c["delta"] = np.abs(c["delta"]) + np.float32(0.1)
+    g = oracle.scan_bwd(c["u"], c["delta"], c["A"], c["B"], c["C"], w_out, D=c["D"], z=c["z"],
+                        delta_bias=c["delta_bias"], delta_softplus=softplus, h0=c["h0"],
+                        dh_last=w_h, zoh_exact=True)
+    for key, gk in KEYS:
+        fd = _fd(c, key, w_out, w_h, softplus, zoh=True)
+        np.testing.assert_allclose(g[gk], fd, rtol=1e-6, atol=1e-7, err_msg=gk)
+
+
+def test_exact_zoh_gradient_at_zero_decay():
+    """A column of A equal to 0: the exact-ZOH gain is dt there, and its derivative in a is
+    dt^2 / 2 (the limit); a one-sided finite difference from a = 0 into a < 0 pins it."""
+    rng = np.random.default_rng(13)
+    c, w_out, w_h = _case(rng, gate=False)
+    c["A"][:, 1] = 0.0
+    g = oracle.scan_bwd(c["u"], c["delta"], c["A"], c["B"], c["C"], w_out, D=c["D"],
+                        delta_bias=c["delta_bias"], h0=c["h0"], dh_last=w_h, zoh_exact=True)
+    step = 2.0 ** -12
+    for d in range(c["A"].shape[0]):
+        vals = []
+        for k in (0, 1, 2):
+            c2 = dict(c)
+            c2["A"] = c["A"].copy()
+            c2["A"][d, 1] = -k * step
+            vals.append(_loss(c2, w_out, w_h, zoh=True))
+        # second-order one-sided difference: f'(0) ~ (3 f(0) - 4 f(-h) + f(-2h)) / (2h)
+        fd = (3 * vals[0] - 4 * vals[1] + vals[2]) / (2 * step)
+        np.testing.assert_allclose(g["dA"][d, 1], fd, rtol=1e-5, atol=1e-6)
+
+
+def test_summed_gradients_do_not_depend_on_thread_count():
+    """The sums over rows (dA, dB, dC, dD, ddelta_bias) run in per-thread partials; any thread
+    count gives the same values to rounding, and one count gives the same bits every time."""
+    rng = np.random.default_rng(17)
+    c, w_out, w_h = _case(rng, batch=3, L=20, D=13, N=5)
+    run = lambda nt: oracle.scan_bwd(c["u"], c["delta"], c["A"], c["B"], c["C"], w_out, D=c["D"],
+                                     z=c["z"], delta_bias=c["delta_bias"], h0=c["h0"],
+                                     dh_last=w_h, nthreads=nt)
+    g1, g4, g4b = run(1), run(4), run(4)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        np.testing.assert_allclose(g4[k], g1[k], rtol=1e-12, atol=1e-14, err_msg=k)
+        np.testing.assert_array_equal(g4[k], g4b[k], err_msg=k)
 
 
 def test_without_gate_skip_bias_or_h0():

@@ -54,16 +54,16 @@ MUTATIONS = [
     ("conv without silu", "        u[(b * seqlen + t) * d_inner + d] = silu(acc);",
      "        u[(b * seqlen + t) * d_inner + d] = acc;"),
     ("adjoint without decay",
-     "        lam[n] = gy * cn + (t == seqlen - 1 ? lam[n] : e_next[n] * lam[n]);",
-     "        lam[n] = gy * cn + lam[n];"),
-    ("softplus derivative dropped", "      double dd = delta_softplus ? ddt / (1.0 + exp(-s)) : ddt;",
-     "      double dd = ddt;"),
-    ("dC from the previous state", "        dC[bc + n] += gy * h[n];", "        dC[bc + n] += gy * hp[n];"),
-    ("dA without the decay factor", "        dA[d * d_state + n] += lam[n] * dt * et * hp[n];",
-     "        dA[d * d_state + n] += lam[n] * dt * hp[n];"),
+     "      lam[n] = gy * cn + (t == seqlen - 1 ? lam[n] : e_next[n] * lam[n]);",
+     "      lam[n] = gy * cn + lam[n];"),
+    ("softplus derivative dropped", "    double dd = delta_softplus ? ddt / (1.0 + exp(-s)) : ddt;",
+     "    double dd = ddt;"),
+    ("dC from the previous state", "      dC[bc + n] += gy * h[n];", "      dC[bc + n] += gy * hp[n];"),
+    ("dA without the decay factor", "      dA[d * d_state + n] += lam[n] * dt * et * hp[n];",
+     "      dA[d * d_state + n] += lam[n] * dt * hp[n];"),
     ("gate derivative without the z term",
-     "        if (dz) dz[e] = dout[e] * y * sg * (1.0 + zv * (1.0 - sg));",
-     "        if (dz) dz[e] = dout[e] * y * sg;"),
+     "      if (dz) dz[e] = dout[e] * y * sg * (1.0 + zv * (1.0 - sg));",
+     "      if (dz) dz[e] = dout[e] * y * sg;"),
     ("head reads the wrong group", "    int64_t b = r / nheads, h = r % nheads, g = h / hpg;",
      "    int64_t b = r / nheads, h = r % nheads, g = h % ngroups;"),
     ("multi-head decay after the input",
@@ -74,6 +74,16 @@ MUTATIONS = [
      "        for (int64_t n = 0; n < d_state; ++n) y += rd(C, bc + n, io_dtype) * hs[n * headdim + p] / decay;"),
     ("conv looks ahead", "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + ts) * d_inner + d, io_dtype);",
      "          if (ts >= 0)\n            xv = rd(x, (b * seqlen + (ts + 1 < seqlen ? ts + 1 : ts)) * d_inner + d, io_dtype);"),
+    ("exact-ZOH gradient ignores the gain", "      double g = bbar_factor(dt, a, zoh_exact);",
+     "      double g = dt;"),
+    ("exact-ZOH gain's dt derivative dropped", "      double g_dt = zoh_exact ? et : 1.0;",
+     "      double g_dt = 1.0;"),
+    ("exact-ZOH input term of dA dropped",
+     "      if (zoh_exact) dA[d * d_state + n] += lam[n] * zoh_gain_da(dt, a, et) * bn * x;\n", ""),
+    ("exact-ZOH dA limit at a = 0", "  if (a == 0.0) return 0.5 * dt * dt;", "  if (a == 0.0) return dt * dt;"),
+    ("summed gradient partial of one thread dropped",
+     "      for (int th = 0; th < nthreads; ++th) acc += part",
+     "      for (int th = 1; th < nthreads; ++th) acc += part"),
 ]
 
 PIN_CALLS = [
@@ -82,6 +92,9 @@ PIN_CALLS = [
     scan2_pins.test_group_sharing,
     lambda: bwd_pins.test_gradients_match_finite_differences(True),
     lambda: bwd_pins.test_gradients_match_finite_differences(False),
+    lambda: bwd_pins.test_exact_zoh_gradients_match_finite_differences(True),
+    bwd_pins.test_exact_zoh_gradient_at_zero_decay,
+    bwd_pins.test_summed_gradients_do_not_depend_on_thread_count,
     bwd_pins.test_decay_free_linear_closed_form,
     lambda: conv_pins.test_matches_numpy_convolution(4, False, True),
     lambda: conv_pins.test_matches_numpy_convolution(2, True, False),
