@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from selective_state_space_36_amd import workloads as wl
-from tests.helpers import TOL, check_close, dev, host
+from tests.helpers import TOL, check_close, check_every_row, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -143,19 +143,28 @@ def test_invalid_conv_arguments():
     assert e.value.status == o.SS_ERR_UNSUPPORTED
 
 
-def test_full_size_conv_sampled():
+def test_full_size_conv_every_row():
     """The 2.8B-shaped layer (batch 4, L 4096, d_inner 5120) through the front end, in the
-    launch configuration the benchmark uses, checked on sampled rows covering several channel
-    blocks and every batch row."""
+    launch configuration the benchmark uses, every row checked: the oracle runs the front end
+    and the scan on each block of channels (channels are independent)."""
     w_ = wl.WORKLOADS[2]
     p = wl.make_prefill(w_)
     w, b, xp = conv_params(np.random.default_rng(2), w_.d_inner, 4, "bf16", w_.batch)
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([
-        np.arange(0, 20), w_.d_inner - 20 + np.arange(40),
-        (w_.batch - 1) * w_.d_inner + np.arange(w_.d_inner - 20, w_.d_inner),
-        rng.integers(0, w_.batch * w_.d_inner, size=60)])).astype(np.int64)
-    g, gh, r, rh = run_conv(p, w, b, xp, rows=rows)
-    gsel = g.transpose(0, 2, 1).reshape(-1, w_.seqlen)[rows]
-    check_close(gsel, r, TOL["bf16"], "out (sampled rows)")
-    check_close(gh.reshape(-1, w_.d_state)[rows], rh, TOL["f32"], "h_last (sampled rows)")
+    print("  conv full size: GPU", flush=True)
+    out, h_last = ops().scan_fwd_conv(
+        dev(p["u"]), dev(w), dev(b), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"]),
+        D=dev(p["D"]), z=dev(p["z"]), delta_bias=dev(p["delta_bias"]), x_prev=dev(xp),
+        return_last_state=True)
+    torch.cuda.synchronize()
+
+    def reference(bi, d0, d1):
+        blk = lambda a: np.ascontiguousarray(a[bi:bi + 1, :, d0:d1])
+        u = oracle.conv_silu(blk(p["u"]), w[d0:d1], b[d0:d1], x_prev=blk(xp))
+        r, rh = oracle.scan_fwd(u, blk(p["delta"]), p["A"][d0:d1],
+                                np.ascontiguousarray(p["B"][bi:bi + 1]),
+                                np.ascontiguousarray(p["C"][bi:bi + 1]), D=p["D"][d0:d1],
+                                z=blk(p["z"]), delta_bias=p["delta_bias"][d0:d1])
+        return r[0].T, rh[0]
+
+    check_every_row(out, h_last, reference, "conv front end, 2.8B layer", out_tol=TOL["bf16"],
+                    h_tol=TOL["f32"])

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 from selective_state_space_36_amd import workloads as wl
-from tests.helpers import TOL, check_close, dev, host
+from tests.helpers import TOL, check_close, check_every_row, dev, host
 from tests.test_oracle_pins import _exact, _parse_golden
 
 pytestmark = pytest.mark.gpu
@@ -166,10 +166,9 @@ def test_hold_gain_elementwise_accuracy():
                                 f"{got[i]!r} want {want[i]!r} rel {rel[i]:.3g}")
 
 
-def test_full_size_zoh_sampled():
+def test_full_size_zoh_every_row():
     """The 2.8B-shaped layer (batch 4, L 4096, d_inner 5120, bf16, gate) under the exact hold, in
-    the launch configuration the benchmark times: sampled rows against the oracle."""
-    from tests.test_gpu_scan import _sample_rows
+    the launch configuration the benchmark times: every row against the oracle."""
     w = wl.WORKLOADS[2]
     print(f"  generating {w.name} ...", flush=True)
     p = wl.make_prefill(w)
@@ -179,16 +178,13 @@ def test_full_size_zoh_sampled():
                                  delta_bias=dev(p["delta_bias"]), return_last_state=True,
                                  zoh_exact=True)
     torch.cuda.synchronize()
-    rows = _sample_rows(w.batch, w.d_inner, 16, seed=5)
-    b_idx, d_idx = rows // w.d_inner, rows % w.d_inner
-    g = host(out[torch.from_numpy(b_idx).cuda(), :, torch.from_numpy(d_idx).cuda()])
-    gh = host(h_last.reshape(-1, w.d_state)[torch.from_numpy(rows).cuda()])
-    del out, h_last
-    print(f"  oracle on {len(rows)} rows x {w.seqlen} steps ...", flush=True)
-    r, rh = oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
-                            delta_bias=p["delta_bias"], zoh_exact=True, rows=rows)
-    check_close(g, r, TOL["bf16"], f"{w.name} exact-hold out")
-    check_close(gh, rh, TOL["f32"], f"{w.name} exact-hold h_last")
+    check_every_row(
+        out, h_last,
+        lambda b, d0, d1: oracle.scan_fwd(
+            p["u"], p["delta"], p["A"], p["B"], p["C"], D=p["D"], z=p["z"],
+            delta_bias=p["delta_bias"], zoh_exact=True,
+            rows=(b * w.d_inner + np.arange(d0, d1)).astype(np.int64)),
+        f"{w.name} exact hold", out_tol=TOL["bf16"], h_tol=TOL["f32"])
 
 
 def test_decode_zoh_matches_oracle_and_prefill():
