@@ -23,7 +23,8 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers owned by the caller; arrays are contiguous and row-major.
- *     The library allocates no device memory and keeps no state between calls.
+ *     The library allocates no device memory and keeps no state between calls (the one
+ *     exception: the static scratch array of ss_scan_fwd_noalloc, described there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only enqueue
  *     work and return; they never synchronise, print or throw.
  *   - Argument errors are detected before anything is launched and leave all outputs untouched.
@@ -95,6 +96,32 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
 /* Workspace bytes ss_scan_fwd can use for this shape (0 when it would not split in time). */
 size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                    int64_t d_state, ss_dtype dtype);
+
+/*
+ * Prefill that allocates nothing, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The same operation,
+ * arguments and results as ss_scan_fwd, without the workspace: when the automatic time split
+ * is used (shapes with few channels and long sequences), its segment end states and step sums
+ * live in a static device array of SS_NOALLOC_SCRATCH_BYTES bytes inside the library, one per
+ * GPU, held from its first use on that GPU until the process ends.
+ *   - The array of the calling thread's current device is used; `stream` must belong to that
+ *     device.  Its address is looked up once per device (hipGetSymbolAddress) and cached.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ *     different streams, or from several threads) race on it and give wrong results.  Calls
+ *     ordered on one stream are safe; nothing in the array needs to start at zero.
+ *   - 1 MiB holds the automatic split of every shape with d_state <= 16 on a 256-CU MI355X
+ *     (the split targets about 3 waves per SIMD, so its carries stay below 12288 rows of
+ *     d_state + 1 floats).  A shape whose split needs more (d_state above 16 with few channels
+ *     and long sequences) -> SS_ERR_INVALID_ARG before any launch; ss_scan_fwd with a workspace
+ *     takes every shape.
+ *   - No hipMalloc, hipFree or other allocating call is made.
+ */
+#define SS_NOALLOC_SCRATCH_BYTES (1u << 20)
+ss_status ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                              const void* C, const float* D, const void* z,
+                              const float* delta_bias, int delta_softplus, const float* h0,
+                              float* h_last, void* out, int64_t batch, int64_t seqlen,
+                              int64_t d_inner, int64_t d_state, ss_dtype dtype, void* stream);
 
 /*
  * Prefill with an explicit time split and options.  nseg > 0 forces the sequence to be cut into

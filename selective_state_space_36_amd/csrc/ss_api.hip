@@ -8,11 +8,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ss_scan.h"
 #include "ss_bwd.h"
 #include "ss_launch.h"
 #include "ss_scan2.h"
+
+// Scratch of ss_scan_fwd_noalloc: the time split's segment end states and step sums.  Each GPU
+// holds its own copy from the library's first use on it until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in); it uses the device address
+// looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[SS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -50,6 +57,31 @@ bool overlap(const Range& a, const Range& b) {
 }
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of the current device's copy of `scratch`, looked up on first use.
+ss_status static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SS_ERR_UNSUPPORTED, "device %d above the %d devices the static scratch serves",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SS_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return SS_OK;
+}
 
 int cu_count() {
   int dev = 0, n = 0;
@@ -110,7 +142,8 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
                     void* workspace, size_t workspace_bytes, int32_t nseg_req, bool forced,
                     uint32_t flags, void* stream, const float* conv_w = nullptr,
                     const float* conv_b = nullptr, const void* x_prev = nullptr,
-                    int32_t conv_k = 0, float* states = nullptr) {
+                    int32_t conv_k = 0, float* states = nullptr,
+                    bool use_static_scratch = false) {
   int64_t es = 0;
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (check_flags(flags) != SS_OK) return SS_ERR_UNSUPPORTED;
@@ -204,6 +237,19 @@ ss_status scan_impl(const void* u, const void* delta, const float* A, const void
                   "needed for nseg=%d", workspace_bytes, ws_bytes(batch, d_inner, d_state, nseg),
                   nseg);
   } else {
+    if (use_static_scratch) {
+      // the allocation-free entry point: the automatic split must fit the static scratch
+      const size_t need = ws_bytes(batch, d_inner, d_state, nseg);
+      if (need > SS_NOALLOC_SCRATCH_BYTES)
+        return fail(SS_ERR_INVALID_ARG, "the time split of this shape needs %zu bytes of "
+                    "scratch, above the %u bytes of ss_scan_fwd_noalloc's static scratch (use "
+                    "ss_scan_fwd with a workspace)", need, SS_NOALLOC_SCRATCH_BYTES);
+      if (nseg > 1) {
+        const ss_status s = static_scratch(&workspace);
+        if (s != SS_OK) return s;
+        workspace_bytes = SS_NOALLOC_SCRATCH_BYTES;
+      }
+    }
     // split only as far as the workspace allows
     while (nseg > 1 && (!workspace || ws_bytes(batch, d_inner, d_state, nseg) > workspace_bytes)) {
       want = std::max<int32_t>(1, want / 2);
@@ -548,6 +594,16 @@ ss_status ss_scan_fwd(const void* u, const void* delta, const float* A, const vo
   return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
                    seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, 0, false, 0,
                    stream);
+}
+
+ss_status ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                              const void* C, const float* D, const void* z,
+                              const float* delta_bias, int delta_softplus, const float* h0,
+                              float* h_last, void* out, int64_t batch, int64_t seqlen,
+                              int64_t d_inner, int64_t d_state, ss_dtype dtype, void* stream) {
+  return scan_impl(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, h_last, out, batch,
+                   seqlen, d_inner, d_state, dtype, nullptr, 0, 0, false, 0, stream, nullptr,
+                   nullptr, nullptr, 0, nullptr, /*use_static_scratch=*/true);
 }
 
 size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,

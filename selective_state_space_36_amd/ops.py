@@ -27,6 +27,8 @@ SIGNATURES = {
     "ss_scan_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                            _i64, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "ss_scan_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
+    "ss_scan_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                   _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp]),
     "ss_scan_fwd_ex": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
                               _vp, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32, _u32, _vp]),
     "ss_scan_fwd_ex_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
@@ -168,6 +170,33 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
         flags = SS_FLAG_ZOH_EXACT if zoh_exact else 0
         _check(lib().ss_scan_fwd_ex(*args, int(nseg or 0), flags, _stream(stream)))
     return (out, h_last) if return_last_state else out
+
+
+def scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                     h0=None, out=None, h_last=None, stream=None):
+    """Prefill through ss_scan_fwd_noalloc: the library allocates nothing and the time split,
+    when used, keeps its carries in the library's static per-GPU scratch.  out (and h_last, if
+    wanted) must be given: this call allocates nothing either.  Returns out."""
+    batch, L, d_inner = u.shape
+    d_state = B.shape[-1]
+    code = _dtype_code(u)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        _dev(t, name, u.dtype, (batch, L, d_inner))
+    for name, t in (("B", B), ("C", C)):
+        _dev(t, name, u.dtype, (batch, L, d_state))
+    _dev(A, "A", torch.float32, (d_inner, d_state))
+    _dev(D, "D", torch.float32, (d_inner,))
+    _dev(delta_bias, "delta_bias", torch.float32, (d_inner,))
+    _dev(h0, "h0", torch.float32, (batch, d_inner, d_state))
+    if out is None:
+        raise ValueError("scan_fwd_noalloc: out must be given")
+    _dev(out, "out", u.dtype, (batch, L, d_inner))
+    _dev(h_last, "h_last", torch.float32, (batch, d_inner, d_state))
+    _check(lib().ss_scan_fwd_noalloc(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        1 if delta_softplus else 0, _ptr(h0), _ptr(h_last), _ptr(out), batch, L, d_inner,
+        d_state, code, _stream(stream)))
+    return out
 
 
 def scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -177,3 +177,28 @@ def test_saved_states_argument_errors_before_launch(lib):
     assert rc == ops.SS_ERR_UNSUPPORTED and b"flag" in lib.ss_last_error()
     assert _bwd(lib, flags=ops.SS_FLAG_STATES_GIVEN, dout=None) == ops.SS_ERR_INVALID_ARG
     assert _bwd(lib, flags=ops.SS_FLAG_STATES_GIVEN, ws=None, wsb=0) == ops.SS_ERR_INVALID_ARG
+
+
+def _noalloc(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE * 2, A=FAKE * 3, B=FAKE * 4, C=FAKE * 5, D=None, z=None,
+             bias=None, sp=1, h0=None, hl=None, out=FAKE * 6, batch=1, L=4, d=8, N=16,
+             dtype=ops.SS_BF16)
+    a.update(kw)
+    return lib.ss_scan_fwd_noalloc(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                   a["bias"], a["sp"], a["h0"], a["hl"], a["out"], a["batch"],
+                                   a["L"], a["d"], a["N"], a["dtype"], None)
+
+
+def test_noalloc_argument_errors_before_launch(lib):
+    """The allocation-free prefill validates like ss_scan_fwd, and rejects a shape whose time
+    split would need more than its static scratch (d_state 64, 16 channels, 2^20 steps) before
+    touching the GPU."""
+    assert _noalloc(lib, N=0) == ops.SS_ERR_UNSUPPORTED
+    assert _noalloc(lib, u=None) == ops.SS_ERR_INVALID_ARG
+    assert _noalloc(lib, out=FAKE) == ops.SS_ERR_INVALID_ARG
+    assert _noalloc(lib, batch=0) == ops.SS_OK
+    big = 1 << 20
+    st = _noalloc(lib, u=1 << 40, delta=2 << 40, A=3 << 40, B=4 << 40, C=5 << 40, out=6 << 40,
+                  L=big, d=16, N=64)
+    assert st == ops.SS_ERR_INVALID_ARG
+    assert b"static scratch" in lib.ss_last_error()
