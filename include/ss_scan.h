@@ -109,14 +109,14 @@ size_t ss_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inne
  *   - Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
  *     different streams, or from several threads) race on it and give wrong results.  Calls
  *     ordered on one stream are safe; nothing in the array needs to start at zero.
- *   - 1 MiB holds the automatic split of every shape with d_state <= 16 on a 256-CU MI355X
- *     (the split targets about 3 waves per SIMD, so its carries stay below 12288 rows of
- *     d_state + 1 floats).  A shape whose split needs more (d_state above 16 with few channels
- *     and long sequences) -> SS_ERR_INVALID_ARG before any launch; ss_scan_fwd with a workspace
- *     takes every shape.
+ *   - 8 MiB holds the automatic split of every shape with d_state <= 16 on a 256-CU MI355X
+ *     (the split targets about 24 waves per SIMD with 4 channels per wave, so its carries stay
+ *     below 98304 rows of d_state + 1 floats, 6.7 MB).  A shape whose split needs more (d_state
+ *     above 16 with few channels and long sequences) -> SS_ERR_INVALID_ARG before any launch;
+ *     ss_scan_fwd with a workspace takes every shape.
  *   - No hipMalloc, hipFree or other allocating call is made.
  */
-#define SS_NOALLOC_SCRATCH_BYTES (1u << 20)
+#define SS_NOALLOC_SCRATCH_BYTES (8u << 20)
 ss_status ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
                               const void* C, const float* D, const void* z,
                               const float* delta_bias, int delta_softplus, const float* h0,

@@ -50,6 +50,14 @@ struct ScanArgs {
   int64_t states_chunks;  // ceil(seqlen / kChunk)
 };
 
+// Batch rows each thread of the decode step's vector path walks (a group of rows of the state
+// is addressed with 32-bit byte offsets, so the host admits that path only when kDecodeRows
+// rows of the state stay under 2^31 bytes).
+#ifndef SS_DECODE_ROWS
+#define SS_DECODE_ROWS 4
+#endif
+constexpr int kDecodeRows = SS_DECODE_ROWS;
+
 struct DecodeArgs {
   float* state;
   const void* u;

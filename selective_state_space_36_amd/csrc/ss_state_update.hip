@@ -11,9 +11,9 @@
 // The step is bound by memory: every state element is read once and written once, with a
 // handful of operations each.  Layout: each channel's d_state floats are split over a
 // power-of-two group of lanes, 4 consecutive states per lane, so that a wave reads and writes one
-// contiguous run of the state with 16-byte accesses.  Each thread handles several such 4-state
-// items and issues all their loads before any arithmetic, to keep enough bytes in flight to cover
-// the memory latency.  The group reduces C . h with cross-lane DPP adds; its first lane finishes
+// contiguous run of the state with 16-byte accesses.  Each thread handles its 4-state slice in
+// several batch rows and issues all their loads before any arithmetic, to keep enough bytes in
+// flight to cover the memory latency.  The group reduces C . h with cross-lane DPP adds; its first lane finishes
 // the element (skip, gate, store).  Address arithmetic is kept to a few 32-bit operations per
 // item: with this little work per byte, index math alone would otherwise bound the kernel.
 #include <hip/hip_runtime.h>
@@ -64,14 +64,20 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Vector path: d_state % 4 == 0, 16-byte aligned state and A, d_inner * d_state < 2^29.
-// Grid: x over the lanes of one batch row (G lanes per channel, 4 consecutive states per lane),
-// y over batch rows (strided when batch exceeds the grid).  Every array is addressed as a raw
-// buffer based at the row (scalar registers) with 32-bit lane offsets, so the index math is a
-// few shifts, and lanes past the row get an offset beyond every range: their loads return 0 and
-// their stores are dropped by the hardware range check.  Each thread takes ITEMS lanes 256
-// apart and issues all their loads before any arithmetic.
-template <class IO, bool GATE, bool ZOH, bool CONV, int G, int ITEMS>
+// Vector path: d_state % 4 == 0, 16-byte aligned state and A, and a group of BI batch rows of
+// the state under 2^31 bytes.  Grid: x over the lanes of one batch row (G lanes per channel, 4
+// consecutive states per lane), y over groups of BI batch rows (strided when there are more
+// groups than the grid holds).  A thread keeps one (channel, 4-state slice) and walks the BI rows
+// of its group: the channel's A, bias and D are loaded once for all of them (A's 16 bytes per
+// lane were as much L2 traffic as the state itself), and the BI rows' state loads are all issued
+// before the thread needs any row's u, delta or z.  When those inputs sit on pages the GPU has
+// not translated yet (a decode loop reading each step's inputs from fresh memory), the first
+// vector access to such a page stalls the CU's memory pipeline for a page-table walk; with
+// several rows per thread more of the state stream is already in flight when it does.
+// Arrays are raw buffers based at the group's first row with 32-bit lane offsets; lanes past the
+// row and rows past the batch get offsets beyond every range, so their loads return 0 and their
+// stores are dropped by the hardware range check.
+template <class IO, bool GATE, bool ZOH, bool CONV, int G, int BI>
 __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs a) {
   using elem = typename IO::elem;
   using raw4 = typename Vec4In<IO>::raw;  // four io elements
@@ -81,10 +87,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
   static_assert((1 << LOG_G) == G && G <= 16, "lanes per channel");
   const int N = a.d_state;
   const int D = static_cast<int>(a.d_inner);
-  const uint32_t st_bytes = static_cast<uint32_t>(D) * N * 4;
+  const uint32_t st_bytes = static_cast<uint32_t>(D) * N * 4;  // one batch row of the state
   const rsrc_t rA = make_buf(a.A, st_bytes);
-  const rsrc_t rbias = make_buf(a.delta_bias, a.delta_bias ? D * 4u : 0u);
-  const rsrc_t rD = make_buf(a.D, a.D ? D * 4u : 0u);
 
   // Per-channel inputs.  With G >= 4 the four lanes of a quad (one channel) split them: lane 0
   // of the quad loads u, lane 1 delta, lane 2 z, and lanes 0/1 also delta_bias/D; DPP quad
@@ -104,98 +108,104 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
   const float* f_src = qq == 0 ? a.delta_bias : ((CONV && qq == 2) ? a.conv_b : a.D);
   const bool f_ok = f_src != nullptr;
   const float* f_base = f_ok ? f_src : a.A;  // any valid address; the value is then zeroed
-  uint32_t so[ITEMS], io[ITEMS], fo[ITEMS], bo[ITEMS], oo[ITEMS];
-  uint32_t dcl[ITEMS];  // channel clamped into the row
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const uint32_t l = (blockIdx.x * ITEMS + i) * kDecodeThreads + threadIdx.x;
-    const uint32_t d = l >> LOG_G, q = l & (G - 1);
-    const bool act = d < static_cast<uint32_t>(D) && q * 4 < static_cast<uint32_t>(N);
-    dcl[i] = d < static_cast<uint32_t>(D) ? d : D - 1;
-    so[i] = act ? (d * N + q * 4) * 4 : kOffNone;  // state and A
-    io[i] = act ? d * ES : kOffNone;                // u, delta, z
-    fo[i] = act ? d * 4 : kOffNone;                 // delta_bias, D
-    bo[i] = act ? q * 4 * ES : kOffNone;            // B, C
-    oo[i] = act && q == 0 ? d * ES : kOffNone;      // out (first lane of the group)
+
+  const uint32_t l = blockIdx.x * kDecodeThreads + threadIdx.x;  // lane within a batch row
+  const uint32_t d = l >> LOG_G, q = l & (G - 1);
+  const bool act = d < static_cast<uint32_t>(D) && q * 4 < static_cast<uint32_t>(N);
+  const uint32_t dcl = d < static_cast<uint32_t>(D) ? d : D - 1;  // channel clamped into the row
+  const uint32_t so = act ? (d * N + q * 4) * 4 : kOffNone;       // state and A, within a row
+  const uint32_t io = act ? d * ES : kOffNone;                    // u, delta, z, within a row
+  const uint32_t bo = act ? q * 4 * ES : kOffNone;                // B, C, within a row
+  const uint32_t oo = act && q == 0 ? d * ES : kOffNone;          // out (first lane of the group)
+
+  // the channel's own values, shared by the rows of every group
+  const float4 av = buf_load<float4>(rA, so);
+  float fv = 0.0f, bias_c = 0.0f, dsk_c = 0.0f, wt = 0.0f;
+  if (QUAD) {
+    fv = f_base[dcl];  // delta_bias, D or the conv bias by lane of the quad
+  } else {
+    const uint32_t fo = act ? d * 4 : kOffNone;
+    bias_c = buf_load<float>(make_buf(a.delta_bias, a.delta_bias ? D * 4u : 0u), fo);
+    dsk_c = buf_load<float>(make_buf(a.D, a.D ? D * 4u : 0u), fo);
+  }
+  const int K = CONV ? a.conv_k : 0;
+  const int jw = qq - (4 - K);  // this lane's window slot as a tap index (< 0: unused)
+  if (CONV) {                   // tap weight (unused slots: a valid address, the value zeroed)
+    const float wv = a.conv_w[int64_t(dcl) * K + (jw >= 0 ? jw : 0)];
+    wt = jw >= 0 ? wv : 0.0f;
   }
 
-  for (int64_t b = blockIdx.y; b < a.batch; b += gridDim.y) {
-    const rsrc_t rs = make_buf(a.state + b * D * N, st_bytes);
-    const rsrc_t ru = make_buf(static_cast<const elem*>(a.u) + b * D, D * ES);
-    const rsrc_t rd = make_buf(static_cast<const elem*>(a.delta) + b * D, D * ES);
-    const rsrc_t rz = make_buf(GATE ? static_cast<const elem*>(a.z) + b * D : nullptr,
-                               GATE ? D * ES : 0u);
-    const rsrc_t rB = make_buf(static_cast<const elem*>(a.B) + b * N, N * ES);
-    const rsrc_t rC = make_buf(static_cast<const elem*>(a.C) + b * N, N * ES);
-    const rsrc_t ro = make_buf(static_cast<elem*>(a.out) + b * D, D * ES);
-    float4 hv[ITEMS], av[ITEMS];
-    raw4 bv[ITEMS], cv[ITEMS];
-    elem xr[ITEMS], dr[ITEMS], zr[ITEMS], wn[ITEMS];
-    float bias[ITEMS], dsk[ITEMS], wt[ITEMS];
-    const int K = CONV ? a.conv_k : 0;
-    const int jw = qq - (4 - K);  // this lane's window slot as a tap index (< 0: unused)
+  for (int64_t b0 = int64_t(blockIdx.y) * BI; b0 < a.batch; b0 += int64_t(gridDim.y) * BI) {
+    const int nb = a.batch - b0 < BI ? static_cast<int>(a.batch - b0) : BI;
+    const rsrc_t rs = make_buf(a.state + b0 * D * N, nb * st_bytes);
+    const rsrc_t rB = make_buf(static_cast<const elem*>(a.B) + b0 * N, nb * N * ES);
+    const rsrc_t rC = make_buf(static_cast<const elem*>(a.C) + b0 * N, nb * N * ES);
+    const rsrc_t ro = make_buf(static_cast<elem*>(a.out) + b0 * D, nb * D * ES);
+    const uint32_t xb = QUAD ? 0u : nb * D * ES;
+    const rsrc_t ru = make_buf(QUAD ? nullptr : static_cast<const elem*>(a.u) + b0 * D, xb);
+    const rsrc_t rd = make_buf(QUAD ? nullptr : static_cast<const elem*>(a.delta) + b0 * D, xb);
+    const rsrc_t rz = make_buf(QUAD || !GATE ? nullptr : static_cast<const elem*>(a.z) + b0 * D,
+                               QUAD || !GATE ? 0u : xb);
+    float4 hv[BI];
+    raw4 bv[BI], cv[BI];
+    elem xr[BI], dr[BI], zr[BI], wn[BI];
+    // the state stream first: every row's 16 bytes in flight before any narrow input returns
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      if (CONV) {  // window element and tap weight of this lane (unused slots: valid
-                   // addresses, values zeroed, so the loads need no branch)
+    for (int i = 0; i < BI; ++i) hv[i] = buf_load<float4>(rs, so + i * st_bytes);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int64_t bi = b0 + (i < nb ? i : nb - 1);  // row clamped into the batch
+      bv[i] = buf_load<raw4>(rB, bo + i * N * ES);
+      cv[i] = buf_load<raw4>(rC, bo + i * N * ES);
+      if (CONV) {  // window element of this lane (unused slots: a valid address, value zeroed)
         const bool from_x = qq == 3 || jw < 0;
-        const elem* src = from_x ? static_cast<const elem*>(a.u) + b * D + dcl[i]
+        const elem* src = from_x ? static_cast<const elem*>(a.u) + bi * D + dcl
                                  : static_cast<const elem*>(a.conv_state) +
-                                       (b * (K - 1) + jw) * D + dcl[i];
+                                       (bi * (K - 1) + jw) * D + dcl;
         const elem v = *src;
-        const float wv = a.conv_w[int64_t(dcl[i]) * K + (jw >= 0 ? jw : 0)];
         wn[i] = jw >= 0 ? v : elem{};
-        wt[i] = jw >= 0 ? wv : 0.0f;
       }
-      hv[i] = buf_load<float4>(rs, so[i]);
-      av[i] = buf_load<float4>(rA, so[i]);
-      bv[i] = buf_load<raw4>(rB, bo[i]);
-      cv[i] = buf_load<raw4>(rC, bo[i]);
       if (QUAD) {
-        xr[i] = aux_base[b * D + dcl[i]];  // u, delta or z by lane of the quad
-        bias[i] = f_base[dcl[i]];          // delta_bias or D by lane of the quad
+        xr[i] = aux_base[bi * D + dcl];  // u, delta or z by lane of the quad
       } else {
-        xr[i] = buf_load<elem>(ru, io[i]);
-        dr[i] = buf_load<elem>(rd, io[i]);
-        if (GATE) zr[i] = buf_load<elem>(rz, io[i]);
-        bias[i] = buf_load<float>(rbias, fo[i]);
-        dsk[i] = buf_load<float>(rD, fo[i]);
+        xr[i] = buf_load<elem>(ru, io + i * D * ES);
+        dr[i] = buf_load<elem>(rd, io + i * D * ES);
+        if (GATE) zr[i] = buf_load<elem>(rz, io + i * D * ES);
       }
     }
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
+    for (int i = 0; i < BI; ++i) {
       float x, s, zv = 0.0f, dskip;
       if (CONV) {
         const float w = IO::widen(xr[i]);
-        const float f = f_ok ? bias[i] : 0.0f;
+        const float f = f_ok ? fv : 0.0f;
         const float win = IO::widen(wn[i]);
-        x = silu_f(group_sum<4>(wt[i] * win) + quad_bcast<2>(f));
+        x = silu_f(group_sum<4>(wt * win) + quad_bcast<2>(f));
         s = quad_bcast<0>(w) + quad_bcast<0>(f);
         if (GATE) zv = quad_bcast<1>(w);
         dskip = quad_bcast<1>(f);
         // shift the window: slot j of the new state is the old slot j + 1 (the last one is x);
-        // the first quad of the channel writes
+        // the first quad of the channel writes, for rows inside the batch
         const int pos = jw - 1;
-        const uint32_t l = (blockIdx.x * ITEMS + i) * kDecodeThreads + threadIdx.x;
-        if (pos >= 0 && (l & (G - 1)) < 4 && (l >> LOG_G) < static_cast<uint32_t>(D))
-          static_cast<elem*>(a.conv_state)[(b * (K - 1) + pos) * D + dcl[i]] = wn[i];
+        if (pos >= 0 && (l & (G - 1)) < 4 && d < static_cast<uint32_t>(D) && i < nb)
+          static_cast<elem*>(a.conv_state)[((b0 + i) * (K - 1) + pos) * D + dcl] = wn[i];
       } else if (QUAD) {
         const float w = IO::widen(xr[i]);
-        const float f = f_ok ? bias[i] : 0.0f;
+        const float f = f_ok ? fv : 0.0f;
         x = quad_bcast<0>(w);
         s = quad_bcast<1>(w) + quad_bcast<0>(f);
         if (GATE) zv = quad_bcast<2>(w);
         dskip = quad_bcast<1>(f);
       } else {
         x = IO::widen(xr[i]);
-        s = IO::widen(dr[i]) + bias[i];
+        s = IO::widen(dr[i]) + bias_c;
         if (GATE) zv = IO::widen(zr[i]);
-        dskip = dsk[i];
+        dskip = dsk_c;
       }
       const float dt = a.softplus ? softplus_f(s) : s;
       const float du = dt * x;
       float hh[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
-      const float aa[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+      const float aa[4] = {av.x, av.y, av.z, av.w};
       float p = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -205,11 +215,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_vec4_kernel(DecodeArgs 
         hh[j] = fmaf(e, hh[j], ZOH ? inc * (zoh_gain(e, y) * (1.0f / kLn2)) : inc);
         p = fmaf(V::get(cv[i], j), hh[j], p);  // inactive lanes: C reads 0, p stays 0
       }
-      buf_store(make_float4(hh[0], hh[1], hh[2], hh[3]), rs, so[i]);
+      buf_store(make_float4(hh[0], hh[1], hh[2], hh[3]), rs, so + i * st_bytes);
       p = group_sum<G>(p);
       float y = fmaf(dskip, x, p);
       if (GATE) y *= silu_f(zv);
-      buf_store(IO::from_float(y), ro, oo[i]);
+      buf_store(IO::from_float(y), ro, oo + i * D * ES);
     }
   }
 }
@@ -260,15 +270,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(DecodeAr
   }
 }
 
-constexpr int kItems = 1;
-
 template <class IO, bool GATE, bool ZOH, int G, bool CONV = false>
 void launch_vec(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t per_block = int64_t(kDecodeThreads) * kItems;
   const int64_t row_lanes = a.d_inner * G;
-  const dim3 grid(static_cast<unsigned>((row_lanes + per_block - 1) / per_block),
-                  static_cast<unsigned>(a.batch < 65535 ? a.batch : 65535));
-  hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, CONV, G, kItems>), grid,
+  const int64_t groups = (a.batch + kDecodeRows - 1) / kDecodeRows;
+  const dim3 grid(static_cast<unsigned>((row_lanes + kDecodeThreads - 1) / kDecodeThreads),
+                  static_cast<unsigned>(groups < 65535 ? groups : 65535));
+  hipLaunchKernelGGL((decode_vec4_kernel<IO, GATE, ZOH, CONV, G, kDecodeRows>), grid,
                      dim3(kDecodeThreads), 0, stream, a);
 }
 
