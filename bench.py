@@ -266,20 +266,20 @@ def bench_variants(args, torch, np, ops, pf, stream):
     bsteps = max(3, args.steps // 10)
     ms_bwd, _ = timed(torch, stream, run_bwd, 5, bsteps, per_launch=False)
     del ws_b
-    st_buf = torch.empty((w.batch, (w.seqlen + 15) // 16, w.d_inner, w.d_state),
-                         dtype=torch.float32, device="cuda")
+    ws_t, st_buf = ops.bwd_workspace(w.batch, w.seqlen, w.d_inner, w.d_state, g["u"].dtype)
     st_out = torch.empty_like(g["u"])
     fwd_s = lambda: ops.scan_fwd_states(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"],
                                         z=g["z"], delta_bias=g["delta_bias"], out=st_out,
                                         states=st_buf, workspace=pf.ws, stream=stream)
     bwd_s = lambda: ops.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dout, D=g["D"],
-                                 z=g["z"], delta_bias=g["delta_bias"], states=st_buf,
-                                 stream=stream)
+                                 z=g["z"], delta_bias=g["delta_bias"], workspace=ws_t,
+                                 states_given=True, stream=stream)
     ms_fs, _ = timed(torch, stream, fwd_s, 5, bsteps, per_launch=False)
     ms_bs, _ = timed(torch, stream, bwd_s, 5, bsteps, per_launch=False)
-    del st_buf, st_out
+    del ws_t, st_buf, st_out
     nb = backward_bytes(w)
     ck = 2 * w.batch * ((w.seqlen + 15) // 16) * w.d_inner * w.d_state * 4
+    part = 2 * w.batch * ((w.seqlen + 15) // 16) * ((w.d_inner + 15) // 16) * 16 * 16 * 2 * 4
     res["backward"] = {
         "us_per_call": round(ms_bwd * 1e3, 2),
         "elements_per_s": round(w.elements / (ms_bwd * 1e-3), 1),
@@ -287,10 +287,12 @@ def bench_variants(args, torch, np, ops, pf, stream):
                      "achieved": round(nb / (ms_bwd * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(nb / (ms_bwd * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                      "traffic": measured_traffic("mamba2.8b-backward"),
-                     "checkpoint_bytes": ck,
+                     "checkpoint_bytes": ck, "partial_sum_bytes": part,
                      "note": "algorithmic bytes: inputs read and gradients written once; the "
                              "chunk-end states the recompute design writes and reads back "
-                             "(checkpoint_bytes) are not in them"},
+                             "(checkpoint_bytes) and the per-workgroup partial sums of dB and "
+                             "dC written and read back for a fixed-order sum "
+                             "(partial_sum_bytes) are not in them"},
         "note": "ss_scan_bwd (forward pass storing chunk-end states + reverse pass "
                 "recomputing each chunk), all input gradients",
         "with_saved_states": {

@@ -61,8 +61,8 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
  *     (exp(dt A[d,n]) - 1) / A[d,n] * B[n], and dt * B[n] where A[d,n] == 0) in place of the
  *     first-order dt * B[n] of the default (aivaro.ru, section 3).  A_bar = exp(dt A) either
  *     way.  It costs a few more operations per state update.
- *   SS_FLAG_STATES_GIVEN (ss_scan_bwd only): the workspace already holds the chunk-end states
- *     of these inputs, as written by ss_scan_fwd_states; the backward then skips its own
+ *   SS_FLAG_STATES_GIVEN (ss_scan_bwd only): the workspace already begins with the chunk-end
+ *     states of these inputs, as written by ss_scan_fwd_states; the backward then skips its own
  *     forward pass.
  */
 enum { SS_FLAG_ZOH_EXACT = 1, SS_FLAG_STATES_GIVEN = 2 };
@@ -149,8 +149,10 @@ size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_i
  *   states : (batch, ceil(seqlen / 16), d_inner, d_state) float32, written: states[b,c,d,:] is
  *            the state after step min(16 c + 15, seqlen - 1).  Caller-owned, of
  *            ss_scan_fwd_states_bytes() bytes; it must not overlap the inputs, out, h_last or
- *            the workspace.  With d_state <= 16 it is exactly the workspace ss_scan_bwd takes
- *            with SS_FLAG_STATES_GIVEN.
+ *            the workspace.  With d_state <= 16 it is exactly the first part of the workspace
+ *            ss_scan_bwd takes with SS_FLAG_STATES_GIVEN: a training step points `states` at the
+ *            start of a buffer of ss_scan_bwd_workspace_bytes() bytes and passes that buffer to
+ *            the backward.
  */
 ss_status ss_scan_fwd_states(const void* u, const void* delta, const float* A, const void* B,
                              const void* C, const float* D, const void* z,
@@ -235,13 +237,16 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
  *   dD, ddelta_bias   : (d_inner) float32, overwritten when non-NULL (the gradient at the given
  *                       D / bias, also when D or delta_bias is NULL, i.e. 0).
  *   dh0               : (batch, d_inner, d_state) float32, written when non-NULL.
- *   workspace         : device scratch of ss_scan_bwd_workspace_bytes() bytes (the chunk-end
- *                       states, (batch, ceil(seqlen / 16), d_inner, d_state) floats), required
- *                       when that is non-zero; SS_ERR_INVALID_ARG if smaller.  Without
- *                       SS_FLAG_STATES_GIVEN the call first writes them there with a forward
- *                       pass (a launch of its own on the stream), then runs the reverse pass.
- * dA, dB, dC, dD and ddelta_bias are sums formed with float atomics: they are reproducible up
- * to rounding order only.  d_state above 16 and SS_FLAG_ZOH_EXACT -> SS_ERR_UNSUPPORTED.
+ *   workspace         : 16-byte aligned device scratch of ss_scan_bwd_workspace_bytes() bytes,
+ *                       required when that is non-zero (SS_ERR_INVALID_ARG if smaller): first
+ *                       the chunk-end states, (batch, ceil(seqlen / 16), d_inner, d_state)
+ *                       floats, then the partial sums of dB and dC per 16-channel block and of
+ *                       dA, dD, ddelta_bias per batch row.  Without SS_FLAG_STATES_GIVEN the
+ *                       call first writes the states there with a forward pass (a launch of its
+ *                       own on the stream), then runs the reverse pass and two reductions.
+ * dA, dB, dC, dD and ddelta_bias are sums over channels or batch rows: each workgroup writes its
+ * partial sum and a second kernel adds the partials in a fixed order, so every output is
+ * bit-for-bit reproducible.  d_state above 16 and SS_FLAG_ZOH_EXACT -> SS_ERR_UNSUPPORTED.
  * Outputs must not overlap inputs, each other or the workspace.
  */
 ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
@@ -254,9 +259,9 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
                       void* stream);
 
 /* Workspace bytes ss_scan_bwd needs for this shape (0 for an empty problem or d_state > 16).
- * With flags SS_FLAG_STATES_GIVEN the workspace is read, not written: it must hold the states
- * ss_scan_fwd_states wrote for the same u, delta, A, B, delta_bias, delta_softplus, h0, sizes
- * and dtype (C, D and z do not enter the states). */
+ * With flags SS_FLAG_STATES_GIVEN the states part of the workspace is read, not written: it
+ * must hold the states ss_scan_fwd_states wrote for the same u, delta, A, B, delta_bias,
+ * delta_softplus, h0, sizes and dtype (C, D and z do not enter the states). */
 size_t ss_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
                                    int64_t d_state, ss_dtype dtype);
 

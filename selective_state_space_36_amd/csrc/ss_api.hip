@@ -396,12 +396,15 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
   return ok();
 }
 
+// Backward workspace: the chunk-end states, then the per-workgroup partial sums of dB, dC and
+// the per-batch-row partials of dA, dD, ddelta_bias (ss::bwd_layout).  0 for an empty problem
+// (nothing to sum) or an unsupported d_state.
 size_t bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
   if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 16) return 0;
   const int64_t nchunks = (seqlen + ss::kBwdChunk - 1) / ss::kBwdChunk;
-  int64_t n;
-  if (!mul_ok(batch * d_inner, nchunks, &n) || !mul_ok(n, d_state * 4, &n)) return 0;
-  return static_cast<size_t>(n);
+  int64_t n;  // a bound on every term of the layout, in bytes
+  if (!mul_ok(batch * (d_inner + 16), nchunks + 1, &n) || !mul_ok(n, 48 * 8, &n)) return 0;
+  return ss::bwd_layout(batch, seqlen, d_inner, d_state).total;
 }
 
 ss_status bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -445,9 +448,11 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   for (const void* p : f_ptrs)
     if (p && !aligned(p, 4)) return fail(SS_ERR_UNSUPPORTED, "float pointer %p misaligned", p);
   const size_t need = bwd_ws_bytes(batch, seqlen, d_inner, d_state);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(SS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes the "
                 "backward needs (ss_scan_bwd_workspace_bytes)", workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(SS_ERR_UNSUPPORTED, "workspace pointer %p not 16-byte aligned", workspace);
   const Range ins[] = {range("u", u, elems, es), range("delta", delta, elems, es),
                        range("z", z, elems, es), range("B", B, bc_elems, es),
                        range("C", C, bc_elems, es), range("A", A, d_inner * d_state, 4),
@@ -475,6 +480,14 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   a.delta_bias = delta_bias; a.h0 = h0; a.dh_last = dh_last; a.du = du; a.ddelta = ddelta;
   a.dz = z ? dz : nullptr; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
   a.ddelta_bias = ddelta_bias; a.dh0 = dh0; a.ck = static_cast<float*>(workspace);
+  if (need > 0) {
+    const ss::BwdLayout lay = ss::bwd_layout(batch, seqlen, d_inner, d_state);
+    char* ws = static_cast<char*>(workspace);
+    a.part_bc = reinterpret_cast<float*>(ws + lay.bc);
+    a.part_a = reinterpret_cast<float*>(ws + lay.a);
+    a.part_d = reinterpret_cast<float*>(ws + lay.d);
+    a.part_b = reinterpret_cast<float*>(ws + lay.b);
+  }
   a.batch = batch; a.seqlen = seqlen; a.d_inner = d_inner;
   a.n_cblk = (d_inner + 15) / 16;
   a.d_state = static_cast<int32_t>(d_state);

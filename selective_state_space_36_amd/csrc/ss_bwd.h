@@ -26,13 +26,19 @@ struct BwdArgs {
   void* du;              // io dtype
   void* ddelta;          // io dtype
   void* dz;              // io dtype, required with z
-  float* dA;             // accumulated (zeroed by the launch)
-  float* dB;             // (batch, seqlen, d_state), accumulated
-  float* dC;             // (batch, seqlen, d_state), accumulated
-  float* dD;             // nullptr: not computed; accumulated
-  float* ddelta_bias;    // nullptr: not computed; accumulated
+  float* dA;             // (d_inner, d_state): sum over batch rows
+  float* dB;             // (batch, seqlen, d_state): sum over channels
+  float* dC;             // (batch, seqlen, d_state): sum over channels
+  float* dD;             // nullptr: not computed; sum over batch rows and steps
+  float* ddelta_bias;    // nullptr: not computed; sum over batch rows and steps
   float* dh0;            // nullptr: not written
   const float* ck;       // workspace: (batch, nchunks, d_inner, d_state) chunk-end states
+  // Per-workgroup partial sums in the workspace, added in a fixed order by the reduction
+  // kernels (no atomics: the summed gradients are bit-reproducible):
+  float* part_bc;        // (batch, nchunks, n_cblk, kBwdChunk, 16, 2): dB, dC of 16 channels
+  float* part_a;         // (batch, d_inner, d_state): dA of one batch row
+  float* part_d;         // (batch, d_inner): dD of one batch row
+  float* part_b;         // (batch, d_inner): ddelta_bias of one batch row
   int64_t batch, seqlen, d_inner;
   int64_t n_cblk;        // channel blocks of 16 per batch row
   int32_t d_state;
@@ -40,8 +46,25 @@ struct BwdArgs {
   int32_t vec_io;        // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, dout
 };
 
-// Zero the accumulated outputs, then run the reverse pass (one workgroup per 16 channels of a
-// batch row) from the chunk-end states in ck.
+// Workspace of the backward: the chunk-end states, then the partial sums (256-byte aligned).
+struct BwdLayout {
+  size_t states, bc, a, d, b, total;  // byte offsets (states at 0) and the total size
+};
+inline BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const int64_t nch = (seqlen + kBwdChunk - 1) / kBwdChunk, ncb = (d_inner + 15) / 16;
+  BwdLayout l{};
+  l.states = 0;
+  l.bc = up(size_t(batch) * nch * d_inner * d_state * 4);
+  l.a = up(l.bc + size_t(batch) * nch * ncb * kBwdChunk * 16 * 2 * 4);
+  l.d = up(l.a + size_t(batch) * d_inner * d_state * 4);
+  l.b = up(l.d + size_t(batch) * d_inner * 4);
+  l.total = up(l.b + size_t(batch) * d_inner * 4);
+  return l;
+}
+
+// Run the reverse pass (one workgroup per 16 channels of a batch row) from the chunk-end states
+// in ck, then add the partial sums into dA, dB, dC, dD and ddelta_bias.
 hipError_t launch_scan_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace ss

@@ -21,11 +21,12 @@
 // state into registers, computes y for the gate's derivative, then runs the adjoint backwards
 // through the 16 steps.  Sums over a channel's states go through per-wave LDS tiles (summed by
 // the owner lane of the step, as in the forward); sums over channels (dB, dC) are reduced over
-// row pairs by a row swap (dB and dC in one swap) and over the eight pairs in LDS, then added to
-// global memory with one atomic per (step, state) and workgroup; dA, dD and dbias likewise once
-// per workgroup.  The atomic sums make dA, dB, dC, dD and dbias reproducible only up to rounding
-// order.  u/delta/z/dout tiles move as 16-byte pieces when the channel blocks are whole, with
-// the pieces of each tile row permuted by step against LDS bank conflicts.
+// row pairs by a row swap (dB and dC in one swap) and over the eight pairs in LDS, then written
+// as the workgroup's partial sum for the chunk (one 2 KB block per chunk and workgroup); dA, dD
+// and dbias are written as per-batch-row partials.  Two small kernels then add the partials in
+// a fixed order (over channel blocks, over batch rows), so every gradient is bit-reproducible.
+// u/delta/z/dout tiles move as 16-byte pieces when the channel blocks are whole, with the pieces
+// of each tile row permuted by step against LDS bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -267,17 +268,17 @@ struct BwdKernel {
           sb += sm.pq[pr >> 1][((pr & 1) * kT + tau) * 16 + n];
           sc += sm.pq[pr >> 1][kGcOff + ((pr & 1) * kT + tau) * 16 + n];
         }
-        if (tau < nv && n < N) {
-          const int64_t o = (row0 + int64_t(c) * kT + tau) * N + n;
-          atomicAdd(a.dB + o, sb);
-          atomicAdd(a.dC + o, sc);
+        if (a.part_bc) {  // this workgroup's sums for the chunk: 16 steps x 16 states x 2
+          const int64_t cb = d0 >> 4;
+          float* dst = a.part_bc + (((b * nchunks + c) * a.n_cblk + cb) * (kT * 16) + tid) * 2;
+          *reinterpret_cast<float2*>(dst) = make_float2(sb, sc);
         }
       }
       __syncthreads();  // the dB and dC tiles are rewritten by the next chunk
       buf ^= 1;
     }
     if (lane_ok) {
-      atomicAdd(a.dA + d * N + k, ga);
+      if (a.part_a) a.part_a[row * N + k] = ga;
       if (a.dh0) a.dh0[row * N + k] = e_next * lam;
     }
     // sums over the row's 16 owner lanes
@@ -286,9 +287,9 @@ struct BwdKernel {
       gd_acc += __shfl_xor(gd_acc, m, 16);
       gb_acc += __shfl_xor(gb_acc, m, 16);
     }
-    if (chan_ok && k == 0) {
-      if (a.dD) atomicAdd(a.dD + d, gd_acc);
-      if (a.ddelta_bias) atomicAdd(a.ddelta_bias + d, gb_acc);
+    if (chan_ok && k == 0 && a.part_d) {
+      a.part_d[row] = gd_acc;
+      a.part_b[row] = gb_acc;
     }
   }
 
@@ -368,6 +369,59 @@ __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
     p[i] = 0.0f;
 }
 
+// dB and dC of one (batch row, chunk): thread (step, state) adds the n_cblk workgroup partials
+// in channel-block order.
+__global__ void __launch_bounds__(256) reduce_bc_kernel(BwdArgs a, int64_t nchunks) {
+  const int64_t bc = blockIdx.x;  // b * nchunks + c
+  const int64_t b = bc / nchunks, c = bc - b * nchunks;
+  const int tid = threadIdx.x, tau = tid >> 4, n = tid & 15;
+  const float2* src = reinterpret_cast<const float2*>(a.part_bc) + bc * a.n_cblk * (kT * 16) + tid;
+  float sb = 0.0f, sc = 0.0f;
+  int64_t cb = 0;
+  for (; cb + 8 <= a.n_cblk; cb += 8) {  // eight loads in flight, added in order
+    float2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[(cb + j) * (kT * 16)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sb += v[j].x;
+      sc += v[j].y;
+    }
+  }
+  for (; cb < a.n_cblk; ++cb) {
+    const float2 v = src[cb * (kT * 16)];
+    sb += v.x;
+    sc += v.y;
+  }
+  const int64_t t = c * kT + tau;
+  if (t < a.seqlen && n < a.d_state) {
+    a.dB[(b * a.seqlen + t) * a.d_state + n] = sb;
+    a.dC[(b * a.seqlen + t) * a.d_state + n] = sc;
+  }
+}
+
+// dA, dD and ddelta_bias: the per-batch-row partials added in batch order.
+__global__ void __launch_bounds__(256) reduce_rows_kernel(BwdArgs a) {
+  const int64_t na = a.d_inner * a.d_state, nd = a.d_inner;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < na + 2 * nd;
+       i += int64_t(gridDim.x) * 256) {
+    const float* src;
+    float* dst;
+    int64_t j, stride;
+    if (i < na) {
+      src = a.part_a, dst = a.dA, j = i, stride = na;
+    } else if (i < na + nd) {
+      src = a.part_d, dst = a.dD, j = i - na, stride = nd;
+    } else {
+      src = a.part_b, dst = a.ddelta_bias, j = i - na - nd, stride = nd;
+    }
+    if (!dst) continue;
+    float acc = 0.0f;
+    for (int64_t b = 0; b < a.batch; ++b) acc += src[b * stride + j];
+    dst[j] = acc;
+  }
+}
+
 hipError_t zero(float* p, int64_t n, hipStream_t stream) {
   if (!p || n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
@@ -398,13 +452,29 @@ void launch_io(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_scan_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
   const int64_t N = a.d_state;
   hipError_t e;
-  if ((e = zero(a.dA, a.d_inner * N, stream)) != hipSuccess) return e;
-  if ((e = zero(a.dB, a.batch * a.seqlen * N, stream)) != hipSuccess) return e;
-  if ((e = zero(a.dC, a.batch * a.seqlen * N, stream)) != hipSuccess) return e;
-  if ((e = zero(a.dD, a.d_inner, stream)) != hipSuccess) return e;
-  if ((e = zero(a.ddelta_bias, a.d_inner, stream)) != hipSuccess) return e;
+  if (!a.part_bc) {
+    // an empty problem (no batch row, channel or step): the sums are zero; the kernel runs only
+    // to pass dh_last to dh0
+    if ((e = zero(a.dA, a.d_inner * N, stream)) != hipSuccess) return e;
+    if ((e = zero(a.dB, a.batch * a.seqlen * N, stream)) != hipSuccess) return e;
+    if ((e = zero(a.dC, a.batch * a.seqlen * N, stream)) != hipSuccess) return e;
+    if ((e = zero(a.dD, a.d_inner, stream)) != hipSuccess) return e;
+    if ((e = zero(a.ddelta_bias, a.d_inner, stream)) != hipSuccess) return e;
+  }
   if (bf16) launch_io<BF16>(a, stream);
   else launch_io<F32>(a, stream);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.part_bc) {
+    const int64_t nchunks = (a.seqlen + kT - 1) / kT;
+    if (a.batch * nchunks > 0)
+      hipLaunchKernelGGL(reduce_bc_kernel, dim3(static_cast<unsigned>(a.batch * nchunks)),
+                         dim3(256), 0, stream, a, nchunks);
+    const int64_t items = a.d_inner * N + 2 * a.d_inner;
+    const int64_t blocks = (items + 255) / 256 < 4096 ? (items + 255) / 256 : 4096;
+    if (blocks > 0)
+      hipLaunchKernelGGL(reduce_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                         stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -246,9 +246,10 @@ def scan_fwd_states(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_so
                     h0=None, return_last_state=False, out=None, h_last=None, states=None,
                     workspace=None, stream=None):
     """Prefill that also saves the state after every 16-step chunk (ss_scan_fwd_states), for
-    scan_bwd(..., states=...).  Arguments as for scan_fwd; states: (batch, ceil(L / 16),
-    d_inner, d_state) float32 or None (allocated here).  Returns (out, states), or
-    (out, states, h_last) with return_last_state."""
+    scan_bwd(..., states_given=True).  Arguments as for scan_fwd; states: (batch, ceil(L / 16),
+    d_inner, d_state) float32 (the states view of bwd_workspace, to hand the workspace to the
+    backward) or None (allocated here).  Returns (out, states), or (out, states, h_last) with
+    return_last_state."""
     batch, L, d_inner = u.shape
     d_state = B.shape[-1]
     code = _dtype_code(u)
@@ -283,14 +284,31 @@ def scan_fwd_states(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_so
     return (out, states, h_last) if return_last_state else (out, states)
 
 
+def bwd_workspace(batch, seqlen, d_inner, d_state, dtype=torch.bfloat16, device="cuda"):
+    """A workspace for scan_bwd (ss_scan_bwd_workspace_bytes bytes, or None when it needs none)
+    and the float32 view of its first part that holds the chunk-end states: give the view to
+    scan_fwd_states(states=...) and the workspace to scan_bwd(..., states_given=True)."""
+    code = SS_BF16 if dtype == torch.bfloat16 else SS_F32
+    nbytes = int(lib().ss_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, code))
+    if nbytes == 0:
+        return None, None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    nct = (seqlen + 15) // 16
+    states = ws[:batch * nct * d_inner * d_state * 4].view(torch.float32).view(
+        batch, nct, d_inner, d_state)
+    return ws, states
+
+
 def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
              h0=None, dh_last=None, want_dD=True, want_ddelta_bias=True, want_dh0=True,
-             workspace=None, states=None, stream=None):
+             workspace=None, states_given=False, stream=None):
     """Gradients of scan_fwd (ss_scan_bwd) for the upstream gradient dout (same dtype and shape
     as out) and optionally dh_last.  Returns a dict: du, ddelta, dz (io dtype; dz None without
     z), dA, dB, dC (float32), dD, ddelta_bias, dh0 (float32, None when not wanted).
-    states: the chunk-end states scan_fwd_states saved for these inputs (then the backward skips
-    its own forward pass: SS_FLAG_STATES_GIVEN); workspace is ignored then."""
+    workspace: uint8 device buffer of ss_scan_bwd_workspace_bytes bytes (allocated here when
+    None).  states_given: the workspace already begins with the chunk-end states that
+    scan_fwd_states saved for these inputs (SS_FLAG_STATES_GIVEN; see bwd_workspace), and the
+    backward skips its own forward pass."""
     batch, L, d_inner = u.shape
     d_state = B.shape[-1]
     code = _dtype_code(u)
@@ -311,13 +329,11 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
              dD=torch.empty((d_inner,), **f32) if want_dD else None,
              ddelta_bias=torch.empty((d_inner,), **f32) if want_ddelta_bias else None,
              dh0=torch.empty((batch, d_inner, d_state), **f32) if want_dh0 else None)
-    flags = 0
-    if states is not None:
-        _dev(states, "states", torch.float32, (batch, (L + 15) // 16, d_inner, d_state))
-        workspace, flags = states, SS_FLAG_STATES_GIVEN
-    elif workspace is None:
-        nbytes = int(lib().ss_scan_bwd_workspace_bytes(batch, L, d_inner, d_state, code))
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=u.device) if nbytes else None
+    flags = SS_FLAG_STATES_GIVEN if states_given else 0
+    if workspace is None:
+        if states_given:
+            raise ValueError("states_given needs the workspace that holds the states")
+        workspace, _ = bwd_workspace(batch, L, d_inner, d_state, u.dtype, u.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ss_scan_bwd(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),

@@ -143,8 +143,13 @@ def test_backward_argument_errors_before_launch(lib):
     assert _bwd(lib, ws=None, wsb=0) == ops.SS_ERR_INVALID_ARG       # workspace needed
     assert b"workspace" in lib.ss_last_error()
     need = lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 16, ops.SS_BF16)
-    assert need == 1 * 16 * 1 * 16 * 4
+    # the chunk-end states (1 chunk x 16 channels x 16 states), then the partial sums: dB/dC of
+    # one 16-channel block (16 steps x 16 states x 2) and dA, dD, dbias of one batch row, each
+    # part 256-byte aligned
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == up(up(up(up(16 * 16 * 4) + 16 * 16 * 2 * 4) + 16 * 16 * 4) + 16 * 4) + 256
     assert _bwd(lib, wsb=need - 4) == ops.SS_ERR_INVALID_ARG
+    assert _bwd(lib, ws=FAKE * 12 + 8, wsb=need) == ops.SS_ERR_UNSUPPORTED  # misaligned
     assert lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 17, ops.SS_BF16) == 0
 
 

@@ -99,8 +99,9 @@ def test_backward_with_saved_states(io):
     z = p["z"] if w.gate else None
     args = (dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"]))
     kw = dict(D=dev(p["D"]), z=dev(z), delta_bias=dev(p["delta_bias"]), h0=dev(h0))
-    _, states = ops().scan_fwd_states(*args, **kw)
-    g_s = ops().scan_bwd(*args, dev(g_out), states=states, **kw)
+    ws, states = ops().bwd_workspace(batch, L, D, N, args[0].dtype)
+    ops().scan_fwd_states(*args, states=states, **kw)
+    g_s = ops().scan_bwd(*args, dev(g_out), workspace=ws, states_given=True, **kw)
     g_r = ops().scan_bwd(*args, dev(g_out), **kw)
     torch.cuda.synchronize()
     ref = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], wl_f64(g_out), D=p["D"],
