@@ -92,9 +92,12 @@ struct BwdKernel {
 
   static __device__ __forceinline__ void run(const BwdArgs& a) {
     __shared__ Smem sm;
-    const int64_t b = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x / a.n_cblk));
-    const int64_t d0 = __builtin_amdgcn_readfirstlane(
-        static_cast<int>((blockIdx.x - b * a.n_cblk) * 16));
+    // XCD-aware order (as in the forward): neighbouring channel blocks, which share the 128-byte
+    // lines of the input tiles (16 bf16 channels are 32 bytes of a row), run on the same XCD and
+    // meet in its L2 instead of each XCD fetching the line
+    const int64_t lg = xcd_remap(blockIdx.x, int64_t(gridDim.x));
+    const int64_t b = __builtin_amdgcn_readfirstlane(static_cast<int>(lg / a.n_cblk));
+    const int64_t d0 = __builtin_amdgcn_readfirstlane(static_cast<int>((lg - b * a.n_cblk) * 16));
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
