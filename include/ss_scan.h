@@ -215,7 +215,7 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
                              uint32_t flags, void* stream);
 
 /*
- * Backward of the prefill (first-order input term): given dout = dL/d out (and optionally
+ * Backward of the prefill (first-order or exact-hold input term): given dout = dL/d out (and optionally
  * dh_last = dL/d h_last), the gradients of every input.  Reverse-mode differentiation of the
  * recurrence above (reading guide, "Método"), with the states recomputed from stored chunk-end
  * states rather than kept (reading guide, "Expansão de Estado Ciente de Hardware": recomputation
@@ -246,7 +246,12 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
  *                       own on the stream), then runs the reverse pass and two reductions.
  * dA, dB, dC, dD and ddelta_bias are sums over channels or batch rows: each workgroup writes its
  * partial sum and a second kernel adds the partials in a fixed order, so every output is
- * bit-for-bit reproducible.  d_state above 16 and SS_FLAG_ZOH_EXACT -> SS_ERR_UNSUPPORTED.
+ * bit-for-bit reproducible.  flags: SS_FLAG_ZOH_EXACT gives the gradients of the exact-hold
+ * input term g_t B_t u_t, g_t = (exp(dt_t A) - 1) / A (then ddt_t = sum_n lam_t e_t (A h_{t-1} +
+ * B_t u_t), du_t = gy_t D + sum_n lam_t g_t B_t, dB_t += lam_t g_t u_t and dA adds
+ * lam_t (dt e_t - g_t) / A B_t u_t); SS_FLAG_STATES_GIVEN as below, not together with the exact
+ * hold (ss_scan_fwd_states saves first-order states): SS_ERR_UNSUPPORTED.  d_state above 16 ->
+ * SS_ERR_UNSUPPORTED.
  * Outputs must not overlap inputs, each other or the workspace.
  */
 ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const void* B,

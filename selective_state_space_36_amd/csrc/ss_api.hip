@@ -418,8 +418,9 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   if (check_dtype(dtype, &es) != SS_OK) return SS_ERR_UNSUPPORTED;
   if (check_flags(flags, SS_FLAG_ZOH_EXACT | SS_FLAG_STATES_GIVEN) != SS_OK)
     return SS_ERR_UNSUPPORTED;
-  if (flags & SS_FLAG_ZOH_EXACT)
-    return fail(SS_ERR_UNSUPPORTED, "the backward implements the first-order input term only");
+  if ((flags & SS_FLAG_ZOH_EXACT) && (flags & SS_FLAG_STATES_GIVEN))
+    return fail(SS_ERR_UNSUPPORTED, "SS_FLAG_STATES_GIVEN takes the first-order states of "
+                "ss_scan_fwd_states; the exact-hold backward recomputes its own");
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
     return fail(SS_ERR_INVALID_ARG, "negative size");
   if (d_state < 1 || d_state > 16)
@@ -492,6 +493,7 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   a.n_cblk = (d_inner + 15) / 16;
   a.d_state = static_cast<int32_t>(d_state);
   a.softplus = delta_softplus ? 1 : 0;
+  a.zoh = (flags & SS_FLAG_ZOH_EXACT) ? 1 : 0;
   a.vec_io = (d_inner % 16 == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
               aligned(delta, 16) && aligned(dout, 16) && (!z || aligned(z, 16))) ? 1 : 0;
   if (batch * a.n_cblk > int64_t(0x7fffffff))
@@ -508,6 +510,7 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
     f.n_cblk = (d_inner + ss::kChanPerWG - 1) / ss::kChanPerWG;
     f.d_state = static_cast<int32_t>(d_state);
     f.softplus = a.softplus;
+    f.zoh = a.zoh;
     f.vec_io = (d_inner % ss::kChanPerWG == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
                 aligned(delta, 16)) ? 1 : 0;
     f.states = static_cast<float*>(workspace);

@@ -43,6 +43,7 @@ struct BwdArgs {
   int64_t n_cblk;        // channel blocks of 16 per batch row
   int32_t d_state;
   int32_t softplus;
+  int32_t zoh;           // exact zero-order-hold input term instead of dt B u
   int32_t vec_io;        // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, dout
 };
 

@@ -62,6 +62,36 @@ __device__ __forceinline__ float zoh_gain(float u, float y) {
   return fabsf(y) < 0.5f ? p : (u - 1.0f) * rcp_hw(y);
 }
 
+// Exact-hold input gain (exp(dt A) - 1) / A for one update of the prefill, from e = 2^y with
+// y = dt A log2(e) and ia = 1 / A (0 where A = 0).  For |y| < 1/8 it is dt R(y),
+// R(y) = (2^y - 1) / (y ln 2) = sum_k (y ln 2)^k / (k + 1)! cut after k = 4 (the rest is below
+// 7e-9 relative there): no cancellation in 2^y - 1 and no division.  Elsewhere it is (e - 1) / A
+// as one fused multiply-add; there |e - 1| >= 0.083, so the 1-ulp error of e is at most 1.5e-6
+// of the difference.  e = 0 (large negative y) gives -1 / A; A = 0 gives dt.
+__device__ __forceinline__ float hold_gain(float e, float y, float dt, float ia) {
+  float q = 1.9236258e-3f;
+  q = fmaf(q, y, 1.3876027e-2f);
+  q = fmaf(q, y, 8.0075502e-2f);
+  q = fmaf(q, y, 3.4657359e-1f);
+  q = fmaf(q, y, 1.0f);
+  return fabsf(y) < 0.125f ? dt * q : fmaf(e, ia, -ia);
+}
+
+// Derivative of that gain g = (exp(dt A) - 1) / A in A, (dt e - g) / A, with the same inputs.
+// For |y| < 1/8 it is dt^2 S(x), x = dt A = y ln 2, S(x) = sum_k (k + 1) x^k / (k + 2)! =
+// 1/2 + x/3 + x^2/8 + x^3/30 + x^4/144 (the rest is below 1e-8 relative there): the difference
+// dt e - g cancels as x -> 0 and tends to dt^2 / 2.  Elsewhere (dt e - (e - 1) / A) / A, where
+// the difference keeps all but about 5 bits.
+__device__ __forceinline__ float hold_gain_da(float e, float y, float dt, float ia) {
+  const float x = y * kLn2;
+  float q = 1.0f / 144.0f;
+  q = fmaf(q, x, 1.0f / 30.0f);
+  q = fmaf(q, x, 0.125f);
+  q = fmaf(q, x, 1.0f / 3.0f);
+  q = fmaf(q, x, 0.5f);
+  return fabsf(y) < 0.125f ? (dt * dt) * q : fmaf(dt, e, -fmaf(e, ia, -ia)) * ia;
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z}).
 __device__ __forceinline__ float silu_f(float z) {
   return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));

@@ -1,4 +1,5 @@
-// ss_scan_bwd.hip -- gfx950 backward of the prefill scan (first-order input term dt B u).
+// ss_scan_bwd.hip -- gfx950 backward of the prefill scan (first-order input term dt B u, or the
+// exact zero-order hold's g B u with g = (exp(dt A) - 1) / A).
 //
 // Gradients by reverse-mode differentiation of the recurrence (Mamba reading guide, "Método":
 // h_t = exp(dt_t A) h_{t-1} + dt_t B_t u_t, y_t = C_t h_t; IBM explainer: D term and gate), with
@@ -10,6 +11,10 @@
 //     dB_t   += lam_t dt_t u_t,  dC_t += gy_t h_t             (summed over channels)
 //     dA     += lam_t dt_t e_t h_{t-1},  dD += gy_t u_t,  dz_t = dout_t y_t silu'(z_t)
 //     ddelta_t = ddt_t sigmoid(delta_t + bias) (softplus'),  dbias += ddelta_t,  dh0 = e_0 lam_0.
+// Under the exact hold (reading guide, "Método") the input term is g_t B_t u_t with
+// g_t = (e_t - 1) / a_n; then dg/ddt = e_t and dg/da = (dt e_t - g_t) / a_n, so
+//     ddt_t = sum_n lam_t (a_n e_t h_{t-1} + e_t B_t u_t),  du_t = gy_t D + sum_n lam_t g_t B_t,
+//     dB_t += lam_t g_t u_t,  dA += lam_t (dt_t e_t h_{t-1} + dg/da B_t u_t).
 //
 // Work layout (as in the forward kernel): one channel per 16-lane DPP row, lane k owns state k
 // and the element work of step k of each 16-step chunk; 16 channels per 256-thread workgroup,
@@ -68,7 +73,7 @@ __device__ __forceinline__ int pslot_shift(int odd) {
 // 49.7 KB of LDS: three workgroups per CU.
 constexpr int kGcOff = 2 * kBwdChunk * 16 + 16;
 
-template <class IO, bool GATE, bool VEC>
+template <class IO, bool GATE, bool VEC, bool ZOH>
 struct BwdKernel {
   using elem = typename IO::elem;
   static constexpr int ES = sizeof(elem);
@@ -114,6 +119,7 @@ struct BwdKernel {
 
     const float a_n = lane_ok ? a.A[d * N + k] : 0.0f;
     const float A2 = a_n * kLog2e;
+    const float ia = (ZOH && a_n != 0.0f) ? 1.0f / a_n : 0.0f;  // exact hold: 1 / A, 0 at A = 0
     const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
     const float dskip = (chan_ok && a.D) ? a.D[d] : 0.0f;
     const int64_t row0 = b * L;  // (b, 0) row of u/delta/z/dout and of B/C
@@ -193,7 +199,8 @@ struct BwdKernel {
       const float sv = own(buf, 1) + bias;
       float dt = a.softplus ? softplus_f(sv) : sv;
       dt = own_ok ? dt : 0.0f;
-      const float du = own_ok ? dt * xu : 0.0f;
+      // first order: the input term is (dt u) B; exact hold: u B times the gain
+      const float du = own_ok ? (ZOH ? xu : dt * xu) : 0.0f;
       float hprev;
       if (c > 0) hprev = lane_ok ? ck_lane[int64_t(c - 1) * ck_chunk] : 0.0f;
       else hprev = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
@@ -205,7 +212,8 @@ struct BwdKernel {
       // recompute the chunk: states, decays and the partial sums C.h of y
       float hh[kT], ee[kT];
       float* pw = &sm.pq[wave][r * kPRow + k];
-      rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, hprev, hh, ee, pw, r & 1);
+      rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, ia, hprev, hh, ee, pw,
+                r & 1);
       wave_lds_sync();
       float y = 0.0f;
       {
@@ -229,8 +237,8 @@ struct BwdKernel {
       float* qw = &sm.pq[wave][4 * kPRow + r * kPRow + k];
       float* gbc_w = &sm.pq[wave][(r & 1) * kGcOff + (r >> 1) * kT * 16];
       float xb[kT], yc[kT];
-      rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, hprev, hh, ee,
-                lam, e_next, ga, pw, qw, xb, yc, r & 1);
+      rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, A2, ia, hprev,
+                hh, ee, lam, e_next, ga, pw, qw, xb, yc, r & 1);
       // dB and dC of each step, summed over channel pairs (independent of one another, so the
       // row swaps of different steps overlap); stored below, over the partial tiles
       float gpair[kT];
@@ -247,7 +255,9 @@ struct BwdKernel {
           gdt += pr[i];
           gx += qr[i];
         }
-        gdt = fmaf(xu, gx, gdt);  // + u_t sum_n lam B, the input term of ddt
+        // first order: + u_t sum_n lam B, the input term of ddt (the exact hold's, e u B lam,
+        // is in the partial sums already)
+        if (!ZOH) gdt = fmaf(xu, gx, gdt);
       }
       wave_lds_sync();  // every lane of the wave has its sums: the tiles take dB and dC
 #pragma unroll
@@ -258,7 +268,8 @@ struct BwdKernel {
         const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
         gb_acc += gdelta;
         const int64_t e = (row0 + int64_t(c) * kT + k) * D + d;
-        static_cast<elem*>(a.du)[e] = IO::from_float(fmaf(gx, dt, gy * dskip));
+        static_cast<elem*>(a.du)[e] =
+            IO::from_float(ZOH ? fmaf(gy, dskip, gx) : fmaf(gx, dt, gy * dskip));
         static_cast<elem*>(a.ddelta)[e] = IO::from_float(gdelta);
         if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
       }
@@ -299,13 +310,16 @@ struct BwdKernel {
   // Recompute step: keep the state and the decay of every step, and the partial sum C.h.
   template <int TAU>
   static __device__ __forceinline__ void rec_step(const float4 (&bcv)[kT / 2], float dt, float du,
-                                                  float A2, float& h, float (&hh)[kT],
+                                                  float A2, float ia, float& h, float (&hh)[kT],
                                                   float (&ee)[kT], float* pw, int odd) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
-    const float e = exp2_hw(row_bcast<TAU>(dt) * A2);
-    h = fmaf(e, h, row_bcast<TAU>(du) * bb);
+    const float dtb = row_bcast<TAU>(dt);
+    const float y = dtb * A2;
+    const float e = exp2_hw(y);
+    const float inc = row_bcast<TAU>(du) * bb;
+    h = fmaf(e, h, ZOH ? inc * hold_gain(e, y, dtb, ia) : inc);
     hh[TAU] = h;
     ee[TAU] = e;
     pw[TAU * kPTau + pslot_shift<TAU>(odd)] = cc * h;
@@ -313,11 +327,11 @@ struct BwdKernel {
   template <int... TAUS>
   static __device__ __forceinline__ void rec_steps(std::integer_sequence<int, TAUS...>,
                                                    const float4 (&bcv)[kT / 2], float dt,
-                                                   float du, float A2, float hprev,
+                                                   float du, float A2, float ia, float hprev,
                                                    float (&hh)[kT], float (&ee)[kT], float* pw,
                                                    int odd) {
     float h = hprev;
-    (rec_step<TAUS>(bcv, dt, du, A2, h, hh, ee, pw, odd), ...);
+    (rec_step<TAUS>(bcv, dt, du, A2, ia, h, hh, ee, pw, odd), ...);
   }
 
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
@@ -327,11 +341,11 @@ struct BwdKernel {
   // and 3 dC.
   template <int TAU>
   static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
-                                                  float xu, float gy, float a_n, float hprev,
-                                                  const float (&hh)[kT], const float (&ee)[kT],
-                                                  float& lam, float& e_next, float& ga, float* pw,
-                                                  float* qw, float (&xb)[kT], float (&yc)[kT],
-                                                  int odd) {
+                                                  float xu, float gy, float a_n, float A2,
+                                                  float ia, float hprev, const float (&hh)[kT],
+                                                  const float (&ee)[kT], float& lam,
+                                                  float& e_next, float& ga, float* pw, float* qw,
+                                                  float (&xb)[kT], float (&yc)[kT], int odd) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
@@ -339,32 +353,45 @@ struct BwdKernel {
     lam = fmaf(e_next, lam, gyb * cc);
     const float hp = TAU > 0 ? hh[TAU > 0 ? TAU - 1 : 0] : hprev;
     const float rr = lam * ee[TAU] * hp;
-    ga = fmaf(row_bcast<TAU>(dt), rr, ga);
+    const float dtb = row_bcast<TAU>(dt);
+    const float dub = row_bcast<TAU>(du);
+    ga = fmaf(dtb, rr, ga);
     const float qq = lam * bb;
-    pw[TAU * kPTau + pslot_shift<TAU>(odd)] = a_n * rr;
-    qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qq;
-    xb[TAU] = lam * row_bcast<TAU>(du);  // this channel's dB and dC terms, summed over
-    yc[TAU] = gyb * hh[TAU];             // channel pairs after the chain
+    if constexpr (ZOH) {
+      // dub is u here; the gain g and its derivative in A come from the recomputed decay
+      const float y = dtb * A2;
+      const float g = hold_gain(ee[TAU], y, dtb, ia);
+      ga = fmaf(qq * dub, hold_gain_da(ee[TAU], y, dtb, ia), ga);
+      pw[TAU * kPTau + pslot_shift<TAU>(odd)] = fmaf(a_n, rr, qq * ee[TAU] * dub);
+      qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qq * g;
+      xb[TAU] = lam * g * dub;
+    } else {
+      pw[TAU * kPTau + pslot_shift<TAU>(odd)] = a_n * rr;
+      qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qq;
+      xb[TAU] = lam * dub;  // this channel's dB and dC terms, summed over channel pairs after
+    }                       // the chain
+    yc[TAU] = gyb * hh[TAU];
     e_next = ee[TAU];
   }
   template <int... TAUS>
   static __device__ __forceinline__ void rev_steps(std::integer_sequence<int, TAUS...>,
                                                    const float4 (&bcv)[kT / 2], float dt,
                                                    float du, float xu, float gy, float a_n,
-                                                   float hprev, const float (&hh)[kT],
-                                                   const float (&ee)[kT], float& lam,
-                                                   float& e_next, float& ga, float* pw, float* qw,
-                                                   float (&xb)[kT], float (&yc)[kT], int odd) {
+                                                   float A2, float ia, float hprev,
+                                                   const float (&hh)[kT], const float (&ee)[kT],
+                                                   float& lam, float& e_next, float& ga, float* pw,
+                                                   float* qw, float (&xb)[kT], float (&yc)[kT],
+                                                   int odd) {
     // fold over the steps in decreasing order
-    (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, hprev, hh, ee, lam, e_next, ga, pw, qw,
-                             xb, yc, odd),
+    (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, A2, ia, hprev, hh, ee, lam, e_next, ga,
+                             pw, qw, xb, yc, odd),
      ...);
   }
 };
 
-template <class IO, bool GATE, bool VEC>
+template <class IO, bool GATE, bool VEC, bool ZOH>
 __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdArgs a) {
-  BwdKernel<IO, GATE, VEC>::run(a);
+  BwdKernel<IO, GATE, VEC, ZOH>::run(a);
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
@@ -433,20 +460,20 @@ hipError_t zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class IO>
+template <class IO, bool ZOH>
 void launch_io(const BwdArgs& a, hipStream_t stream) {
   if (a.batch * a.n_cblk == 0) return;  // nothing but the zeroed sums
   const dim3 grid(static_cast<unsigned>(a.batch * a.n_cblk)), block(kBwdThreads);
   if (a.vec_io) {
     if (a.z)
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, true, ZOH>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, true, ZOH>), grid, block, 0, stream, a);
   } else {
     if (a.z)
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, false, ZOH>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, false, ZOH>), grid, block, 0, stream, a);
   }
 }
 
@@ -464,8 +491,8 @@ hipError_t launch_scan_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     if ((e = zero(a.dD, a.d_inner, stream)) != hipSuccess) return e;
     if ((e = zero(a.ddelta_bias, a.d_inner, stream)) != hipSuccess) return e;
   }
-  if (bf16) launch_io<BF16>(a, stream);
-  else launch_io<F32>(a, stream);
+  if (bf16) a.zoh ? launch_io<BF16, true>(a, stream) : launch_io<BF16, false>(a, stream);
+  else a.zoh ? launch_io<F32, true>(a, stream) : launch_io<F32, false>(a, stream);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.part_bc) {
     const int64_t nchunks = (a.seqlen + kT - 1) / kT;

@@ -479,21 +479,6 @@ struct ScanKernel {
     }
   }
 
-  // Exact-hold gain (exp(dt A) - 1) / A, from e = 2^y with y = dt A log2(e) and ia = 1 / A (0
-  // where A = 0).  For |y| < 1/8 it is dt R(y), R(y) = (2^y - 1) / (y ln 2) = sum_k (y ln 2)^k /
-  // (k + 1)! cut after k = 4 (the rest is below 7e-9 relative there): no cancellation in 2^y - 1
-  // and no division.  Elsewhere it is (e - 1) / A as one fused multiply-add; there |e - 1| >=
-  // 0.083, so the 1-ulp error of e is at most 1.5e-6 of the difference.  e = 0 (large negative y)
-  // gives -1 / A; A = 0 gives dt.
-  static __device__ __forceinline__ float hold_gain(float e, float y, float dt, float ia) {
-    float q = 1.9236258e-3f;
-    q = fmaf(q, y, 1.3876027e-2f);
-    q = fmaf(q, y, 8.0075502e-2f);
-    q = fmaf(q, y, 3.4657359e-1f);
-    q = fmaf(q, y, 1.0f);
-    return fabsf(y) < 0.125f ? dt * q : fmaf(e, ia, -ia);
-  }
-
   // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
   // (B, C) pairs for this lane's states, two steps per float4 (with one state per lane: B only,
   // four steps per float4; with FOLD the lane stores its new state instead of C_t[n] h_t[n]).

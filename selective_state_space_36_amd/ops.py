@@ -301,14 +301,15 @@ def bwd_workspace(batch, seqlen, d_inner, d_state, dtype=torch.bfloat16, device=
 
 def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_softplus=True,
              h0=None, dh_last=None, want_dD=True, want_ddelta_bias=True, want_dh0=True,
-             workspace=None, states_given=False, stream=None):
+             workspace=None, states_given=False, zoh_exact=False, stream=None):
     """Gradients of scan_fwd (ss_scan_bwd) for the upstream gradient dout (same dtype and shape
     as out) and optionally dh_last.  Returns a dict: du, ddelta, dz (io dtype; dz None without
     z), dA, dB, dC (float32), dD, ddelta_bias, dh0 (float32, None when not wanted).
     workspace: uint8 device buffer of ss_scan_bwd_workspace_bytes bytes (allocated here when
     None).  states_given: the workspace already begins with the chunk-end states that
     scan_fwd_states saved for these inputs (SS_FLAG_STATES_GIVEN; see bwd_workspace), and the
-    backward skips its own forward pass."""
+    backward skips its own forward pass.  zoh_exact: gradients of the exact zero-order-hold
+    input term (SS_FLAG_ZOH_EXACT; not with states_given)."""
     batch, L, d_inner = u.shape
     d_state = B.shape[-1]
     code = _dtype_code(u)
@@ -329,7 +330,7 @@ def scan_bwd(u, delta, A, B, C, dout, D=None, z=None, delta_bias=None, delta_sof
              dD=torch.empty((d_inner,), **f32) if want_dD else None,
              ddelta_bias=torch.empty((d_inner,), **f32) if want_ddelta_bias else None,
              dh0=torch.empty((batch, d_inner, d_state), **f32) if want_dh0 else None)
-    flags = SS_FLAG_STATES_GIVEN if states_given else 0
+    flags = (SS_FLAG_STATES_GIVEN if states_given else 0) | (SS_FLAG_ZOH_EXACT if zoh_exact else 0)
     if workspace is None:
         if states_given:
             raise ValueError("states_given needs the workspace that holds the states")

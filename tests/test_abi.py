@@ -134,7 +134,9 @@ def _bwd(lib, **kw):
 
 def test_backward_argument_errors_before_launch(lib):
     assert _bwd(lib, N=32) == ops.SS_ERR_UNSUPPORTED
-    assert _bwd(lib, flags=ops.SS_FLAG_ZOH_EXACT) == ops.SS_ERR_UNSUPPORTED
+    assert _bwd(lib, flags=ops.SS_FLAG_ZOH_EXACT | ops.SS_FLAG_STATES_GIVEN) == \
+        ops.SS_ERR_UNSUPPORTED                                       # exact hold: no given states
+    assert _bwd(lib, flags=ops.SS_FLAG_ZOH_EXACT, dout=None) == ops.SS_ERR_INVALID_ARG
     assert _bwd(lib, z=FAKE * 13) == ops.SS_ERR_INVALID_ARG          # z without dz
     assert b"dz" in lib.ss_last_error()
     assert _bwd(lib, dout=None) == ops.SS_ERR_INVALID_ARG

@@ -46,7 +46,7 @@ def check_grad(got, ref, tol, what):
                              f"want {ref[i]!r}")
 
 
-def run_bwd(p, *, gate=True, skip=True, h0=True, dh_last=True, softplus=True, seed=0):
+def run_bwd(p, *, gate=True, skip=True, h0=True, dh_last=True, softplus=True, seed=0, zoh=False):
     batch, L, D = p["u"].shape
     N = p["B"].shape[-1]
     rng = np.random.default_rng(seed)
@@ -59,16 +59,17 @@ def run_bwd(p, *, gate=True, skip=True, h0=True, dh_last=True, softplus=True, se
     z = p["z"] if gate else None
     Dk = p["D"] if skip else None
     print(f"  bwd case: shape={p['u'].shape} N={N} bf16={bf16} gate={gate} skip={skip} "
-          f"h0={h0} dh_last={dh_last} softplus={softplus}", flush=True)
+          f"h0={h0} dh_last={dh_last} softplus={softplus} zoh={zoh}", flush=True)
     g = ops().scan_bwd(dev(p["u"]), dev(p["delta"]), dev(p["A"]), dev(p["B"]), dev(p["C"]),
                        dev(g_out), D=dev(Dk), z=dev(z), delta_bias=dev(p["delta_bias"]),
-                       delta_softplus=softplus, h0=dev(h0a), dh_last=dev(dhl))
+                       delta_softplus=softplus, h0=dev(h0a), dh_last=dev(dhl), zoh_exact=zoh)
     torch.cuda.synchronize()
     ref = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
                           (wl_f64(g_out)), D=Dk, z=z, delta_bias=p["delta_bias"],
                           delta_softplus=softplus,
                           h0=None if h0a is None else h0a.astype(np.float64),
-                          dh_last=None if dhl is None else dhl.astype(np.float64))
+                          dh_last=None if dhl is None else dhl.astype(np.float64),
+                          zoh_exact=zoh)
     io_tol = 2e-2 if bf16 else 1e-3
     for key in ("du", "ddelta", "dz"):
         if ref[key] is None or g[key] is None:
@@ -117,6 +118,63 @@ def test_softplus_off_and_no_optional_inputs():
     p["delta"] = (np.abs(p["delta"]) * 0.1 + 0.01).astype(np.float32)
     p["delta_bias"] = None
     run_bwd(p, gate=False, skip=False, h0=False, dh_last=False, softplus=False)
+
+
+# ------------------------------------------------------------------------------------------
+# exact zero-order hold (SS_FLAG_ZOH_EXACT): gradients of (exp(dt A) - 1) / A * B u
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("gate,skip,softplus", [(False, True, True), (True, True, True),
+                                                (True, False, False)])
+def test_zoh_bwd_fp32(gate, skip, softplus):
+    p = wl.make_prefill(wl.WORKLOADS[0], batch=2, seqlen=90, d_inner=32, seed=51)
+    if gate:
+        p["z"] = np.random.default_rng(4).standard_normal(p["u"].shape).astype(np.float32)
+    if not softplus:  # dt used as given: positive, no bias
+        p["delta"] = (np.abs(p["delta"]) * 0.1 + 0.01).astype(np.float32)
+        p["delta_bias"] = None
+    run_bwd(p, gate=gate, skip=skip, softplus=softplus, zoh=True, seed=51)
+
+
+def test_zoh_bwd_mixed_A_covers_both_gain_forms():
+    """A spread from 0 to -40 and dt from 1e-3 to ~1, so that |dt A log2 e| falls on both sides
+    of the 1/8 switch between the series and the direct forms of the gain and of its derivative
+    in A (A = 0 exactly in one column: the gain is dt, its derivative dt^2 / 2)."""
+    rng = np.random.default_rng(61)
+    p = wl.make_prefill(wl.WORKLOADS[0], batch=2, seqlen=70, d_inner=24, seed=61)
+    A = -np.exp(rng.uniform(np.log(1e-3), np.log(40.0), size=(24, 16))).astype(np.float32)
+    A[:, 3] = 0.0
+    p["A"] = A
+    p["delta_bias"] = rng.uniform(-7.0, 0.5, size=24).astype(np.float32)
+    run_bwd(p, gate=False, zoh=True, seed=61)
+
+
+@pytest.mark.parametrize("d_state", [1, 5])
+def test_zoh_bwd_state_sizes(d_state):
+    p = wl.make_prefill(wl.WORKLOADS[0], batch=2, seqlen=40, d_inner=20, seed=d_state)
+    rng = np.random.default_rng(d_state)
+    p["B"] = rng.standard_normal((2, 40, d_state)).astype(np.float32)
+    p["C"] = rng.standard_normal((2, 40, d_state)).astype(np.float32)
+    p["A"] = np.ascontiguousarray(np.tile(-np.arange(1, d_state + 1, dtype=np.float32), (20, 1)))
+    run_bwd(p, gate=False, zoh=True, seed=d_state)
+
+
+def test_zoh_bwd_bf16_and_repeatable():
+    p = wl.make_prefill(wl.WORKLOADS[1], batch=2, seqlen=300, d_inner=48, seed=71)
+    g1, _ = run_bwd(p, zoh=True, seed=71)
+    g2, _ = run_bwd(p, zoh=True, seed=71)
+    for key in ("du", "ddelta", "dz", "dh0", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_zoh_bwd_rejects_given_states():
+    o = ops()
+    p = wl.make_prefill(wl.WORKLOADS[0], batch=1, seqlen=8, d_inner=16, seed=1)
+    args = [dev(p[k]) for k in ("u", "delta", "A", "B", "C")]
+    ws, states = o.bwd_workspace(1, 8, 16, 16, torch.float32)
+    o.scan_fwd_states(*args, states=states)
+    with pytest.raises(o.SSError) as e:
+        o.scan_bwd(*args, dev(p["u"]), workspace=ws, states_given=True, zoh_exact=True)
+    assert e.value.status == o.SS_ERR_UNSUPPORTED
 
 
 def test_medium_bf16_bwd():

@@ -120,12 +120,14 @@ def test_full_decode_all_steps():
 
 
 @pytest.mark.timeout(900)
-def test_full_backward_every_gradient():
+@pytest.mark.parametrize("zoh", [False, True])
+def test_full_backward_every_gradient(zoh):
     """The backward of the 2.8B-shaped layer for a seeded upstream gradient: every element of
     every gradient against the oracle's reverse mode over the whole layer, including dB and dC
     (each entry a sum over all 5120 channels) and dA, dD, ddelta_bias (sums over batch and
     steps).  Bound, elementwise: |gpu - ref| <= tol + tol * |ref|, tol = 2e-2 for the
-    bf16-stored du, ddelta, dz and 1e-3 for the float32 ones."""
+    bf16-stored du, ddelta, dz and 1e-3 for the float32 ones.  Both input terms: first order
+    and the exact zero-order hold."""
     w = wl.WORKLOADS[2]
     print(f"  generating {w.name}", flush=True)
     p = wl.make_prefill(w)
@@ -134,7 +136,7 @@ def test_full_backward_every_gradient():
     g = _to_gpu(p)
     print("  GPU backward", flush=True)
     gr = ops().scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dev(g_out), D=g["D"],
-                        z=g["z"], delta_bias=g["delta_bias"])
+                        z=g["z"], delta_bias=g["delta_bias"], zoh_exact=zoh)
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() for k, v in gr.items() if v is not None}
     del gr, g
@@ -142,7 +144,7 @@ def test_full_backward_every_gradient():
     print("  oracle backward", flush=True)
     ref = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"],
                           wl.bf16_bits_to_f32(g_out).astype(np.float64), D=p["D"], z=p["z"],
-                          delta_bias=p["delta_bias"])
+                          delta_bias=p["delta_bias"], zoh_exact=zoh)
     for key in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias"):
         tol = 2e-2 if key in ("du", "ddelta", "dz") else 1e-3
         want = ref[key]
