@@ -149,7 +149,7 @@ size_t ss_scan_fwd_ex_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_i
  *   states : (batch, ceil(seqlen / 16), d_inner, d_state) float32, written: states[b,c,d,:] is
  *            the state after step min(16 c + 15, seqlen - 1).  Caller-owned, of
  *            ss_scan_fwd_states_bytes() bytes; it must not overlap the inputs, out, h_last or
- *            the workspace.  With d_state <= 16 it is exactly the first part of the workspace
+ *            the workspace.  It is exactly the first part of the workspace
  *            ss_scan_bwd takes with SS_FLAG_STATES_GIVEN: a training step points `states` at the
  *            start of a buffer of ss_scan_bwd_workspace_bytes() bytes and passes that buffer to
  *            the backward.
@@ -250,7 +250,7 @@ ss_status ss_state_update_ex(float* state, const void* u, const void* delta, con
  * input term g_t B_t u_t, g_t = (exp(dt_t A) - 1) / A (then ddt_t = sum_n lam_t e_t (A h_{t-1} +
  * B_t u_t), du_t = gy_t D + sum_n lam_t g_t B_t, dB_t += lam_t g_t u_t and dA adds
  * lam_t (dt e_t - g_t) / A B_t u_t); SS_FLAG_STATES_GIVEN as below, not together with the exact
- * hold (ss_scan_fwd_states saves first-order states): SS_ERR_UNSUPPORTED.  d_state above 16 ->
+ * hold (ss_scan_fwd_states saves first-order states): SS_ERR_UNSUPPORTED.  d_state above 64 ->
  * SS_ERR_UNSUPPORTED.
  * Outputs must not overlap inputs, each other or the workspace.
  */
@@ -263,7 +263,7 @@ ss_status ss_scan_bwd(const void* u, const void* delta, const float* A, const vo
                       ss_dtype dtype, void* workspace, size_t workspace_bytes, uint32_t flags,
                       void* stream);
 
-/* Workspace bytes ss_scan_bwd needs for this shape (0 for an empty problem or d_state > 16).
+/* Workspace bytes ss_scan_bwd needs for this shape (0 for an empty problem or d_state > 64).
  * With flags SS_FLAG_STATES_GIVEN the states part of the workspace is read, not written: it
  * must hold the states ss_scan_fwd_states wrote for the same u, delta, A, B, delta_bias,
  * delta_softplus, h0, sizes and dtype (C, D and z do not enter the states). */

@@ -400,10 +400,10 @@ ss_status decode_impl(float* state, const void* u, const void* delta, const floa
 // the per-batch-row partials of dA, dD, ddelta_bias (ss::bwd_layout).  0 for an empty problem
 // (nothing to sum) or an unsupported d_state.
 size_t bwd_ws_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state) {
-  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 16) return 0;
+  if (batch <= 0 || seqlen <= 0 || d_inner <= 0 || d_state < 1 || d_state > 64) return 0;
   const int64_t nchunks = (seqlen + ss::kBwdChunk - 1) / ss::kBwdChunk;
   int64_t n;  // a bound on every term of the layout, in bytes
-  if (!mul_ok(batch * (d_inner + 16), nchunks + 1, &n) || !mul_ok(n, 48 * 8, &n)) return 0;
+  if (!mul_ok(batch * (d_inner + 16), nchunks + 1, &n) || !mul_ok(n, 1024 * 8, &n)) return 0;
   return ss::bwd_layout(batch, seqlen, d_inner, d_state).total;
 }
 
@@ -423,8 +423,8 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
                 "ss_scan_fwd_states; the exact-hold backward recomputes its own");
   if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state < 0)
     return fail(SS_ERR_INVALID_ARG, "negative size");
-  if (d_state < 1 || d_state > 16)
-    return fail(SS_ERR_UNSUPPORTED, "backward: d_state=%lld outside 1..16", (long long)d_state);
+  if (d_state < 1 || d_state > 64)
+    return fail(SS_ERR_UNSUPPORTED, "backward: d_state=%lld outside 1..64", (long long)d_state);
   int64_t rows, elems, bc_elems, st_elems;
   if (!mul_ok(batch, d_inner, &rows) || !mul_ok(rows, seqlen, &elems) ||
       !mul_ok(batch * seqlen, d_state, &bc_elems) || !mul_ok(rows, d_state, &st_elems) ||

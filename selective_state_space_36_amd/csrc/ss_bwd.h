@@ -7,7 +7,8 @@
 namespace ss {
 
 // Backward geometry: like the prefill, 16 lanes (one DPP row) per channel and 16 channels per
-// 256-thread workgroup, time in 16-step chunks; d_state <= 16.
+// 256-thread workgroup, time in 16-step chunks; d_state <= 64 as 1, 2 or 4 groups of 16 states
+// per lane.
 constexpr int kBwdThreads = 256;
 constexpr int kBwdChunk = 16;
 
@@ -35,7 +36,8 @@ struct BwdArgs {
   const float* ck;       // workspace: (batch, nchunks, d_inner, d_state) chunk-end states
   // Per-workgroup partial sums in the workspace, added in a fixed order by the reduction
   // kernels (no atomics: the summed gradients are bit-reproducible):
-  float* part_bc;        // (batch, nchunks, n_cblk, kBwdChunk, 16, 2): dB, dC of 16 channels
+  float* part_bc;        // (batch, nchunks, n_cblk, kBwdChunk, np, 2): dB, dC of 16 channels,
+                         // np = bwd_states_padded(d_state)
   float* part_a;         // (batch, d_inner, d_state): dA of one batch row
   float* part_d;         // (batch, d_inner): dD of one batch row
   float* part_b;         // (batch, d_inner): ddelta_bias of one batch row
@@ -47,6 +49,9 @@ struct BwdArgs {
   int32_t vec_io;        // whole 16-channel blocks with 16-byte aligned rows of u, delta, z, dout
 };
 
+// States per channel as the backward kernel lays them out: 16, 32 or 64.
+inline int bwd_states_padded(int64_t d_state) { return d_state <= 16 ? 16 : d_state <= 32 ? 32 : 64; }
+
 // Workspace of the backward: the chunk-end states, then the partial sums (256-byte aligned).
 struct BwdLayout {
   size_t states, bc, a, d, b, total;  // byte offsets (states at 0) and the total size
@@ -57,7 +62,7 @@ inline BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int6
   BwdLayout l{};
   l.states = 0;
   l.bc = up(size_t(batch) * nch * d_inner * d_state * 4);
-  l.a = up(l.bc + size_t(batch) * nch * ncb * kBwdChunk * 16 * 2 * 4);
+  l.a = up(l.bc + size_t(batch) * nch * ncb * kBwdChunk * bwd_states_padded(d_state) * 2 * 4);
   l.d = up(l.a + size_t(batch) * d_inner * d_state * 4);
   l.b = up(l.d + size_t(batch) * d_inner * 4);
   l.total = up(l.b + size_t(batch) * d_inner * 4);

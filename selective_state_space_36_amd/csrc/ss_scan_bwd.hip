@@ -73,12 +73,13 @@ __device__ __forceinline__ int pslot_shift(int odd) {
 // 49.7 KB of LDS: three workgroups per CU.
 constexpr int kGcOff = 2 * kBwdChunk * 16 + 16;
 
-template <class IO, bool GATE, bool VEC, bool ZOH>
+template <class IO, bool GATE, bool VEC, bool ZOH, int NL>
 struct BwdKernel {
   using elem = typename IO::elem;
   static constexpr int ES = sizeof(elem);
   static constexpr int PIECE_E = 16 / ES;        // elements per 16-byte piece
   static constexpr int PIECES = 16 / PIECE_E;    // pieces per 16-channel tile row
+  static constexpr int NP = 16 * NL;             // states per channel, padded: NL per lane
   // The 16-byte pieces of row (step) k of an input tile are stored XOR-permuted by
   // (k / (8 / PIECES)) mod PIECES, so that the owner lanes of steps 4 (bf16) or 2 (fp32) apart
   // do not read the same LDS banks (32 banks of 4 bytes; rows are 32 or 64 bytes).
@@ -87,7 +88,7 @@ struct BwdKernel {
   }
 
   struct alignas(16) Smem {
-    float2 bc[2][16][kT + 2];       // (B_t[n], C_t[n]) of the chunk, double-buffered
+    float2 bc[2][NP][kT + 2];       // (B_t[n], C_t[n]) of the chunk, double-buffered
     elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
     // per wave: partial sums over states, p (y, then ddt) at 0 and q (du) at 4 * kPRow; after
     // the owner sums, the dB and dC tiles of the wave's row pairs
@@ -111,36 +112,46 @@ struct BwdKernel {
     const int64_t D = a.d_inner, N = a.d_state, L = a.seqlen;
     const int64_t d = d0 + cl;
     const bool chan_ok = d < D;
-    const bool lane_ok = chan_ok && k < N;
     const int64_t row = b * D + d;
     const int nchunks = static_cast<int>((L + kT - 1) / kT);
     const int last_valid = static_cast<int>(L - int64_t(nchunks - 1) * kT);
     auto nvalid_of = [&](int c) { return c == nchunks - 1 ? last_valid : kT; };
 
-    const float a_n = lane_ok ? a.A[d * N + k] : 0.0f;
-    const float A2 = a_n * kLog2e;
-    const float ia = (ZOH && a_n != 0.0f) ? 1.0f / a_n : 0.0f;  // exact hold: 1 / A, 0 at A = 0
+    // per lane and state group j (state n = k + 16 j)
+    bool ok_j[NL];
+    float a_n[NL], A2[NL], ia[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      ok_j[j] = chan_ok && k + 16 * j < N;
+      a_n[j] = ok_j[j] ? a.A[d * N + k + 16 * j] : 0.0f;
+      A2[j] = a_n[j] * kLog2e;
+      ia[j] = (ZOH && a_n[j] != 0.0f) ? 1.0f / a_n[j] : 0.0f;  // exact hold: 1 / A, 0 at A = 0
+    }
     const float bias = (chan_ok && a.delta_bias) ? a.delta_bias[d] : 0.0f;
     const float dskip = (chan_ok && a.D) ? a.D[d] : 0.0f;
     const int64_t row0 = b * L;  // (b, 0) row of u/delta/z/dout and of B/C
 
     // ---- tile loads: wave w loads tensor w of (u, delta, z, dout), element by element through
     // a raw buffer sized to the chunk's valid steps (loads past the end read 0; channels past
-    // d_inner read the next row or 0 and are not used); every thread loads one (step, state) of
-    // B and C.
+    // d_inner read the next row or 0 and are not used); every thread loads NL (step, state)
+    // elements of B and C.
     const void* tens[4] = {a.u, a.delta, a.z, a.dout};
     const int tl_row = lane / PIECES, tl_pc = lane % PIECES;
     const bool tl_on = lane < kT * PIECES;
     const uint32_t tl_off =
         tl_on ? static_cast<uint32_t>((tl_row * D + tl_pc * PIECE_E) * ES) : kOffNone;
     const int bc_tau = tid >> 4, bc_n = tid & 15;
-    const uint32_t bc_off = bc_n < N ? static_cast<uint32_t>((bc_tau * N + bc_n) * ES) : kOffNone;
+    uint32_t bc_off[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      bc_off[j] = bc_n + 16 * j < N ? static_cast<uint32_t>((bc_tau * N + bc_n + 16 * j) * ES)
+                                    : kOffNone;
 
     // Global loads of chunk c go to registers (issued before the current chunk is computed) and
     // are written to LDS buffer `buf` after it.
     elem pv[PIECE_E];
     uint4 pvv{0, 0, 0, 0};
-    float pbv = 0.0f, pcv = 0.0f;
+    float pbv[NL], pcv[NL];
     auto issue = [&](int c) {
       const int nv = nvalid_of(c);
       const int64_t t0 = int64_t(c) * kT;
@@ -157,9 +168,12 @@ struct BwdKernel {
       }
       const uint32_t bc_bytes = static_cast<uint32_t>(nv * N * ES);
       const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + (row0 + t0) * N * ES, bc_bytes);
-      pbv = IO::widen(buf_load<elem>(rb, bc_off));
       const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
-      pcv = IO::widen(buf_load<elem>(rc, bc_off));
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        pbv[j] = IO::widen(buf_load<elem>(rb, bc_off[j]));
+        pcv[j] = IO::widen(buf_load<elem>(rc, bc_off[j]));
+      }
     };
     auto stage = [&](int buf) {
       if ((GATE || wave_u != 2) && tl_on) {
@@ -171,13 +185,19 @@ struct BwdKernel {
           for (int e = 0; e < PIECE_E; ++e) dst[e] = pv[e];
         }
       }
-      sm.bc[buf][bc_n][bc_tau] = make_float2(pbv, pcv);
+#pragma unroll
+      for (int j = 0; j < NL; ++j) sm.bc[buf][bc_n + 16 * j][bc_tau] = make_float2(pbv[j], pcv[j]);
     };
     const int own_col = ((cl / PIECE_E) ^ pswz(k)) * PIECE_E + cl % PIECE_E;
     auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][own_col]); };
+    auto read_bc = [&](int buf, int j, float4 (&bcv)[kT / 2]) {
+#pragma unroll
+      for (int i = 0; i < kT / 2; ++i)
+        bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k + 16 * j][2 * i]);
+    };
 
     // chunk-end states, (batch, chunk, d_inner, d_state): the wave's four channels of a chunk are
-    // 256 contiguous bytes
+    // contiguous
     const float* ck_lane = a.ck + ((b * nchunks) * D + d) * N + k;
     const int64_t ck_chunk = D * N;
     int buf = 0;
@@ -187,10 +207,36 @@ struct BwdKernel {
       __syncthreads();
     }
 
-    // ---- pass 2: chunks backwards
-    float lam = (a.dh_last && lane_ok) ? a.dh_last[row * N + k] : 0.0f;
-    float e_next = 1.0f;
-    float ga = 0.0f, gd_acc = 0.0f, gb_acc = 0.0f;
+    // ---- chunks backwards
+    float lam[NL], e_next[NL], ga[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      lam[j] = (a.dh_last && ok_j[j]) ? a.dh_last[row * N + k + 16 * j] : 0.0f;
+      e_next[j] = 1.0f;
+      ga[j] = 0.0f;
+    }
+    float gd_acc = 0.0f, gb_acc = 0.0f;
+    const int own_slot = r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau;
+    float* pw = &sm.pq[wave][r * kPRow + k];
+    float* qw = &sm.pq[wave][4 * kPRow + r * kPRow + k];
+    float* gbc_w = &sm.pq[wave][(r & 1) * kGcOff + (r >> 1) * kT * 16];
+    // the workgroup's dB and dC of state group j for the chunk: the eight row-pair tiles added,
+    // then written as this workgroup's partial sum (16 steps x NP states x 2)
+    auto reduce_bc = [&](int c, int j) {
+      const int tau = tid >> 4, n = tid & 15;
+      float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int pr = 0; pr < 8; ++pr) {
+        sb += sm.pq[pr >> 1][((pr & 1) * kT + tau) * 16 + n];
+        sc += sm.pq[pr >> 1][kGcOff + ((pr & 1) * kT + tau) * 16 + n];
+      }
+      if (a.part_bc) {
+        const int64_t cb = d0 >> 4;
+        float* dst = a.part_bc +
+                     (((b * nchunks + c) * a.n_cblk + cb) * (kT * NP) + tau * NP + 16 * j + n) * 2;
+        *reinterpret_cast<float2*>(dst) = make_float2(sb, sc);
+      }
+    };
     for (int c = nchunks - 1; c >= 0; --c) {
       if (c > 0) issue(c - 1);
       const int nv = nvalid_of(c);
@@ -201,23 +247,36 @@ struct BwdKernel {
       dt = own_ok ? dt : 0.0f;
       // first order: the input term is (dt u) B; exact hold: u B times the gain
       const float du = own_ok ? (ZOH ? xu : dt * xu) : 0.0f;
-      float hprev;
-      if (c > 0) hprev = lane_ok ? ck_lane[int64_t(c - 1) * ck_chunk] : 0.0f;
-      else hprev = (a.h0 && lane_ok) ? a.h0[row * N + k] : 0.0f;
-
-      float4 bcv[kT / 2];
+      float hprev[NL];
 #pragma unroll
-      for (int i = 0; i < kT / 2; ++i)
-        bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k][2 * i]);
+      for (int j = 0; j < NL; ++j) {
+        if (c > 0) hprev[j] = ok_j[j] ? ck_lane[int64_t(c - 1) * ck_chunk + 16 * j] : 0.0f;
+        else hprev[j] = (a.h0 && ok_j[j]) ? a.h0[row * N + k + 16 * j] : 0.0f;
+      }
+
       // recompute the chunk: states, decays and the partial sums C.h of y
-      float hh[kT], ee[kT];
-      float* pw = &sm.pq[wave][r * kPRow + k];
-      rec_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2, ia, hprev, hh, ee, pw,
-                r & 1);
+      float4 bcv[kT / 2];
+      float hh[kT], ee[kT], acc[kT];
+      if constexpr (NL == 1) {
+        read_bc(buf, 0, bcv);
+        rec_steps<0>(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2[0], ia[0], hprev[0],
+                     hh, ee, pw, acc, r & 1);
+      } else {
+#pragma unroll
+        for (int t = 0; t < kT; ++t) acc[t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          read_bc(buf, j, bcv);
+          rec_steps<1>(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2[j], ia[j],
+                       hprev[j], hh, ee, pw, acc, r & 1);
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) pw[t * kPTau + ((t ^ kPSwap) - t) * kPTau * (r & 1)] = acc[t];
+      }
       wave_lds_sync();
       float y = 0.0f;
       {
-        const float* pr = &sm.pq[wave][r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau];
+        const float* pr = &sm.pq[wave][own_slot];
 #pragma unroll
         for (int i = 0; i < 16; ++i) y += pr[i];
       }
@@ -234,34 +293,77 @@ struct BwdKernel {
       gd_acc = fmaf(gy, xu, gd_acc);
 
       // the adjoint backwards through the chunk
-      float* qw = &sm.pq[wave][4 * kPRow + r * kPRow + k];
-      float* gbc_w = &sm.pq[wave][(r & 1) * kGcOff + (r >> 1) * kT * 16];
       float xb[kT], yc[kT];
-      rev_steps(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n, A2, ia, hprev,
-                hh, ee, lam, e_next, ga, pw, qw, xb, yc, r & 1);
-      // dB and dC of each step, summed over channel pairs (independent of one another, so the
-      // row swaps of different steps overlap); stored below, over the partial tiles
-      float gpair[kT];
-#pragma unroll
-      for (int t = 0; t < kT; ++t) gpair[t] = sum_row_pairs2(xb[t], yc[t]);
-      wave_lds_sync();
       float gdt = 0.0f, gx = 0.0f;
-      {
-        const int own_slot = r * kPRow + (k ^ (kPSwap * (r & 1))) * kPTau;
-        const float* pr = &sm.pq[wave][own_slot];
-        const float* qr = &sm.pq[wave][4 * kPRow + own_slot];
+      if constexpr (NL == 1) {
+        rev_steps<false>(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n[0],
+                         A2[0], ia[0], hprev[0], hh, ee, lam[0], e_next[0], ga[0], pw, qw, acc,
+                         acc, xb, yc, r & 1);
+        // dB and dC of each step, summed over channel pairs (independent of one another, so
+        // the row swaps of different steps overlap); stored below, over the partial tiles
+        float gpair[kT];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          gdt += pr[i];
-          gx += qr[i];
+        for (int t = 0; t < kT; ++t) gpair[t] = sum_row_pairs2(xb[t], yc[t]);
+        wave_lds_sync();
+        {
+          const float* pr = &sm.pq[wave][own_slot];
+          const float* qr = &sm.pq[wave][4 * kPRow + own_slot];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            gdt += pr[i];
+            gx += qr[i];
+          }
         }
-        // first order: + u_t sum_n lam B, the input term of ddt (the exact hold's, e u B lam,
-        // is in the partial sums already)
-        if (!ZOH) gdt = fmaf(xu, gx, gdt);
-      }
-      wave_lds_sync();  // every lane of the wave has its sums: the tiles take dB and dC
+        wave_lds_sync();  // every lane of the wave has its sums: the tiles take dB and dC
 #pragma unroll
-      for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = gpair[t];
+        for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = gpair[t];
+      } else {
+        // state groups in turn: recompute the group's states (the sums of y are done), run its
+        // adjoint, accumulate its shares of the sums over states in registers, and reduce its
+        // dB and dC over the workgroup's channels (the partial tiles are free until the end)
+        float qacc[kT];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          acc[t] = 0.0f;
+          qacc[t] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          read_bc(buf, j, bcv);
+          rec_steps<2>(std::make_integer_sequence<int, kT>{}, bcv, dt, du, A2[j], ia[j],
+                       hprev[j], hh, ee, pw, acc, r & 1);
+          rev_steps<true>(std::make_integer_sequence<int, kT>{}, bcv, dt, du, xu, gy, a_n[j],
+                          A2[j], ia[j], hprev[j], hh, ee, lam[j], e_next[j], ga[j], pw, qw, acc,
+                          qacc, xb, yc, r & 1);
+          float gpair[kT];
+#pragma unroll
+          for (int t = 0; t < kT; ++t) gpair[t] = sum_row_pairs2(xb[t], yc[t]);
+#pragma unroll
+          for (int t = 0; t < kT; ++t) gbc_w[t * 16 + k] = gpair[t];
+          __syncthreads();  // every wave's dB and dC tiles of the group
+          reduce_bc(c, j);
+          __syncthreads();  // the tiles are rewritten by the next group
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+          const int slot = t * kPTau + ((t ^ kPSwap) - t) * kPTau * (r & 1);
+          pw[slot] = acc[t];
+          qw[slot] = qacc[t];
+        }
+        wave_lds_sync();
+        {
+          const float* pr = &sm.pq[wave][own_slot];
+          const float* qr = &sm.pq[wave][4 * kPRow + own_slot];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            gdt += pr[i];
+            gx += qr[i];
+          }
+        }
+      }
+      // first order: + u_t sum_n lam B, the input term of ddt (the exact hold's, e u B lam, is
+      // in the partial sums already)
+      if (!ZOH) gdt = fmaf(xu, gx, gdt);
       // the next chunk's tiles first: its wait for the loads would also wait for the stores below
       if (c > 0) stage(buf ^ 1);
       if (own_ok) {
@@ -274,26 +376,18 @@ struct BwdKernel {
         if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
       }
       __syncthreads();  // the wave tiles of dB and dC, and the next chunk's tiles, are complete
-      {
-        const int tau = tid >> 4, n = tid & 15;
-        float sb = 0.0f, sc = 0.0f;
-#pragma unroll
-        for (int pr = 0; pr < 8; ++pr) {
-          sb += sm.pq[pr >> 1][((pr & 1) * kT + tau) * 16 + n];
-          sc += sm.pq[pr >> 1][kGcOff + ((pr & 1) * kT + tau) * 16 + n];
-        }
-        if (a.part_bc) {  // this workgroup's sums for the chunk: 16 steps x 16 states x 2
-          const int64_t cb = d0 >> 4;
-          float* dst = a.part_bc + (((b * nchunks + c) * a.n_cblk + cb) * (kT * 16) + tid) * 2;
-          *reinterpret_cast<float2*>(dst) = make_float2(sb, sc);
-        }
+      if constexpr (NL == 1) {
+        reduce_bc(c, 0);
+        __syncthreads();  // the dB and dC tiles are rewritten by the next chunk
       }
-      __syncthreads();  // the dB and dC tiles are rewritten by the next chunk
       buf ^= 1;
     }
-    if (lane_ok) {
-      if (a.part_a) a.part_a[row * N + k] = ga;
-      if (a.dh0) a.dh0[row * N + k] = e_next * lam;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      if (ok_j[j]) {
+        if (a.part_a) a.part_a[row * N + k + 16 * j] = ga[j];
+        if (a.dh0) a.dh0[row * N + k + 16 * j] = e_next[j] * lam[j];
+      }
     }
     // sums over the row's 16 owner lanes
 #pragma unroll
@@ -307,11 +401,14 @@ struct BwdKernel {
     }
   }
 
-  // Recompute step: keep the state and the decay of every step, and the partial sum C.h.
-  template <int TAU>
+  // Recompute step: keep the state and the decay of every step; MODE 0 writes the partial sum
+  // C.h of y to the wave tile, MODE 1 adds it to acc (several state groups), MODE 2 only
+  // recomputes.
+  template <int TAU, int MODE>
   static __device__ __forceinline__ void rec_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float A2, float ia, float& h, float (&hh)[kT],
-                                                  float (&ee)[kT], float* pw, int odd) {
+                                                  float (&ee)[kT], float* pw, float (&acc)[kT],
+                                                  int odd) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
     const float cc = (TAU & 1) ? v.w : v.y;
@@ -322,29 +419,31 @@ struct BwdKernel {
     h = fmaf(e, h, ZOH ? inc * hold_gain(e, y, dtb, ia) : inc);
     hh[TAU] = h;
     ee[TAU] = e;
-    pw[TAU * kPTau + pslot_shift<TAU>(odd)] = cc * h;
+    if constexpr (MODE == 0) pw[TAU * kPTau + pslot_shift<TAU>(odd)] = cc * h;
+    else if constexpr (MODE == 1) acc[TAU] = fmaf(cc, h, acc[TAU]);
   }
-  template <int... TAUS>
+  template <int MODE, int... TAUS>
   static __device__ __forceinline__ void rec_steps(std::integer_sequence<int, TAUS...>,
                                                    const float4 (&bcv)[kT / 2], float dt,
                                                    float du, float A2, float ia, float hprev,
                                                    float (&hh)[kT], float (&ee)[kT], float* pw,
-                                                   int odd) {
+                                                   float (&acc)[kT], int odd) {
     float h = hprev;
-    (rec_step<TAUS>(bcv, dt, du, A2, ia, h, hh, ee, pw, odd), ...);
+    (rec_step<TAUS, MODE>(bcv, dt, du, A2, ia, h, hh, ee, pw, acc, odd), ...);
   }
 
   // Adjoint step TAU (taken in decreasing TAU): lam <- gy C + e_next lam, then the step's
   // contributions.  Partial sums over states go to the wave tiles pw (the A e h_prev part of ddt)
-  // and qw (lam B, which gives du and the u B part of ddt); dB and dC are summed over each pair of
-  // the wave's channels (rows) after the chain (xb, yc), rows 0 and 2 storing dB and rows 1
-  // and 3 dC.
-  template <int TAU>
+  // and qw (lam B, which gives du and the u B part of ddt), or with ACC (several state groups)
+  // are added to pacc and qacc; dB and dC are summed over each pair of the wave's channels
+  // (rows) after the chain (xb, yc), rows 0 and 2 storing dB and rows 1 and 3 dC.
+  template <int TAU, bool ACC>
   static __device__ __forceinline__ void rev_step(const float4 (&bcv)[kT / 2], float dt, float du,
                                                   float xu, float gy, float a_n, float A2,
                                                   float ia, float hprev, const float (&hh)[kT],
                                                   const float (&ee)[kT], float& lam,
                                                   float& e_next, float& ga, float* pw, float* qw,
+                                                  float (&pacc)[kT], float (&qacc)[kT],
                                                   float (&xb)[kT], float (&yc)[kT], int odd) {
     const float4 v = bcv[TAU / 2];
     const float bb = (TAU & 1) ? v.z : v.x;
@@ -357,41 +456,50 @@ struct BwdKernel {
     const float dub = row_bcast<TAU>(du);
     ga = fmaf(dtb, rr, ga);
     const float qq = lam * bb;
+    float pv, qv;
     if constexpr (ZOH) {
       // dub is u here; the gain g and its derivative in A come from the recomputed decay
       const float y = dtb * A2;
       const float g = hold_gain(ee[TAU], y, dtb, ia);
       ga = fmaf(qq * dub, hold_gain_da(ee[TAU], y, dtb, ia), ga);
-      pw[TAU * kPTau + pslot_shift<TAU>(odd)] = fmaf(a_n, rr, qq * ee[TAU] * dub);
-      qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qq * g;
+      pv = fmaf(a_n, rr, qq * ee[TAU] * dub);
+      qv = qq * g;
       xb[TAU] = lam * g * dub;
     } else {
-      pw[TAU * kPTau + pslot_shift<TAU>(odd)] = a_n * rr;
-      qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qq;
+      pv = a_n * rr;
+      qv = qq;
       xb[TAU] = lam * dub;  // this channel's dB and dC terms, summed over channel pairs after
     }                       // the chain
+    if constexpr (ACC) {
+      pacc[TAU] += pv;
+      qacc[TAU] += qv;
+    } else {
+      pw[TAU * kPTau + pslot_shift<TAU>(odd)] = pv;
+      qw[TAU * kPTau + pslot_shift<TAU>(odd)] = qv;
+    }
     yc[TAU] = gyb * hh[TAU];
     e_next = ee[TAU];
   }
-  template <int... TAUS>
+  template <bool ACC, int... TAUS>
   static __device__ __forceinline__ void rev_steps(std::integer_sequence<int, TAUS...>,
                                                    const float4 (&bcv)[kT / 2], float dt,
                                                    float du, float xu, float gy, float a_n,
                                                    float A2, float ia, float hprev,
                                                    const float (&hh)[kT], const float (&ee)[kT],
                                                    float& lam, float& e_next, float& ga, float* pw,
-                                                   float* qw, float (&xb)[kT], float (&yc)[kT],
-                                                   int odd) {
+                                                   float* qw, float (&pacc)[kT],
+                                                   float (&qacc)[kT], float (&xb)[kT],
+                                                   float (&yc)[kT], int odd) {
     // fold over the steps in decreasing order
-    (rev_step<kT - 1 - TAUS>(bcv, dt, du, xu, gy, a_n, A2, ia, hprev, hh, ee, lam, e_next, ga,
-                             pw, qw, xb, yc, odd),
+    (rev_step<kT - 1 - TAUS, ACC>(bcv, dt, du, xu, gy, a_n, A2, ia, hprev, hh, ee, lam, e_next,
+                                  ga, pw, qw, pacc, qacc, xb, yc, odd),
      ...);
   }
 };
 
-template <class IO, bool GATE, bool VEC, bool ZOH>
+template <class IO, bool GATE, bool VEC, bool ZOH, int NL>
 __global__ void __launch_bounds__(kBwdThreads) scan_bwd_kernel(BwdArgs a) {
-  BwdKernel<IO, GATE, VEC, ZOH>::run(a);
+  BwdKernel<IO, GATE, VEC, ZOH, NL>::run(a);
 }
 
 __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
@@ -399,34 +507,37 @@ __global__ void __launch_bounds__(256) zero_kernel(float* p, int64_t n) {
     p[i] = 0.0f;
 }
 
-// dB and dC of one (batch row, chunk): thread (step, state) adds the n_cblk workgroup partials
-// in channel-block order.
-__global__ void __launch_bounds__(256) reduce_bc_kernel(BwdArgs a, int64_t nchunks) {
+// dB and dC of one (batch row, chunk): each output (step, state) adds the n_cblk workgroup
+// partials (16 steps x np padded states x 2 each) in channel-block order.
+__global__ void __launch_bounds__(256) reduce_bc_kernel(BwdArgs a, int64_t nchunks, int np) {
   const int64_t bc = blockIdx.x;  // b * nchunks + c
   const int64_t b = bc / nchunks, c = bc - b * nchunks;
-  const int tid = threadIdx.x, tau = tid >> 4, n = tid & 15;
-  const float2* src = reinterpret_cast<const float2*>(a.part_bc) + bc * a.n_cblk * (kT * 16) + tid;
-  float sb = 0.0f, sc = 0.0f;
-  int64_t cb = 0;
-  for (; cb + 8 <= a.n_cblk; cb += 8) {  // eight loads in flight, added in order
-    float2 v[8];
+  const int64_t blk = int64_t(kT) * np;  // float2 per partial
+  for (int idx = threadIdx.x; idx < kT * np; idx += 256) {
+    const int tau = idx / np, n = idx - tau * np;
+    const float2* src = reinterpret_cast<const float2*>(a.part_bc) + bc * a.n_cblk * blk + idx;
+    float sb = 0.0f, sc = 0.0f;
+    int64_t cb = 0;
+    for (; cb + 8 <= a.n_cblk; cb += 8) {  // eight loads in flight, added in order
+      float2 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = src[(cb + j) * (kT * 16)];
+      for (int j = 0; j < 8; ++j) v[j] = src[(cb + j) * blk];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sb += v[j].x;
-      sc += v[j].y;
+      for (int j = 0; j < 8; ++j) {
+        sb += v[j].x;
+        sc += v[j].y;
+      }
     }
-  }
-  for (; cb < a.n_cblk; ++cb) {
-    const float2 v = src[cb * (kT * 16)];
-    sb += v.x;
-    sc += v.y;
-  }
-  const int64_t t = c * kT + tau;
-  if (t < a.seqlen && n < a.d_state) {
-    a.dB[(b * a.seqlen + t) * a.d_state + n] = sb;
-    a.dC[(b * a.seqlen + t) * a.d_state + n] = sc;
+    for (; cb < a.n_cblk; ++cb) {
+      const float2 v = src[cb * blk];
+      sb += v.x;
+      sc += v.y;
+    }
+    const int64_t t = c * kT + tau;
+    if (t < a.seqlen && n < a.d_state) {
+      a.dB[(b * a.seqlen + t) * a.d_state + n] = sb;
+      a.dC[(b * a.seqlen + t) * a.d_state + n] = sc;
+    }
   }
 }
 
@@ -460,21 +571,30 @@ hipError_t zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <class IO, bool ZOH>
-void launch_io(const BwdArgs& a, hipStream_t stream) {
-  if (a.batch * a.n_cblk == 0) return;  // nothing but the zeroed sums
+template <class IO, bool ZOH, int NL>
+void launch_nl(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.batch * a.n_cblk)), block(kBwdThreads);
   if (a.vec_io) {
     if (a.z)
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, true, ZOH>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, true, ZOH, NL>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, true, ZOH>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, true, ZOH, NL>), grid, block, 0, stream, a);
   } else {
     if (a.z)
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, false, ZOH>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, true, false, ZOH, NL>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, false, ZOH>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((scan_bwd_kernel<IO, false, false, ZOH, NL>), grid, block, 0, stream, a);
   }
+}
+
+// State groups of 16 per lane: 1 (d_state <= 16), 2 (<= 32) or 4 (<= 64, the padding states of
+// 33..48 read 0 and stay 0).
+template <class IO, bool ZOH>
+void launch_io(const BwdArgs& a, hipStream_t stream) {
+  if (a.batch * a.n_cblk == 0) return;  // nothing but the zeroed sums
+  if (a.d_state <= 16) launch_nl<IO, ZOH, 1>(a, stream);
+  else if (a.d_state <= 32) launch_nl<IO, ZOH, 2>(a, stream);
+  else launch_nl<IO, ZOH, 4>(a, stream);
 }
 
 }  // namespace
@@ -498,7 +618,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     const int64_t nchunks = (a.seqlen + kT - 1) / kT;
     if (a.batch * nchunks > 0)
       hipLaunchKernelGGL(reduce_bc_kernel, dim3(static_cast<unsigned>(a.batch * nchunks)),
-                         dim3(256), 0, stream, a, nchunks);
+                         dim3(256), 0, stream, a, nchunks, bwd_states_padded(a.d_state));
     const int64_t items = a.d_inner * N + 2 * a.d_inner;
     const int64_t blocks = (items + 255) / 256 < 4096 ? (items + 255) / 256 : 4096;
     if (blocks > 0)

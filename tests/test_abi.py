@@ -133,7 +133,7 @@ def _bwd(lib, **kw):
 
 
 def test_backward_argument_errors_before_launch(lib):
-    assert _bwd(lib, N=32) == ops.SS_ERR_UNSUPPORTED
+    assert _bwd(lib, N=65) == ops.SS_ERR_UNSUPPORTED
     assert _bwd(lib, flags=ops.SS_FLAG_ZOH_EXACT | ops.SS_FLAG_STATES_GIVEN) == \
         ops.SS_ERR_UNSUPPORTED                                       # exact hold: no given states
     assert _bwd(lib, flags=ops.SS_FLAG_ZOH_EXACT, dout=None) == ops.SS_ERR_INVALID_ARG
@@ -152,7 +152,12 @@ def test_backward_argument_errors_before_launch(lib):
     assert need == up(up(up(up(16 * 16 * 4) + 16 * 16 * 2 * 4) + 16 * 16 * 4) + 16 * 4) + 256
     assert _bwd(lib, wsb=need - 4) == ops.SS_ERR_INVALID_ARG
     assert _bwd(lib, ws=FAKE * 12 + 8, wsb=need) == ops.SS_ERR_UNSUPPORTED  # misaligned
-    assert lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 17, ops.SS_BF16) == 0
+    assert lib.ss_scan_bwd_workspace_bytes(1, 4, 16, 65, ops.SS_BF16) == 0
+    # wider states: 32 and 64 padded states in the partial sums
+    up = lambda x: (x + 255) // 256 * 256
+    for n, npad in ((20, 32), (40, 64), (64, 64)):
+        want = up(up(up(up(16 * n * 4) + 16 * npad * 2 * 4) + 16 * n * 4) + 16 * 4) + 256
+        assert lib.ss_scan_bwd_workspace_bytes(1, 4, 16, n, ops.SS_BF16) == want, n
 
 
 def _fwd_states(lib, **kw):

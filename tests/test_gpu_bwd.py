@@ -103,7 +103,7 @@ def test_bf16_ragged_bwd(batch, seqlen, d_inner):
     run_bwd(p, seed=seqlen)
 
 
-@pytest.mark.parametrize("d_state", [1, 5, 16])
+@pytest.mark.parametrize("d_state", [1, 5, 16, 17, 24, 32, 33, 40, 64])
 def test_state_sizes_bwd(d_state):
     p = wl.make_prefill(wl.WORKLOADS[0], batch=2, seqlen=70, d_inner=24, seed=d_state)
     rng = np.random.default_rng(d_state)
@@ -166,6 +166,43 @@ def test_zoh_bwd_bf16_and_repeatable():
         assert torch.equal(g1[key], g2[key]), key
 
 
+@pytest.mark.parametrize("d_state", [32, 64])
+def test_wide_state_bwd_bf16_with_given_states(d_state):
+    """Wide states (two and four groups of 16 per lane) in bf16 with the gate, through both the
+    recomputing backward and the one taking the states a forward saved, and repeatable."""
+    p = wl.make_prefill(wl.WORKLOADS[1], batch=2, seqlen=200, d_inner=48, seed=d_state)
+    rng = np.random.default_rng(d_state)
+    mk = lambda: wl.f32_to_bf16_bits(rng.standard_normal((2, 200, d_state)).astype(np.float32))
+    p["B"], p["C"] = mk(), mk()
+    p["A"] = np.ascontiguousarray(np.tile(-np.arange(1, d_state + 1, dtype=np.float32), (48, 1)))
+    g1, ref = run_bwd(p, seed=d_state)
+    o = ops()
+    args = [dev(p[k]) for k in ("u", "delta", "A", "B", "C")]
+    kw = dict(D=dev(p["D"]), z=dev(p["z"]), delta_bias=dev(p["delta_bias"]))
+    g_out = dev(wl.f32_to_bf16_bits(np.random.default_rng(d_state).standard_normal(
+        p["u"].shape).astype(np.float32)))
+    ws, states = o.bwd_workspace(2, 200, 48, d_state, torch.bfloat16)
+    o.scan_fwd_states(*args, states=states, **kw)
+    g_s = o.scan_bwd(*args, g_out, workspace=ws, states_given=True, **kw)
+    g_r = o.scan_bwd(*args, g_out, **kw)
+    g_r2 = o.scan_bwd(*args, g_out, **kw)
+    torch.cuda.synchronize()
+    for key in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert torch.equal(g_r[key], g_r2[key]), key
+        tol = 2e-2 if key in ("du", "ddelta", "dz") else 1e-4
+        check_grad(host(g_s[key]), host(g_r[key]), tol, key + " (given vs recomputed)")
+
+
+@pytest.mark.parametrize("d_state", [24, 64])
+def test_wide_state_zoh_bwd(d_state):
+    p = wl.make_prefill(wl.WORKLOADS[0], batch=2, seqlen=40, d_inner=20, seed=d_state)
+    rng = np.random.default_rng(d_state)
+    p["B"] = rng.standard_normal((2, 40, d_state)).astype(np.float32)
+    p["C"] = rng.standard_normal((2, 40, d_state)).astype(np.float32)
+    p["A"] = (-np.exp(rng.uniform(np.log(1e-2), np.log(20.0), size=(20, d_state)))).astype(np.float32)
+    run_bwd(p, gate=False, zoh=True, seed=d_state)
+
+
 def test_zoh_bwd_rejects_given_states():
     o = ops()
     p = wl.make_prefill(wl.WORKLOADS[0], batch=1, seqlen=8, d_inner=16, seed=1)
@@ -219,10 +256,10 @@ def test_invalid_bwd_arguments():
     p = wl.make_prefill(wl.WORKLOADS[0], batch=1, seqlen=8, d_inner=16, seed=1)
     args = [dev(p[k]) for k in ("u", "delta", "A", "B", "C")]
     g_out = dev(p["u"])
-    # d_state above 16
-    B32 = torch.zeros((1, 8, 32), device="cuda")
+    # d_state above 64
+    B72 = torch.zeros((1, 8, 72), device="cuda")
     with pytest.raises(o.SSError) as e:
-        o.scan_bwd(args[0], args[1], torch.zeros((16, 32), device="cuda"), B32, B32.clone(), g_out)
+        o.scan_bwd(args[0], args[1], torch.zeros((16, 72), device="cuda"), B72, B72.clone(), g_out)
     assert e.value.status == o.SS_ERR_UNSUPPORTED
     # workspace too small
     with pytest.raises(o.SSError) as e:
