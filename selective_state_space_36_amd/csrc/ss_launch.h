@@ -54,7 +54,7 @@ struct ScanArgs {
 // is addressed with 32-bit byte offsets, so the host admits that path only when kDecodeRows
 // rows of the state stay under 2^31 bytes).
 #ifndef SS_DECODE_ROWS
-#define SS_DECODE_ROWS 4
+#define SS_DECODE_ROWS 8
 #endif
 constexpr int kDecodeRows = SS_DECODE_ROWS;
 
