@@ -82,8 +82,10 @@ struct ScanKernel {
   // the owner adding 16 products (31 instructions per chunk -> 17).  Wider states keep the
   // per-lane partial sums: their states would not fit the per-wave tile.
   static constexpr bool FOLD = NL == 1 && !SUMMARY;
-  // One state per lane: B and C in tiles of their own (a summary pass stages only B).
-  static constexpr bool SPLIT = NL == 1;
+  // B in a tile of its own, four steps per 16-byte read: with one state per lane (C then in a
+  // tile of its own as well, read as rows by the owner lanes) and in every summary pass, which
+  // never forms C . h and so neither loads nor stages C.
+  static constexpr bool SPLIT = NL == 1 || SUMMARY;
   // The 16-byte pieces of row (step) k of a u/delta/z/out tile are stored XOR-permuted by
   // (k / (8 / PIECES)) mod PIECES.  The owner lanes of steps 4 (bf16) or 2 (fp32) apart read the
   // same column of rows that share LDS banks (rows are 32 or 64 bytes; LDS has 32 banks of 4
@@ -99,8 +101,11 @@ struct ScanKernel {
     float b[2][kT][kSRow];  // B_t[n] per chunk, row n (read by the lane of state n)
     float c[2][kT][kSRow];  // C_t[n] per chunk, row t (read by the owner lane of step t)
   };
+  struct BTile {
+    float b[2][NP][kSRow];  // B_t[n] per chunk, row n (summary passes)
+  };
   struct alignas(16) Smem {
-    std::conditional_t<SPLIT, SplitTile, PairTile> bt;
+    std::conditional_t<FOLD, SplitTile, std::conditional_t<SUMMARY, BTile, PairTile>> bt;
     uint4 in[2][NTEN][kT][PIECES];  // raw u, delta, z tiles per chunk
     uint4 out[2][kT][PIECES];       // raw output tile per chunk
     float p[kWaves][4 * kPRow];     // per-wave partial sums or states [row][step][lane]
@@ -257,7 +262,7 @@ struct ScanKernel {
 #pragma unroll
       for (int i = 0; i < BC_PER_THREAD; ++i) {
         pre.rb[i] = buf_load<elem>(rb, bc_off[i]);
-        pre.rc[i] = buf_load<elem>(rc, bc_off[i]);
+        if constexpr (!SUMMARY) pre.rc[i] = buf_load<elem>(rc, bc_off[i]);
       }
       if (wave_u < NTEN) {  // uniform
         const rsrc_t ri = io_buf(in_base, ci);
@@ -277,7 +282,7 @@ struct ScanKernel {
       for (int i = 0; i < BC_PER_THREAD; ++i) {
         if constexpr (SPLIT) {
           sm.bt.b[buf][bc_n[i]][bc_tau[i]] = IO::widen(pre.rb[i]);
-          if constexpr (!SUMMARY) sm.bt.c[buf][bc_tau[i]][bc_n[i]] = IO::widen(pre.rc[i]);
+          if constexpr (FOLD) sm.bt.c[buf][bc_tau[i]][bc_n[i]] = IO::widen(pre.rc[i]);
         } else {
           sm.bt.bc[buf][bc_n[i]][bc_tau[i]] =
               make_float2(IO::widen(pre.rb[i]), IO::widen(pre.rc[i]));
@@ -480,8 +485,9 @@ struct ScanKernel {
   }
 
   // One recurrence step (TAU of the chunk) for this lane's states.  bcv holds the chunk's
-  // (B, C) pairs for this lane's states, two steps per float4 (with one state per lane: B only,
-  // four steps per float4; with FOLD the lane stores its new state instead of C_t[n] h_t[n]).
+  // (B, C) pairs for this lane's states, two steps per float4 (with one state per lane and in
+  // summary passes: B only, four steps per float4; with FOLD the lane stores its new state
+  // instead of C_t[n] h_t[n]).
   template <int TAU>
   static __device__ __forceinline__ void step(Smem& sm, const float4 (&bcv)[NL][kT / 2],
                                               float dt, float du, const float (&A2)[NL],
@@ -535,7 +541,7 @@ struct ScanKernel {
       if constexpr (SPLIT) {
 #pragma unroll
         for (int i = 0; i < kT / 4; ++i)
-          bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bt.b[buf][k][4 * i]);
+          bcv[j][i] = *reinterpret_cast<const float4*>(&sm.bt.b[buf][k + 16 * j][4 * i]);
       } else {
 #pragma unroll
         for (int i = 0; i < kT / 2; ++i)
