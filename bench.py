@@ -8,6 +8,10 @@ Sections, in the order they run:
   cold_start  the first W + K launches of the main prefill on a GPU that has been idle: its clock
               is still ramping up (per-dispatch cycle counts are constant while the duration
               falls), reported as measured;
+  clock_settle  untimed launches of the main prefill, in blocks of 10, until the per-launch time
+              stops falling (two block-to-block changes under 1 %, at least 60 and at most 400
+              launches);
+  main        W untimed + K timed steps of the 2.8B layer -> value, roofline;
   decode      the batch-128 single-token step (ss_state_update) 1000 times back to back: inputs
               pre-generated in one arena as stated (every step reads fresh addresses), the same
               from a HIP graph, 8 rotating states, inputs in fixed buffers refreshed each step
@@ -16,8 +20,6 @@ Sections, in the order they run:
   variants    the exact hold, the fused front end, the backward and the training path on the
               2.8B layer;
   workloads   the Mamba-130M-shaped and the 2^20-step layers, each through ss_scan_fwd;
-  main        W untimed + K timed steps of the 2.8B layer -> value, roofline (by now the clock
-              has settled);
   parity      every row of the 130M and 2.8B layers and sampled rows of the 2^20-step layer
               against the fp64 oracle, and 100 decode steps on every row;
   cpu_baseline  the fp64 C oracle on this host's cores on the 2.8B layer.
@@ -185,6 +187,22 @@ def timed(torch, stream, fn, warmup, steps, per_launch=True):
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / max(steps, 1), [a.elapsed_time(b) for a, b in ev]
+
+
+def clock_settle(torch, stream, fn, block=10, min_launches=60, max_launches=400, tol=0.01):
+    """Untimed launches of fn, `block` at a time, until the mean per-launch time has changed by
+    less than `tol` over each of the last two blocks (at least `min_launches`, at most
+    `max_launches`).  Under sustained load the GPU raises its clock over the first tens of
+    milliseconds while the cycles per launch stay the same; the timed steps then measure the
+    kernel, not the ramp.  Returns the block means in microseconds."""
+    means = []
+    while len(means) * block < max_launches:
+        _, per = timed(torch, stream, fn, 0, block)
+        means.append(sum(per) / len(per) * 1e3)
+        if (len(means) * block >= min_launches and len(means) >= 3 and
+                all(abs(means[-i] - means[-i - 1]) < tol * means[-i - 1] for i in (1, 2))):
+            break
+    return means
 
 
 class Prefill:
@@ -622,6 +640,19 @@ def main():
             note="the main prefill's first W + K launches on an idle GPU: the clock ramps up "
                  "over the first ~100 launches (per-dispatch cycle counts stay constant)")
         log(f"cold start: {extra['cold_start']}")
+
+    # the main timed region, once the clock has settled
+    means = clock_settle(torch, stream, main_pf.step)
+    settle = dict(launches=10 * len(means), block_us=[round(m, 1) for m in means],
+                  rule="blocks of 10 untimed launches until two consecutive block-to-block "
+                       "changes are under 1 % (at least 60, at most 400 launches)")
+    log(f"clock settle: {settle['launches']} launches, blocks {settle['block_us']}")
+    log(f"main: warmup {args.warmup}, timed {args.steps}")
+    ms_step, per = timed(torch, stream, main_pf.step, args.warmup, args.steps)
+    line = main_pf.line(ms_step, per)
+    log(f"prefill {ms_step * 1e3:.1f} us/step (kernel avg {line['kernel_us']} us)")
+    ms_kernel = line["kernel_us"] * 1e-3
+
     if "decode" in sec:
         extra["decode"] = bench_decode(args, torch, np, ops, wl, stream)
     if "multihead" in sec:
@@ -641,13 +672,6 @@ def main():
             extra["workloads"][pf.w.name]["kernels"] = (
                 "summary pass + output pass (time split)" if pf.ws_bytes else "output pass")
             log(f"{pf.w.name}: {extra['workloads'][pf.w.name]['us_per_call']} us per call")
-
-    # the main timed region
-    log(f"main: warmup {args.warmup}, timed {args.steps}")
-    ms_step, per = timed(torch, stream, main_pf.step, args.warmup, args.steps)
-    line = main_pf.line(ms_step, per)
-    log(f"prefill {ms_step * 1e3:.1f} us/step (kernel avg {line['kernel_us']} us)")
-    ms_kernel = line["kernel_us"] * 1e-3
 
     if "parity" in sec:
         par = {}
@@ -699,8 +723,10 @@ def main():
                 "exp_peak_per_s": PEAK_VALU_SLOTS / 2,
                 "exp_frac": round(w.elements * (w.d_state + (2 if w.gate else 1))
                                   / ms_kernel / (PEAK_VALU_SLOTS / 2), 4)},
-        "order": "the timed steps run last, after the sections below (the GPU clock has "
-                 "settled); cold_start holds the same kernel's first launches on an idle GPU",
+        "order": "cold_start (the kernel's first W + K launches on an idle GPU), then "
+                 "clock_settle (untimed launches until the per-launch time stops falling), then "
+                 "the W untimed and K timed steps; the other sections run after them",
+        "clock_settle": settle,
     }
     result.update(extra)
     if "cpu" in sec:
