@@ -237,8 +237,24 @@ struct BwdKernel {
         *reinterpret_cast<float2*>(dst) = make_float2(sb, sc);
       }
     };
+    // the state at the start of chunk c: the stored end state of chunk c - 1, or h0
+    auto load_start = [&](int c, float (&hs)[NL]) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        if (c > 0) hs[j] = ok_j[j] ? ck_lane[int64_t(c - 1) * ck_chunk + 16 * j] : 0.0f;
+        else hs[j] = (a.h0 && ok_j[j]) ? a.h0[row * N + k + 16 * j] : 0.0f;
+      }
+    };
+    // loaded a chunk ahead, like the input tiles: a load issued at the chunk's start and used at
+    // once would expose its latency in every chunk
+    float hnext[NL];
+    if (nchunks > 0) load_start(nchunks - 1, hnext);
     for (int c = nchunks - 1; c >= 0; --c) {
       if (c > 0) issue(c - 1);
+      float hprev[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) hprev[j] = hnext[j];
+      if (c > 0) load_start(c - 1, hnext);
       const int nv = nvalid_of(c);
       const bool own_ok = chan_ok && k < nv;
       const float xu = own(buf, 0);
@@ -247,12 +263,6 @@ struct BwdKernel {
       dt = own_ok ? dt : 0.0f;
       // first order: the input term is (dt u) B; exact hold: u B times the gain
       const float du = own_ok ? (ZOH ? xu : dt * xu) : 0.0f;
-      float hprev[NL];
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        if (c > 0) hprev[j] = ok_j[j] ? ck_lane[int64_t(c - 1) * ck_chunk + 16 * j] : 0.0f;
-        else hprev[j] = (a.h0 && ok_j[j]) ? a.h0[row * N + k + 16 * j] : 0.0f;
-      }
 
       // recompute the chunk: states, decays and the partial sums C.h of y
       float4 bcv[kT / 2];
