@@ -147,12 +147,30 @@ struct BwdKernel {
       bc_off[j] = bc_n + 16 * j < N ? static_cast<uint32_t>((bc_tau * N + bc_n + 16 * j) * ES)
                                     : kOffNone;
 
+    // chunk-end states, (batch, chunk, d_inner, d_state): the workgroup's 16 channels of a chunk
+    // are contiguous.  Read through a buffer over those channels (and over h0's for the first
+    // chunk), so that states past d_state or channels past d_inner read 0 without a select.
+    const uint32_t st_bytes = static_cast<uint32_t>((D - d0 < 16 ? D - d0 : 16) * N * 4);
+    uint32_t st_off[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      st_off[j] = ok_j[j] ? static_cast<uint32_t>((cl * N + k + 16 * j) * 4) : kOffNone;
+
     // Global loads of chunk c go to registers (issued before the current chunk is computed) and
-    // are written to LDS buffer `buf` after it.
+    // are written to LDS buffer `buf` after it; the state at the chunk's start (the stored end
+    // state of chunk c - 1, or h0) goes to hcur there.  Nothing loaded here is used before that
+    // point, so no load's latency shows in the chunk that issues it: B and C stay in the io type
+    // until then, and the start state is taken over only once the tile loads have arrived.
     elem pv[PIECE_E];
     uint4 pvv{0, 0, 0, 0};
-    float pbv[NL], pcv[NL];
+    elem pbv[NL], pcv[NL];
+    float hld[NL], hcur[NL];
     auto issue = [&](int c) {
+      const rsrc_t rs = c > 0 ? make_buf(a.ck + ((b * nchunks + c - 1) * D + d0) * N, st_bytes)
+                              : make_buf(a.h0 ? a.h0 + (b * D + d0) * N : a.ck,
+                                         a.h0 ? st_bytes : 0u);
+#pragma unroll
+      for (int j = 0; j < NL; ++j) hld[j] = buf_load<float>(rs, st_off[j]);
       const int nv = nvalid_of(c);
       const int64_t t0 = int64_t(c) * kT;
       const uint32_t io_bytes = static_cast<uint32_t>((nv * D - d0) * ES);
@@ -171,8 +189,8 @@ struct BwdKernel {
       const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        pbv[j] = IO::widen(buf_load<elem>(rb, bc_off[j]));
-        pcv[j] = IO::widen(buf_load<elem>(rc, bc_off[j]));
+        pbv[j] = buf_load<elem>(rb, bc_off[j]);
+        pcv[j] = buf_load<elem>(rc, bc_off[j]);
       }
     };
     auto stage = [&](int buf) {
@@ -186,7 +204,11 @@ struct BwdKernel {
         }
       }
 #pragma unroll
-      for (int j = 0; j < NL; ++j) sm.bc[buf][bc_n + 16 * j][bc_tau] = make_float2(pbv[j], pcv[j]);
+      for (int j = 0; j < NL; ++j) {
+        sm.bc[buf][bc_n + 16 * j][bc_tau] = make_float2(IO::widen(pbv[j]), IO::widen(pcv[j]));
+        hcur[j] = hld[j];
+        asm volatile("" ::"v"(hcur[j]));  // the load is complete here, not in the next chunk
+      }
     };
     const int own_col = ((cl / PIECE_E) ^ pswz(k)) * PIECE_E + cl % PIECE_E;
     auto own = [&](int buf, int ten) -> float { return IO::widen(sm.in[buf][ten][k][own_col]); };
@@ -196,10 +218,6 @@ struct BwdKernel {
         bcv[i] = *reinterpret_cast<const float4*>(&sm.bc[buf][k + 16 * j][2 * i]);
     };
 
-    // chunk-end states, (batch, chunk, d_inner, d_state): the wave's four channels of a chunk are
-    // contiguous
-    const float* ck_lane = a.ck + ((b * nchunks) * D + d) * N + k;
-    const int64_t ck_chunk = D * N;
     int buf = 0;
     if (nchunks > 0) {  // the last chunk first
       issue(nchunks - 1);
@@ -237,24 +255,11 @@ struct BwdKernel {
         *reinterpret_cast<float2*>(dst) = make_float2(sb, sc);
       }
     };
-    // the state at the start of chunk c: the stored end state of chunk c - 1, or h0
-    auto load_start = [&](int c, float (&hs)[NL]) {
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        if (c > 0) hs[j] = ok_j[j] ? ck_lane[int64_t(c - 1) * ck_chunk + 16 * j] : 0.0f;
-        else hs[j] = (a.h0 && ok_j[j]) ? a.h0[row * N + k + 16 * j] : 0.0f;
-      }
-    };
-    // loaded a chunk ahead, like the input tiles: a load issued at the chunk's start and used at
-    // once would expose its latency in every chunk
-    float hnext[NL];
-    if (nchunks > 0) load_start(nchunks - 1, hnext);
     for (int c = nchunks - 1; c >= 0; --c) {
-      if (c > 0) issue(c - 1);
       float hprev[NL];
 #pragma unroll
-      for (int j = 0; j < NL; ++j) hprev[j] = hnext[j];
-      if (c > 0) load_start(c - 1, hnext);
+      for (int j = 0; j < NL; ++j) hprev[j] = hcur[j];
+      if (c > 0) issue(c - 1);
       const int nv = nvalid_of(c);
       const bool own_ok = chan_ok && k < nv;
       const float xu = own(buf, 0);
