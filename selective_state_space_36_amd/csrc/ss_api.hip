@@ -494,8 +494,10 @@ ss_status bwd_impl(const void* u, const void* delta, const float* A, const void*
   a.d_state = static_cast<int32_t>(d_state);
   a.softplus = delta_softplus ? 1 : 0;
   a.zoh = (flags & SS_FLAG_ZOH_EXACT) ? 1 : 0;
+  // 16-byte tile loads of u, delta, z, dout and 16-byte tile stores of du, ddelta, dz
   a.vec_io = (d_inner % 16 == 0 && (d_inner * es) % 16 == 0 && aligned(u, 16) &&
-              aligned(delta, 16) && aligned(dout, 16) && (!z || aligned(z, 16))) ? 1 : 0;
+              aligned(delta, 16) && aligned(dout, 16) && (!z || aligned(z, 16)) &&
+              aligned(du, 16) && aligned(ddelta, 16) && (!dz || aligned(dz, 16))) ? 1 : 0;
   if (batch * a.n_cblk > int64_t(0x7fffffff))
     return fail(SS_ERR_INVALID_ARG, "too many workgroups (batch * d_inner too large)");
   hipStream_t st = static_cast<hipStream_t>(stream);

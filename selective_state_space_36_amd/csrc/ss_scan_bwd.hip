@@ -90,6 +90,7 @@ struct BwdKernel {
   struct alignas(16) Smem {
     float2 bc[2][NP][kT + 2];       // (B_t[n], C_t[n]) of the chunk, double-buffered
     elem in[2][4][kT][16];          // u, delta, z, dout tiles [buf][tensor][step][channel]
+    elem gout[3][kT][16];           // du, ddelta, dz of the chunk [tensor][step][channel]
     // per wave: partial sums over states, p (y, then ddt) at 0 and q (du) at 4 * kPRow; after
     // the owner sums, the dB and dC tiles of the wave's row pairs
     float pq[4][2 * 4 * kPRow];
@@ -384,13 +385,32 @@ struct BwdKernel {
       if (own_ok) {
         const float gdelta = a.softplus ? gdt * rcp_hw(1.0f + exp2_hw(-sv * kLog2e)) : gdt;
         gb_acc += gdelta;
-        const int64_t e = (row0 + int64_t(c) * kT + k) * D + d;
-        static_cast<elem*>(a.du)[e] =
-            IO::from_float(ZOH ? fmaf(gy, dskip, gx) : fmaf(gx, dt, gy * dskip));
-        static_cast<elem*>(a.ddelta)[e] = IO::from_float(gdelta);
-        if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
+        const elem gu = IO::from_float(ZOH ? fmaf(gy, dskip, gx) : fmaf(gx, dt, gy * dskip));
+        if (VEC) {  // into the chunk's gradient tiles, stored below as 16-byte pieces
+          sm.gout[0][k][own_col] = gu;
+          sm.gout[1][k][own_col] = IO::from_float(gdelta);
+          if (GATE) sm.gout[2][k][own_col] = IO::from_float(gz);
+        } else {
+          const int64_t e = (row0 + int64_t(c) * kT + k) * D + d;
+          static_cast<elem*>(a.du)[e] = gu;
+          static_cast<elem*>(a.ddelta)[e] = IO::from_float(gdelta);
+          if (GATE) static_cast<elem*>(a.dz)[e] = IO::from_float(gz);
+        }
       }
       __syncthreads();  // the wave tiles of dB and dC, and the next chunk's tiles, are complete
+      // Waves 0, 1 (and 2 with the gate) store the du, ddelta (and dz) tiles, one 16-byte piece
+      // per lane through a buffer over the chunk's valid steps: 2-byte stores from the owner
+      // lanes touched 16 rows per instruction, and their issue held up the next chunk's loads.
+      // The reads are done before the next barrier, after which the tiles are written again.
+      if (VEC && wave_u < (GATE ? 3 : 2) && tl_on) {
+        void* dst = wave_u == 0 ? a.du : (wave_u == 1 ? a.ddelta : a.dz);
+        const uint32_t io_bytes = static_cast<uint32_t>((nvalid_of(c) * D - d0) * ES);
+        const rsrc_t ro = make_buf(
+            static_cast<char*>(dst) + ((row0 + int64_t(c) * kT) * D + d0) * ES, io_bytes);
+        buf_store(*reinterpret_cast<const uint4*>(
+                      &sm.gout[wave_u][tl_row][(tl_pc ^ pswz(tl_row)) * PIECE_E]),
+                  ro, tl_off);
+      }
       if constexpr (NL == 1) {
         reduce_bc(c, 0);
         __syncthreads();  // the dB and dC tiles are rewritten by the next chunk
