@@ -220,8 +220,9 @@ struct ScanKernel {
     const bool tl_on = lane < kT * PIECES;
     const uint32_t tl_off =
         tl_on ? static_cast<uint32_t>((tl_row * D + tl_pc * (16 / ES)) * ES) : kOffNone;
-    const char* in_base = static_cast<const char*>(wave_u == 0 ? a.u : (wave_u == 1 ? a.delta
-                                                                                     : a.z));
+    // wave w < NTEN loads tensor w; the other waves get a valid base they never load from
+    const char* in_base = static_cast<const char*>(
+        wave_u == 0 ? a.u : (wave_u == 1 ? a.delta : (wave_u == 2 && NTEN == 3 ? a.z : a.u)));
     const int64_t io_chunk_bytes = kT * D * ES;
     const int64_t io_off0 = (row0 * D + d0) * ES;  // byte offset of chunk 0's tiles
     int bc_tau[BC_PER_THREAD], bc_n[BC_PER_THREAD];
@@ -247,25 +248,37 @@ struct ScanKernel {
     // valid steps of chunk ci (kT except for a partial last chunk); uniform over the workgroup
     const int last_valid = static_cast<int>(t_end - t_begin - int64_t(nchunks - 1) * kT);
     auto nvalid_of = [&](int ci) { return ci == nchunks - 1 ? last_valid : kT; };
-    // The range ends with the last valid row: channels past d_inner in that row (reached only by
-    // the element path) read 0 and are not written.
-    auto io_buf = [&](const void* base, int ci) {
-      return make_buf(static_cast<const char*>(base) + io_off0 + int64_t(ci) * io_chunk_bytes,
-                      static_cast<uint32_t>((nvalid_of(ci) * D - d0) * ES));
-    };
+    // Tile bases advance by a fixed stride per chunk: running pointers in scalar registers, one
+    // add per chunk, rather than each chunk's 64-bit offsets recomputed from its index (some 40
+    // scalar instructions per chunk on every wave's critical path).  The io ranges end with the
+    // chunk's last valid row: channels past d_inner in that row (reached only by the element
+    // path) read 0 and are not written.
+    const int64_t bc_chunk_bytes = int64_t(kT) * N * ES;
+    const uint32_t bc_bytes_full = static_cast<uint32_t>(kT * N * ES);
+    const uint32_t bc_bytes_last = static_cast<uint32_t>(last_valid * N * ES);
+    const uint32_t io_bytes_full = static_cast<uint32_t>((kT * D - d0) * ES);
+    const uint32_t io_bytes_last = static_cast<uint32_t>((last_valid * D - d0) * ES);
+    const char* b_next = static_cast<const char*>(a.B) + row0 * N * ES;  // next chunk to load
+    const char* c_next = static_cast<const char*>(a.C) + row0 * N * ES;
+    const char* in_next = in_base + io_off0;
+    const char* out_next = SUMMARY ? nullptr : static_cast<const char*>(a.out) + io_off0;
 
     auto load_chunk = [&](int ci) {
-      const int64_t bc_off0 = ((row0 + int64_t(ci) * kT) * N) * ES;
-      const uint32_t bc_bytes = static_cast<uint32_t>(nvalid_of(ci) * N * ES);
-      const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + bc_off0, bc_bytes);
-      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + bc_off0, bc_bytes);
+      const bool last = ci == nchunks - 1;
+      const uint32_t bc_bytes = last ? bc_bytes_last : bc_bytes_full;
+      const rsrc_t rb = make_buf(b_next, bc_bytes);
+      const rsrc_t rc = make_buf(c_next, bc_bytes);
+      b_next += bc_chunk_bytes;
+      c_next += bc_chunk_bytes;
 #pragma unroll
       for (int i = 0; i < BC_PER_THREAD; ++i) {
         pre.rb[i] = buf_load<elem>(rb, bc_off[i]);
         if constexpr (!SUMMARY) pre.rc[i] = buf_load<elem>(rc, bc_off[i]);
       }
+      const char* in_cur = in_next;
+      in_next += io_chunk_bytes;
       if (wave_u < NTEN) {  // uniform
-        const rsrc_t ri = io_buf(in_base, ci);
+        const rsrc_t ri = make_buf(in_cur, last ? io_bytes_last : io_bytes_full);
         if (VEC) {
           pre.rin = buf_load<uint4>(ri, tl_off);
         } else {
@@ -299,8 +312,10 @@ struct ScanKernel {
         asm volatile("" ::"v"(st_val.x), "v"(st_val.y), "v"(st_val.z), "v"(st_val.w));
     };
     auto store_out = [&](int buf, int ci) {
+      const char* out_cur = out_next;
+      out_next += io_chunk_bytes;
       if (!SUMMARY && wave_u == NTEN && tl_on) {
-        const rsrc_t ro = io_buf(a.out, ci);
+        const rsrc_t ro = make_buf(out_cur, ci == nchunks - 1 ? io_bytes_last : io_bytes_full);
         const uint4 v = sm.out[buf][tl_row][tl_pc ^ pswz(tl_row)];
         if (VEC) {
           st_val = v;
