@@ -166,18 +166,41 @@ struct BwdKernel {
     uint4 pvv{0, 0, 0, 0};
     elem pbv[NL], pcv[NL];
     float hld[NL], hcur[NL];
+    // Chunk bases as running pointers in scalar registers, stepped down one chunk per call (the
+    // chunks are issued from the last to the first) instead of recomputed from the chunk index
+    // with 64-bit arithmetic on every wave's critical path.
+    const int64_t io_stride = int64_t(kT) * D * ES, bc_stride = int64_t(kT) * N * ES;
+    const int64_t last_row = row0 + int64_t(nchunks > 0 ? nchunks - 1 : 0) * kT;
+    const uint32_t io_bytes_full = static_cast<uint32_t>((kT * D - d0) * ES);
+    const uint32_t io_bytes_last = static_cast<uint32_t>((last_valid * D - d0) * ES);
+    const uint32_t bc_bytes_full = static_cast<uint32_t>(kT * N * ES);
+    const uint32_t bc_bytes_last = static_cast<uint32_t>(last_valid * N * ES);
+    // this wave's input tensor (waves that load none get a valid base they never read)
+    const char* t_next = static_cast<const char*>(GATE || wave_u != 2 ? tens[wave_u] : a.u) +
+                         (last_row * D + d0) * ES;
+    const char* b_next = static_cast<const char*>(a.B) + last_row * N * ES;
+    const char* c_next = static_cast<const char*>(a.C) + last_row * N * ES;
+    // this wave's gradient tile (waves that store none get a valid base they never write)
+    char* g_next = static_cast<char*>(wave_u == 0 ? a.du
+                                                  : (wave_u == 1 ? a.ddelta
+                                                                 : (GATE && wave_u == 2 ? a.dz
+                                                                                        : a.du))) +
+                   (last_row * D + d0) * ES;
+    // the stored end state of chunk c - 1 for chunk c: from chunk nchunks - 2 down
+    const float* s_next = a.ck + ((b * nchunks + (nchunks > 1 ? nchunks - 2 : 0)) * D + d0) * N;
     auto issue = [&](int c) {
-      const rsrc_t rs = c > 0 ? make_buf(a.ck + ((b * nchunks + c - 1) * D + d0) * N, st_bytes)
+      const rsrc_t rs = c > 0 ? make_buf(s_next, st_bytes)
                               : make_buf(a.h0 ? a.h0 + (b * D + d0) * N : a.ck,
                                          a.h0 ? st_bytes : 0u);
+      s_next -= D * N;
 #pragma unroll
       for (int j = 0; j < NL; ++j) hld[j] = buf_load<float>(rs, st_off[j]);
-      const int nv = nvalid_of(c);
-      const int64_t t0 = int64_t(c) * kT;
-      const uint32_t io_bytes = static_cast<uint32_t>((nv * D - d0) * ES);
+      const bool last = c == nchunks - 1;
+      const uint32_t io_bytes = last ? io_bytes_last : io_bytes_full;
+      const char* t_cur = t_next;
+      t_next -= io_stride;
       if (GATE || wave_u != 2) {  // uniform: z only with the gate
-        const rsrc_t rt = make_buf(
-            static_cast<const char*>(tens[wave_u]) + ((row0 + t0) * D + d0) * ES, io_bytes);
+        const rsrc_t rt = make_buf(t_cur, io_bytes);
         if (VEC) {
           pvv = buf_load<uint4>(rt, tl_off);
         } else {
@@ -185,9 +208,11 @@ struct BwdKernel {
           for (int e = 0; e < PIECE_E; ++e) pv[e] = buf_load<elem>(rt, tl_off + e * ES);
         }
       }
-      const uint32_t bc_bytes = static_cast<uint32_t>(nv * N * ES);
-      const rsrc_t rb = make_buf(static_cast<const char*>(a.B) + (row0 + t0) * N * ES, bc_bytes);
-      const rsrc_t rc = make_buf(static_cast<const char*>(a.C) + (row0 + t0) * N * ES, bc_bytes);
+      const uint32_t bc_bytes = last ? bc_bytes_last : bc_bytes_full;
+      const rsrc_t rb = make_buf(b_next, bc_bytes);
+      const rsrc_t rc = make_buf(c_next, bc_bytes);
+      b_next -= bc_stride;
+      c_next -= bc_stride;
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         pbv[j] = buf_load<elem>(rb, bc_off[j]);
@@ -402,11 +427,10 @@ struct BwdKernel {
       // per lane through a buffer over the chunk's valid steps: 2-byte stores from the owner
       // lanes touched 16 rows per instruction, and their issue held up the next chunk's loads.
       // The reads are done before the next barrier, after which the tiles are written again.
+      char* g_cur = g_next;
+      g_next -= io_stride;
       if (VEC && wave_u < (GATE ? 3 : 2) && tl_on) {
-        void* dst = wave_u == 0 ? a.du : (wave_u == 1 ? a.ddelta : a.dz);
-        const uint32_t io_bytes = static_cast<uint32_t>((nvalid_of(c) * D - d0) * ES);
-        const rsrc_t ro = make_buf(
-            static_cast<char*>(dst) + ((row0 + int64_t(c) * kT) * D + d0) * ES, io_bytes);
+        const rsrc_t ro = make_buf(g_cur, c == nchunks - 1 ? io_bytes_last : io_bytes_full);
         buf_store(*reinterpret_cast<const uint4*>(
                       &sm.gout[wave_u][tl_row][(tl_pc ^ pswz(tl_row)) * PIECE_E]),
                   ro, tl_off);
