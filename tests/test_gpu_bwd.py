@@ -97,10 +97,19 @@ def test_tiny_fp32_bwd(gate, skip):
 
 
 @pytest.mark.parametrize("batch,seqlen,d_inner", [(1, 1, 16), (2, 33, 17), (3, 300, 50),
-                                                  (2, 256, 64)])
+                                                  (2, 256, 64), (2, 37, 32), (1, 100, 48)])
 def test_bf16_ragged_bwd(batch, seqlen, d_inner):
+    # d_inner a multiple of 16 takes the 16-byte tile path (gradients stored from LDS tiles),
+    # with a partial last chunk when seqlen % 16 != 0; other widths the element path
     p = wl.make_prefill(wl.WORKLOADS[1], batch=batch, seqlen=seqlen, d_inner=d_inner, seed=41)
     run_bwd(p, seed=seqlen)
+
+
+@pytest.mark.parametrize("seqlen", [45, 16])
+def test_fp32_tile_path_bwd(seqlen):
+    """fp32 io on the 16-byte tile path (four pieces per tile row), ragged and whole chunks."""
+    p = wl.make_prefill(wl.WORKLOADS[0], batch=2, seqlen=seqlen, d_inner=32, seed=seqlen)
+    run_bwd(p, gate=False, seed=seqlen)
 
 
 @pytest.mark.parametrize("d_state", [1, 5, 16, 17, 24, 32, 33, 40, 64])
