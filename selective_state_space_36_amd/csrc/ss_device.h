@@ -152,12 +152,13 @@ __device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t off) {
 }
 
 // Value of `x` held by lane (k - S) mod 16 of this lane's 16-lane row, k being this lane's
-// index in the row (DPP row_ror:S).
+// index in the row (DPP row_ror:S).  Every lane has a source in its row, so bound_ctrl never
+// applies; set, it tells the compiler that no lane keeps the old value (no move to clear it).
 template <int S>
 __device__ __forceinline__ float row_ror(float x) {
   static_assert(S >= 1 && S < 16, "rotation");
   return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + S, 0xf, 0xf, false));
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + S, 0xf, 0xf, true));
 }
 
 // Make this wavefront's LDS writes visible to all of its lanes (no workgroup barrier).

@@ -159,21 +159,16 @@ struct ScanKernel {
                                           a.d_state + k
                          : nullptr;
 
-    // Front end (CONV): tap weights of a 4-wide window ending at this lane's step, split by
-    // whether the tap's step lies in this chunk (cw_cur) or the previous one (cw_prev), and the
-    // lane's x of the previous chunk (for the first chunk, x before the segment: from x itself,
-    // from the caller's history x_prev before t = 0, or 0).
-    float cw_own = 0.0f, cbias = 0.0f, cw_cur[3] = {0.0f, 0.0f, 0.0f};
-    float cw_prev[3] = {0.0f, 0.0f, 0.0f};
+    // Front end (CONV): tap weights of a 4-wide window ending at this lane's step (cw[s - 1]
+    // for the step t - s), and the lane's x of the previous chunk (for the first chunk, x before
+    // the segment: from x itself, from the caller's history x_prev before t = 0, or 0).
+    float cw_own = 0.0f, cbias = 0.0f, cw[3] = {0.0f, 0.0f, 0.0f};
     float xprev = 0.0f;
     if (CONV && chan_ok) {
       const int K = a.conv_k;
 #pragma unroll
-      for (int s = 1; s <= 3; ++s) {  // tap at step t - s
-        const float w = s < K ? a.conv_w[d * K + (K - 1 - s)] : 0.0f;
-        cw_cur[s - 1] = k >= s ? w : 0.0f;
-        cw_prev[s - 1] = k < s ? w : 0.0f;
-      }
+      for (int s = 1; s <= 3; ++s)  // tap at step t - s
+        cw[s - 1] = s < K ? a.conv_w[d * K + (K - 1 - s)] : 0.0f;
       cw_own = a.conv_w[d * K + (K - 1)];
       cbias = a.conv_b ? a.conv_b[d] : 0.0f;
       const int64_t tp = t_begin - kT + k;  // the step this lane held in the "previous chunk"
@@ -368,13 +363,13 @@ struct ScanKernel {
       const bool own_ok = chan_ok && k < nvalid_of(ci);
       if (CONV) {  // xu holds x_t here; u_t = silu(conv)
         const float xc = xu;
+        // x_{t-s} is in lane k - s of this chunk for k >= s and in lane k - s + 16 of the
+        // previous one otherwise: each source lane j offers this chunk's x if j < 16 - s, else
+        // the previous chunk's, and one row rotation by s delivers it
         float acc = fmaf(cw_own, xc, cbias);
-        acc = fmaf(cw_cur[0], row_ror<1>(xc), acc);
-        acc = fmaf(cw_prev[0], row_ror<1>(xprev), acc);
-        acc = fmaf(cw_cur[1], row_ror<2>(xc), acc);
-        acc = fmaf(cw_prev[1], row_ror<2>(xprev), acc);
-        acc = fmaf(cw_cur[2], row_ror<3>(xc), acc);
-        acc = fmaf(cw_prev[2], row_ror<3>(xprev), acc);
+        acc = fmaf(cw[0], row_ror<1>(k < 15 ? xc : xprev), acc);
+        acc = fmaf(cw[1], row_ror<2>(k < 14 ? xc : xprev), acc);
+        acc = fmaf(cw[2], row_ror<3>(k < 13 ? xc : xprev), acc);
         xprev = xc;
         xu = silu_f(acc);
       }
