@@ -45,11 +45,13 @@ struct Vec4In<BF16> {
   }
 };
 
-// Value of x held by lane J of this lane's quad (DPP quad_perm broadcast).
+// Value of x held by lane J of this lane's quad (DPP quad_perm broadcast).  Quad permutations
+// always have a source lane, so bound_ctrl never applies; set, it tells the compiler that no lane
+// keeps the old value (no move to clear it).
 template <int J>
 __device__ __forceinline__ float quad_bcast(float x) {
   return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), J * 0x55, 0xf, 0xf, false));
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), J * 0x55, 0xf, 0xf, true));
 }
 
 // Sum of x over aligned groups of G lanes (G a power of two <= 64), the result in every lane of
@@ -57,9 +59,9 @@ __device__ __forceinline__ float quad_bcast(float x) {
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
   if (G >= 2)
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, true));
   if (G >= 4)
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, true));
   for (int m = 4; m < G; m <<= 1) x += __shfl_xor(x, m, G);
   return x;
 }
