@@ -98,12 +98,14 @@ __device__ __forceinline__ float silu_f(float z) {
 }
 
 // Value of `x` held by lane SRC of this lane's 16-lane row (DPP row_newbcast).  When the result
-// feeds a multiply the compiler folds the broadcast into the multiply itself.
+// feeds a multiply the compiler folds the broadcast into the multiply itself.  Every lane has
+// its source, so bound_ctrl never applies; set, it spares the move that would clear the
+// destination of a broadcast kept as a move (one feeding a fused multiply-add).
 template <int SRC>
 __device__ __forceinline__ float row_bcast(float x) {
   static_assert(SRC >= 0 && SRC < 16, "row lane");
   return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + SRC, 0xf, 0xf, false));
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + SRC, 0xf, 0xf, true));
 }
 
 // Raw buffer resource over `bytes` bytes at `base` (stride 0).  The hardware range check makes
