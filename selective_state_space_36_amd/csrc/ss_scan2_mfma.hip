@@ -57,6 +57,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float lo_f(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float hi_f(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
+// Four bf16 of column n0 + l16 (l16 = lane % 16) in rows s0 .. s0 + 3 of a row-major LDS tile
+// of `stride` elements per row, as (rows s0, s0 + 1) and (s0 + 2, s0 + 3) pairs: an MFMA operand
+// half with K running down a column.  The gfx950 LDS transpose read (ds_read_b64_tr_b16) hands
+// lane i of each 16-lane group element i % 4 of the 8 bytes read by lanes i / 4 + 4 m of the
+// group, m = 0..3 (lane layout checked on the MI355X); so lane j reads the 4 elements of row
+// s0 + j / 4 starting at column n0 + 4 (j % 4).
+__device__ __forceinline__ uint2 tr_read4(const uint16_t* tile, int stride, int s0, int n0,
+                                          int l16) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef v4s __attribute__((address_space(3)))* lds_v4s;
+  const uint16_t* q = tile + (s0 + (l16 >> 2)) * stride + n0 + 4 * (l16 & 3);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(q)));
+}
+
 // Split (a, b) into high and low bf16 pairs: a = hi + lo to about 2^-17 relative.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16(a, b);
@@ -86,7 +100,6 @@ __device__ __forceinline__ int swz(int r, int s) {
 template <int N>
 struct alignas(16) Smem2 {
   uint16_t b[kQ][N + 8];        // B of the chunk, (s, n); later: per-wave z tiles
-  uint16_t bt[N][kTP];          // B transposed, (n, s) (swizzled)
   uint16_t c[kQ][N + 8];        // C, (t, n)
   uint16_t xt[kP][kTP];         // x transposed, (p, s) (swizzled); later: per-wave output tiles
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
@@ -259,18 +272,6 @@ scan2_mfma_kernel(Scan2Args a) {
           *reinterpret_cast<uint4*>(&sm.b[4 * rq + r][8 * nb]) = br[k][r];
           *reinterpret_cast<uint4*>(&sm.c[4 * rq + r][8 * nb]) = cr[k][r];
         }
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          uint32_t r4[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint4 q = br[k][r];
-            r4[r] = (cc >> 1) == 0 ? q.x : (cc >> 1) == 1 ? q.y : (cc >> 1) == 2 ? q.z : q.w;
-          }
-          const uint2 v = (cc & 1) ? make_uint2(highs(r4[0], r4[1]), highs(r4[2], r4[3]))
-                                   : make_uint2(lows(r4[0], r4[1]), lows(r4[2], r4[3]));
-          *reinterpret_cast<uint2*>(&sm.bt[8 * nb + cc][swz(8 * nb + cc, 4 * rq)]) = v;
-        }
       }
     }
     // ---- step sizes and decays of the chunk (every wave keeps its own copy)
@@ -377,8 +378,10 @@ scan2_mfma_kernel(Scan2Args a) {
                  wlo.w[q]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const Op bt = *reinterpret_cast<const Op*>(
-              &sm.bt[16 * nt + l16][swz(16 * nt + l16, 32 * kb + 8 * g4)]);
+          // B^T rows n = 16 nt + l16, K = s = 32 kb + 8 g4 + 0..7, read from the row-major tile
+          const uint2 k03 = tr_read4(&sm.b[0][0], N + 8, 32 * kb + 8 * g4, 16 * nt, l16);
+          const uint2 k47 = tr_read4(&sm.b[0][0], N + 8, 32 * kb + 8 * g4 + 4, 16 * nt, l16);
+          const Op bt = {{k03.x, k03.y, k47.x, k47.y}};
           S[nt] = mfma(bt, whi, S[nt]);
           S[nt] = mfma(bt, wlo, S[nt]);
         }
