@@ -17,9 +17,10 @@
 // the state in registers; wave w owns head channels 16w..16w+15 (one 16-column tile of S, X and
 // Y), so the state never leaves the wave.  The 10 causal 16x16 tiles of C B^T are shared: each
 // wave computes some of them, applies the mask and decays, and writes the split products to LDS.
-// Per chunk the workgroup stages B (row-major and transposed), C and x (transposed) in LDS from
-// 16-byte / 8-byte global loads issued one chunk ahead; each wave transposes its own z tile into
-// LDS once the B tile is free, and writes its outputs through an LDS tile as 16-byte stores.
+// Per chunk the workgroup stages B, C and x in LDS as loaded (16-byte / 8-byte global loads
+// issued one chunk ahead) and reads the operands that need a transpose with the LDS transpose
+// read; each wave transposes its own z tile into LDS once the B tile is free, and writes its
+// outputs through an LDS tile as 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,7 +35,10 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 
 constexpr int kQ = kScan2MfmaChunk;  // chunk length = wave width
 constexpr int kP = 64;               // head channels (headdim) handled by the workgroup
-constexpr int kTP = kQ + 8;          // bf16 per row of the (p, s) and (t, s) tiles
+constexpr int kTP = kQ + 8;          // bf16 per row of the (t, s) tiles
+// bf16 per row of the x tile (s, p): 160 bytes, so that the four rows a transpose read covers
+// start 8 banks apart and the read is free of bank conflicts
+constexpr int kXS = kP + 16;
 
 struct Op {  // one MFMA operand: 8 bf16 in 4 dwords
   uint32_t w[4];
@@ -85,23 +89,17 @@ __device__ __forceinline__ uint32_t highs(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-// LDS of one workgroup: 80 KB at d_state 128, so that two workgroups share a CU.  Two regions
-// are reused within a chunk: once every wave is past the C B^T tiles and the state update, the
-// B tile holds each wave's z tile (p, t); and once a wave has read its x for the epilogue, its
-// own 16 rows of the x tile hold its output tile (t, p).
-// Column of element s in row r of a transposed tile ((p, s) for x, (n, s) for B): the eight
-// 16-byte groups of a row are XOR-permuted by (r / 8) mod 8.  The transposed stores write rows
-// 4 or 8 apart from neighbouring lanes, which would otherwise land on the same LDS banks; the
-// MFMA operand reads (16 bytes of 8 consecutive s) stay contiguous and conflict-free.
-__device__ __forceinline__ int swz(int r, int s) {
-  return (((s >> 3) ^ ((r >> 3) & 7)) << 3) | (s & 7);
-}
-
+// LDS of one workgroup: 64 KB at d_state 128.  B, C and x are staged as loaded (row-major);
+// the operands that run K down a column (B^T for the state update, x for the products and the
+// epilogue) come from them by LDS transpose reads (tr_read4).  Two regions are reused within a
+// chunk: once every wave is past the C B^T tiles and the state update, the B tile holds each
+// wave's z tile (p, t); and once a wave has read its x for the epilogue, its own 16 columns of
+// the x tile hold its output tile (t, p).
 template <int N>
 struct alignas(16) Smem2 {
   uint16_t b[kQ][N + 8];        // B of the chunk, (s, n); later: per-wave z tiles
   uint16_t c[kQ][N + 8];        // C, (t, n)
-  uint16_t xt[kP][kTP];         // x transposed, (p, s) (swizzled); later: per-wave output tiles
+  uint16_t x[kQ][kXS];          // x, (s, p); later, in each wave's 16 columns, its output tile
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
   uint16_t mlo[kQ][kTP];        // low part
   float ac[kQ];                 // c_t, the chunk's cumulative log2 decay
@@ -253,15 +251,8 @@ scan2_mfma_kernel(Scan2Args a) {
     __syncthreads();  // the previous chunk's LDS reads are done
     // ---- stage the chunk in LDS
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {  // x transposed: (p, 4 consecutive steps) per write
-      const int w = cc >> 1;
-      uint32_t r4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) r4[r] = w == 0 ? xr[r].x : xr[r].y;
-      const uint2 v = (cc & 1) ? make_uint2(highs(r4[0], r4[1]), highs(r4[2], r4[3]))
-                               : make_uint2(lows(r4[0], r4[1]), lows(r4[2], r4[3]));
-      *reinterpret_cast<uint2*>(&sm.xt[4 * xp + cc][swz(4 * xp + cc, 4 * xq)]) = v;
-    }
+    for (int r = 0; r < 4; ++r)  // x as loaded: 4 channels of a step per write
+      *reinterpret_cast<uint2*>(&sm.x[4 * xq + r][4 * xp]) = xr[r];
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + 256 * k;
@@ -367,7 +358,11 @@ scan2_mfma_kernel(Scan2Args a) {
       for (int nt = 0; nt < NT; ++nt) S[nt] *= eEnd;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        xop[kb] = *reinterpret_cast<const Op*>(&sm.xt[p][swz(p, 32 * kb + 8 * g4)]);
+        {  // x of channel p, K = s = 32 kb + 8 g4 + 0..7, down a column of the x tile
+          const uint2 k03 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4, 16 * wv, l16);
+          const uint2 k47 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4 + 4, 16 * wv, l16);
+          xop[kb] = Op{{k03.x, k03.y, k47.x, k47.y}};
+        }
         const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4]);
         const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4 + 4]);
         const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -418,7 +413,7 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tb = 16 * j + 4 * g4;
-      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.xt[p][swz(p, tb)]);
+      const uint2 xv = tr_read4(&sm.x[0][0], kXS, tb, 16 * wv, l16);  // steps tb..tb+3
       xs[j][0] = lo_f(xv.x);
       xs[j][1] = hi_f(xv.x);
       xs[j][2] = lo_f(xv.y);
@@ -431,8 +426,8 @@ scan2_mfma_kernel(Scan2Args a) {
         zs[j][3] = hi_f(zv.y);
       }
     }
-    // the wave's output tile (t, 16 channels) over its own rows of the x tile, read above
-    uint16_t* ot = &sm.xt[16 * wv][0];
+    // the wave's output tile (t, 16 channels) over its own 16 columns of the x tile, read above
+    // (no other wave reads them)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tb = 16 * j + 4 * g4;
@@ -440,7 +435,7 @@ scan2_mfma_kernel(Scan2Args a) {
       for (int r = 0; r < 4; ++r) {
         float y = fmaf(Dh, xs[j][r], Y[j][r]);
         if (GATE) y *= silu_f(zs[j][r]);
-        ot[(tb + r) * 16 + l16] = BF16::from_float(y);
+        sm.x[tb + r][16 * wv + l16] = BF16::from_float(y);
       }
     }
     wave_lds_sync();
@@ -448,7 +443,7 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int t = 32 * it + (l >> 1), piece = l & 1;
-      pend[it] = *reinterpret_cast<const uint4*>(&ot[t * 16 + 8 * piece]);
+      pend[it] = *reinterpret_cast<const uint4*>(&sm.x[t][16 * wv + 8 * piece]);
     }
     lds_reads_done();  // the next chunk's staging overwrites these rows after the barrier
   }
