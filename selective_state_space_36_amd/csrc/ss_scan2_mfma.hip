@@ -97,7 +97,8 @@ __device__ __forceinline__ uint32_t highs(uint32_t a, uint32_t b) {
 // the x tile hold its output tile (t, p).
 template <int N>
 struct alignas(16) Smem2 {
-  uint16_t b[kQ][N + 8];        // B of the chunk, (s, n); later: per-wave z tiles
+  uint16_t b[kQ][N + 16];       // B of the chunk, (s, n) (rows start 8 banks apart for the
+                                // transpose reads); later: per-wave z tiles
   uint16_t c[kQ][N + 8];        // C, (t, n)
   uint16_t x[kQ][kXS];          // x, (s, p); later, in each wave's 16 columns, its output tile
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
@@ -374,8 +375,8 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           // B^T rows n = 16 nt + l16, K = s = 32 kb + 8 g4 + 0..7, read from the row-major tile
-          const uint2 k03 = tr_read4(&sm.b[0][0], N + 8, 32 * kb + 8 * g4, 16 * nt, l16);
-          const uint2 k47 = tr_read4(&sm.b[0][0], N + 8, 32 * kb + 8 * g4 + 4, 16 * nt, l16);
+          const uint2 k03 = tr_read4(&sm.b[0][0], N + 16, 32 * kb + 8 * g4, 16 * nt, l16);
+          const uint2 k47 = tr_read4(&sm.b[0][0], N + 16, 32 * kb + 8 * g4 + 4, 16 * nt, l16);
           const Op bt = {{k03.x, k03.y, k47.x, k47.y}};
           S[nt] = mfma(bt, whi, S[nt]);
           S[nt] = mfma(bt, wlo, S[nt]);
