@@ -288,8 +288,13 @@ scan2_mfma_kernel(Scan2Args a) {
 
     // ---- the causal tiles of C B^T owned by this wave -> masked, decayed, split, to LDS.  The
     // 10 tiles (s-tile ti <= t-tile tj) in the order (0,0) (0,1) (1,1) (0,2) ... (3,3) are dealt
-    // to the waves round-robin (3, 3, 2, 2 tiles).
-    for (int k = wv; k < 10; k += 4) {
+    // to the waves round-robin; waves 2 and 3, which own two, repeat tile 0 or 1 as their third,
+    // writing the same bits to the same place as its owner, so that every wave runs the same
+    // three tiles without a branch and their products and the S_in split can interleave.
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int kk = wv + 4 * i;
+      const int k = kk < 10 ? kk : kk - 10;
       const int tj = (k >= 1) + (k >= 3) + (k >= 6);
       const int ti = k - tj * (tj + 1) / 2;
       f32x4 g = {0.0f, 0.0f, 0.0f, 0.0f};
