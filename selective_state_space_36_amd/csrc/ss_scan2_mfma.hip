@@ -110,19 +110,17 @@ struct alignas(16) Smem2 {
 };
 
 // Inclusive prefix sum over the 64 lanes of the wave: Hillis-Steele steps inside each 16-lane
-// row by DPP row shifts (lanes shifted in from outside the row read 0), then the totals of the
-// rows below added from scalar lane reads.
-__device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
+// row by DPP row shifts (lanes shifted in from outside the row read 0), then the row totals
+// carried across rows by the GFX9 row broadcasts: lane 15 of rows 0 and 2 added to rows 1 and 3,
+// then lane 31 (the total of rows 0 and 1) to rows 2 and 3 (rows left out of a row mask add 0).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
-  const int row = lane >> 4;
-  const float below = row == 0 ? 0.0f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
-  return x + below;
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
+  return x;
 }
 
 template <int N, bool GATE>
@@ -234,7 +232,7 @@ scan2_mfma_kernel(Scan2Args a) {
 
   // Output tile of the previous chunk, stored at the start of the next one: stores issued right
   // after the next chunk's loads would make the wait for those loads wait for the stores too.
-  uint4 pend[2];
+  uint4 pend[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   rsrc_t pend_r = make_buf(og, 0);
   auto store_pending = [&]() {
 #pragma unroll
@@ -266,24 +264,27 @@ scan2_mfma_kernel(Scan2Args a) {
         }
       }
     }
+    // the chunk's dt, before the loads below replace it with the next chunk's
+    const uint16_t dcur = dtr;
+    // the output stores and the next chunk's loads go out first: they are what the chunk's
+    // arithmetic hides
+    store_pending();  // on the first chunk pend_r covers no bytes: nothing is written
+    fetch(t0 + kQ);  // past the end on the last chunk: no memory is touched
+    fetch_z(t0);
     // ---- step sizes and decays of the chunk (every wave keeps its own copy)
     float acEnd;
     {
-      const float s = BF16::widen(dtr) + bias;
+      const float s = BF16::widen(dcur) + bias;
       float dv = a.softplus ? softplus_f(s) : s;
       dv = l < nv ? dv : 0.0f;
-      const float c = wave_prefix_sum(dv * A2, l);
+      const float c = wave_prefix_sum(dv * A2);
       acEnd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-      if (wv == 0) {  // every wave has the same values; one copy in LDS
-        sm.ac[l] = c;
-        sm.dtv[l] = dv;
-        sm.e[l] = exp2_hw(c);
-        sm.w[l] = exp2_hw(acEnd - c) * dv;
-      }
+      // every wave has the same values and writes them: identical bits to the same place
+      sm.ac[l] = c;
+      sm.dtv[l] = dv;
+      sm.e[l] = exp2_hw(c);
+      sm.w[l] = exp2_hw(acEnd - c) * dv;
     }
-    if (ch > 0) store_pending();
-    fetch(t0 + kQ);  // past the end on the last chunk: no memory is touched
-    fetch_z(t0);
     __syncthreads();  // staged tiles visible
 
     // ---- the causal tiles of C B^T owned by this wave -> masked, decayed, split, to LDS.  The
