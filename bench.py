@@ -48,6 +48,16 @@ SLOTS_PER_UPDATE = 6          # 1 exp (2 slots) + dt*A, (dt*u)*B, state FMA, C.h
 SLOTS_PER_ELEMENT_GATED = 19  # bias add, softplus (exp 2 + log 4 + add), dt*u, skip FMA,
                               # silu (exp 2 + add + rcp 4 + mul), gate mul
 SLOTS_PER_ELEMENT_PLAIN = 10
+# Backward, per update: the recomputed step (dt*A, exp 2, (dt*u)*B, state FMA, C.h for the
+# gate's y: 6) and the adjoint step (lambda: 2; the ddt term lambda (a e h_prev + B u): 5; the
+# du term: 1; dB and dC terms with their channel sums: 4; the dA term: 2): 20.  Per element:
+# softplus 8, its derivative (exp 2 + add + rcp 4) 7, silu and its derivative 13, du, ddelta,
+# dD, dbias 5, dt*u 1, widening and narrowing 7: 41.  The forward pass storing the chunk-end
+# states (without saved states): per update 5 (no C.h), per element 11 (softplus, dt*u, widening).
+BWD_SLOTS_PER_UPDATE = 20
+BWD_SLOTS_PER_ELEMENT = 41
+STATES_SLOTS_PER_UPDATE = 5
+STATES_SLOTS_PER_ELEMENT = 11
 SECTIONS = ("cold", "decode", "multihead", "variants", "workloads", "parity", "cpu")
 
 
@@ -157,6 +167,28 @@ def decode_bytes_per_step(w) -> int:
 def valu_slots(w) -> float:
     return w.elements * (w.d_state * SLOTS_PER_UPDATE +
                          (SLOTS_PER_ELEMENT_GATED if w.gate else SLOTS_PER_ELEMENT_PLAIN))
+
+
+def bwd_valu_slots(w, states_given=False) -> float:
+    """VALU slots of the backward: per update the recomputed step and the adjoint step, per
+    element the element-wise derivatives; without saved states the forward pass that stores the
+    chunk-end states adds its own step and softplus."""
+    per = w.elements * (w.d_state * BWD_SLOTS_PER_UPDATE + BWD_SLOTS_PER_ELEMENT)
+    if not states_given:
+        per += w.elements * (w.d_state * STATES_SLOTS_PER_UPDATE + STATES_SLOTS_PER_ELEMENT)
+    return per
+
+
+def exp_stats(w, ms_kernel: float) -> dict:
+    """Transcendentals of the prefill: one v_exp_f32 per update; per element one exp and one log
+    for softplus and, with the gate, one exp and one rcp for silu.  v_exp_f32 issues at half the
+    VALU slot rate."""
+    exps = w.d_state + 1 + (1 if w.gate else 0)
+    per_s = w.elements * exps / (ms_kernel * 1e-3)
+    return {"per_update": 1, "exp_per_element": exps,
+            "other_transcendentals_per_element": 1 + (1 if w.gate else 0),
+            "exp_per_s": round(per_s, 1), "exp_peak_per_s": PEAK_VALU_SLOTS / 2,
+            "exp_frac": round(per_s / (PEAK_VALU_SLOTS / 2), 4)}
 
 
 def dev(x, torch, np):
@@ -298,10 +330,18 @@ def bench_variants(args, torch, np, ops, pf, stream):
     nb = backward_bytes(w)
     ck = 2 * w.batch * ((w.seqlen + 15) // 16) * w.d_inner * w.d_state * 4
     part = 2 * w.batch * ((w.seqlen + 15) // 16) * ((w.d_inner + 15) // 16) * 16 * 16 * 2 * 4
+    sl, sl_g = bwd_valu_slots(w), bwd_valu_slots(w, states_given=True)
     res["backward"] = {
         "us_per_call": round(ms_bwd * 1e3, 2),
         "elements_per_s": round(w.elements / (ms_bwd * 1e-3), 1),
-        "roofline": {"bound": "hbm", "algorithmic_bytes": nb,
+        "roofline": {"bound": "alu", "valu_slots": sl,
+                     "achieved": round(sl / (ms_bwd * 1e-3) / 1e12, 3),
+                     "peak": round(PEAK_VALU_SLOTS / 1e12, 3), "unit": "T VALU-slot/s",
+                     "frac": round(sl / (ms_bwd * 1e-3) / PEAK_VALU_SLOTS, 4),
+                     "note": "slots per update: 20 for the recomputed and adjoint steps, 5 for "
+                             "the forward pass storing the chunk-end states; per element 41 + "
+                             "11 (exp 2 slots, log and rcp 4)"},
+        "hbm": {"bound": "hbm", "algorithmic_bytes": nb,
                      "achieved": round(nb / (ms_bwd * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(nb / (ms_bwd * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                      "traffic": measured_traffic("mamba2.8b-backward"),
@@ -315,6 +355,7 @@ def bench_variants(args, torch, np, ops, pf, stream):
                 "recomputing each chunk), all input gradients",
         "with_saved_states": {
             "forward_us": round(ms_fs * 1e3, 2), "backward_us": round(ms_bs * 1e3, 2),
+            "backward_valu_frac": round(sl_g / (ms_bs * 1e-3) / PEAK_VALU_SLOTS, 4),
             "note": "ss_scan_fwd_states (the forward also writing the chunk-end states) then "
                     "ss_scan_bwd with SS_FLAG_STATES_GIVEN (no forward pass of its own)"}}
     log(f"backward {ms_bwd * 1e3:.1f} us, training path {ms_fs * 1e3:.1f} + {ms_bs * 1e3:.1f} us")
@@ -714,15 +755,7 @@ def main():
                      "kernel": "scan_kernel (prefill output pass)",
                      "kernel_us": line["kernel_us"]},
         "hbm": line["hbm"],
-        # transcendentals: one v_exp_f32 per update, and per element 2 for softplus (exp, log)
-        # and 2 for silu (exp, rcp); v_exp_f32 issues at half the VALU rate
-        "exp": {"per_update": 1,
-                "per_element": w.d_state + (4 if w.gate else 2),
-                "exp_per_s": round(w.elements * (w.d_state + (2 if w.gate else 1))
-                                   / ms_kernel, 1),
-                "exp_peak_per_s": PEAK_VALU_SLOTS / 2,
-                "exp_frac": round(w.elements * (w.d_state + (2 if w.gate else 1))
-                                  / ms_kernel / (PEAK_VALU_SLOTS / 2), 4)},
+        "exp": exp_stats(w, ms_kernel),
         "order": "cold_start (the kernel's first W + K launches on an idle GPU), then "
                  "clock_settle (untimed launches until the per-launch time stops falling), then "
                  "the W untimed and K timed steps; the other sections run after them",

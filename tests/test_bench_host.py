@@ -39,6 +39,24 @@ def test_valu_slot_count():
     assert bench.PEAK_VALU_SLOTS == pytest.approx(39.3216e12)
 
 
+def test_exp_rate_is_per_second():
+    w = wl.WORKLOADS[2]
+    st = bench.exp_stats(w, 0.35)  # 350 us per call
+    # 16 update exps + softplus + silu per element
+    assert st["exp_per_element"] == 18
+    assert st["exp_per_s"] == pytest.approx(w.elements * 18 / 350e-6, rel=1e-6)
+    assert st["exp_frac"] == pytest.approx(w.elements * 18 / 350e-6 / (bench.PEAK_VALU_SLOTS / 2),
+                                           abs=1e-4)
+    assert 0.1 < st["exp_frac"] < 1.0
+
+
+def test_backward_valu_slot_count():
+    w = wl.WORKLOADS[2]
+    given = bench.bwd_valu_slots(w, states_given=True)
+    assert given == w.elements * (16 * 20 + 41)
+    assert bench.bwd_valu_slots(w) == given + w.elements * (16 * 5 + 11)
+
+
 def _fake_timer(monkeypatch, per_launch_ms):
     """bench.timed replaced by one that hands out the given per-launch times in order."""
     it = iter(per_launch_ms)
