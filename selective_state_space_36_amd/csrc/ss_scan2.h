@@ -27,6 +27,10 @@ struct Scan2Args {
   int64_t n_pblk;        // ceil(headdim / kScan2PBlock)
   int32_t d_state;
   int32_t softplus;
+  // chunked kernel only (set by its launcher): the first n_whole (batch row, head) pairs run
+  // whole, each of the others in q_split time pieces
+  int64_t n_whole;
+  int32_t q_split;
 };
 
 hipError_t launch_scan2(const Scan2Args& a, bool bf16, hipStream_t stream);

@@ -14,8 +14,9 @@
 // bits, and each takes two products, so the result keeps close to fp32 accuracy.
 //
 // Work layout: one workgroup (4 waves) per (batch row, head) walks the chunks in order and keeps
-// the state in registers; wave w owns head channels 16w..16w+15 (one 16-column tile of S, X and
-// Y), so the state never leaves the wave.  The 10 causal 16x16 tiles of C B^T are shared: each
+// the state in registers (with more pairs than CUs but fewer than two per CU, some pairs are cut
+// into time pieces instead; see launch_n); wave w owns head channels 16w..16w+15 (one 16-column
+// tile of S, X and Y), so the state never leaves the wave.  The 10 causal 16x16 tiles of C B^T are shared: each
 // wave computes some of them, applies the mask and decays, and writes the split products to LDS.
 // Per chunk the workgroup stages B, C and x in LDS as loaded (16-byte / 8-byte global loads
 // issued one chunk ahead) and reads the operands that need a transpose with the LDS transpose
@@ -136,7 +137,21 @@ scan2_mfma_kernel(Scan2Args a) {
   const int tid = threadIdx.x;
   const int wv = tid >> 6, l = tid & 63, l16 = l & 15, g4 = l >> 4;
   const int64_t H = a.nheads, L = a.seqlen, G = a.ngroups;
-  const int64_t bh = xcd_remap(blockIdx.x, gridDim.x);
+  // Workgroups 0 .. n_whole - 1 take whole (batch row, head) pairs; the rest take the remaining
+  // pairs in q_split pieces each, piece k the chunks [k nchunks / q, (k + 1) nchunks / q), after
+  // running the state alone over the chunks before it (see launch_n).
+  const int64_t nchunks = (L + kQ - 1) / kQ;
+  int64_t bh, cbeg = 0, cend = nchunks;
+  if (int64_t(blockIdx.x) < a.n_whole) {
+    bh = xcd_remap(blockIdx.x, a.n_whole);
+  } else {
+    const int64_t np = int64_t(gridDim.x) - a.n_whole;
+    const int64_t pc = xcd_remap(blockIdx.x - a.n_whole, np);
+    const int64_t k = pc % a.q_split;
+    bh = a.n_whole + pc / a.q_split;
+    cbeg = k * nchunks / a.q_split;
+    cend = (k + 1) * nchunks / a.q_split;
+  }
   const int64_t b = bh / H, h = bh - b * H;
   const int64_t grp = h / (H / G);
   const float A2 = a.A[h] * kLog2e;
@@ -177,7 +192,7 @@ scan2_mfma_kernel(Scan2Args a) {
   uint16_t dtr;
   // Loads of the chunk at t0 into registers.  Each tile is a buffer over the chunk's valid steps
   // (none past the sequence end: then every load returns 0 and touches no memory).
-  auto fetch = [&](int64_t t0) {
+  auto fetch = [&](int64_t t0, bool with_c) {
     const int64_t left = L - t0;
     const uint32_t nv = static_cast<uint32_t>(left <= 0 ? 0 : left < kQ ? left : kQ);
     auto bytes = [nv](uint32_t row, uint32_t last) { return nv ? (nv - 1) * row + last : 0u; };
@@ -193,7 +208,7 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         br[k][r] = buf_load<uint4>(rb, boff[k][r]);
-        cr[k][r] = buf_load<uint4>(rc, boff[k][r]);
+        if (with_c) cr[k][r] = buf_load<uint4>(rc, boff[k][r]);
       }
   };
 
@@ -242,9 +257,80 @@ scan2_mfma_kernel(Scan2Args a) {
     }
   };
 
-  const int64_t nchunks = (L + kQ - 1) / kQ;
-  fetch(0);
-  for (int64_t ch = 0; ch < nchunks; ++ch) {
+  // S_out = e^{c_end} S_in + B^T (w o X) for the chunk staged in LDS; leaves this wave's x
+  // operand (K = steps) in xop for the chunk's M X
+  auto update_state = [&](Op (&xop)[2], float acEnd) {
+    const float eEnd = exp2_hw(acEnd);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) S[nt] *= eEnd;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      {  // x of channel p, K = s = 32 kb + 8 g4 + 0..7, down a column of the x tile
+        const uint2 k03 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4, 16 * wv, l16);
+        const uint2 k47 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4 + 4, 16 * wv, l16);
+        xop[kb] = Op{{k03.x, k03.y, k47.x, k47.y}};
+      }
+      const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4 + 4]);
+      const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      Op whi, wlo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        split2(lo_f(xop[kb].w[q]) * ww[2 * q], hi_f(xop[kb].w[q]) * ww[2 * q + 1], whi.w[q],
+               wlo.w[q]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        // B^T rows n = 16 nt + l16, K = s = 32 kb + 8 g4 + 0..7, read from the row-major tile
+        const uint2 k03 = tr_read4(&sm.b[0][0], N + 16, 32 * kb + 8 * g4, 16 * nt, l16);
+        const uint2 k47 = tr_read4(&sm.b[0][0], N + 16, 32 * kb + 8 * g4 + 4, 16 * nt, l16);
+        const Op bt = {{k03.x, k03.y, k47.x, k47.y}};
+        S[nt] = mfma(bt, whi, S[nt]);
+        S[nt] = mfma(bt, wlo, S[nt]);
+      }
+    }
+  };
+
+  // ---- the state alone over the chunks before this workgroup's range: staging of B and x,
+  // the decays and the state update (no outputs)
+  auto decays = [&](uint16_t dcur, int nv, float& acEnd) {
+    const float s = BF16::widen(dcur) + bias;
+    float dv = a.softplus ? softplus_f(s) : s;
+    dv = l < nv ? dv : 0.0f;
+    const float c = wave_prefix_sum(dv * A2);
+    acEnd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+    // every wave has the same values and writes them: identical bits to the same place
+    sm.ac[l] = c;
+    sm.dtv[l] = dv;
+    sm.e[l] = exp2_hw(c);
+    sm.w[l] = exp2_hw(acEnd - c) * dv;
+  };
+  fetch(0, cbeg == 0);
+  for (int64_t ch = 0; ch < cbeg; ++ch) {
+    const int64_t t0 = ch * kQ;
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<uint2*>(&sm.x[4 * xq + r][4 * xp]) = xr[r];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = tid + 256 * k;
+      if (UNITS % 256 == 0 || u < UNITS) {
+        const int rq = u / (N / 8), nb = u % (N / 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<uint4*>(&sm.b[4 * rq + r][8 * nb]) = br[k][r];
+      }
+    }
+    const uint16_t dcur = dtr;
+    fetch(t0 + kQ, ch + 1 == cbeg);  // the range's first chunk needs C as well
+    float acEnd;
+    decays(dcur, static_cast<int>(L - t0 < kQ ? L - t0 : kQ), acEnd);
+    __syncthreads();  // staged tiles visible
+    Op xop[2];
+    update_state(xop, acEnd);
+  }
+
+  for (int64_t ch = cbeg; ch < cend; ++ch) {
     const int64_t t0 = ch * kQ;
     const int nv = static_cast<int>(L - t0 < kQ ? L - t0 : kQ);
     __syncthreads();  // the previous chunk's LDS reads are done
@@ -269,22 +355,11 @@ scan2_mfma_kernel(Scan2Args a) {
     // the output stores and the next chunk's loads go out first: they are what the chunk's
     // arithmetic hides
     store_pending();  // on the first chunk pend_r covers no bytes: nothing is written
-    fetch(t0 + kQ);  // past the end on the last chunk: no memory is touched
+    fetch(t0 + kQ, true);  // past the end on the last chunk: no memory is touched
     fetch_z(t0);
     // ---- step sizes and decays of the chunk (every wave keeps its own copy)
     float acEnd;
-    {
-      const float s = BF16::widen(dcur) + bias;
-      float dv = a.softplus ? softplus_f(s) : s;
-      dv = l < nv ? dv : 0.0f;
-      const float c = wave_prefix_sum(dv * A2);
-      acEnd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-      // every wave has the same values and writes them: identical bits to the same place
-      sm.ac[l] = c;
-      sm.dtv[l] = dv;
-      sm.e[l] = exp2_hw(c);
-      sm.w[l] = exp2_hw(acEnd - c) * dv;
-    }
+    decays(dcur, nv, acEnd);
     __syncthreads();  // staged tiles visible
 
     // ---- the causal tiles of C B^T owned by this wave -> masked, decayed, split, to LDS.  The
@@ -359,36 +434,7 @@ scan2_mfma_kernel(Scan2Args a) {
 
     // ---- S_out = e^{c_end} S_in + B^T (w o X)
     Op xop[2];
-    {
-      const float eEnd = exp2_hw(acEnd);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S[nt] *= eEnd;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        {  // x of channel p, K = s = 32 kb + 8 g4 + 0..7, down a column of the x tile
-          const uint2 k03 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4, 16 * wv, l16);
-          const uint2 k47 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4 + 4, 16 * wv, l16);
-          xop[kb] = Op{{k03.x, k03.y, k47.x, k47.y}};
-        }
-        const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4 + 4]);
-        const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        Op whi, wlo;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          split2(lo_f(xop[kb].w[q]) * ww[2 * q], hi_f(xop[kb].w[q]) * ww[2 * q + 1], whi.w[q],
-                 wlo.w[q]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          // B^T rows n = 16 nt + l16, K = s = 32 kb + 8 g4 + 0..7, read from the row-major tile
-          const uint2 k03 = tr_read4(&sm.b[0][0], N + 16, 32 * kb + 8 * g4, 16 * nt, l16);
-          const uint2 k47 = tr_read4(&sm.b[0][0], N + 16, 32 * kb + 8 * g4 + 4, 16 * nt, l16);
-          const Op bt = {{k03.x, k03.y, k47.x, k47.y}};
-          S[nt] = mfma(bt, whi, S[nt]);
-          S[nt] = mfma(bt, wlo, S[nt]);
-        }
-      }
-    }
+    update_state(xop, acEnd);
     __syncthreads();  // every wave's tiles of C B^T are in LDS
 
     // ---- Y += M X over the causal blocks, then skip, gate and store
@@ -454,9 +500,9 @@ scan2_mfma_kernel(Scan2Args a) {
     }
     lds_reads_done();  // the next chunk's staging overwrites these rows after the barrier
   }
-  if (nchunks > 0) store_pending();
+  if (cend > cbeg) store_pending();
 
-  if (a.h_last) {
+  if (a.h_last && cend == nchunks) {
     float* hl = a.h_last + bh * N * kP;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -465,9 +511,35 @@ scan2_mfma_kernel(Scan2Args a) {
   }
 }
 
+// Each (batch row, head) pair is a sequential walk over the chunks, two of which share a CU.
+// With more pairs than CUs but fewer than two per CU, the CUs given two whole pairs would set the
+// time while the others idle half of it.  So when the pairs number between one and two per CU,
+// one pair per CU runs whole and each remaining pair is cut into q time pieces (q = CUs / extra
+// pairs, at most 4), one workgroup each: every CU then holds one whole pair and one piece.  A
+// piece first runs the state alone (B, x and the decays; no C, no outputs) over the chunks before
+// its own, about a third of a chunk's work each.
 template <int N>
-void launch_n(const Scan2Args& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(a.batch * a.nheads));
+void launch_n(const Scan2Args& a0, hipStream_t stream) {
+  Scan2Args a = a0;
+  const int64_t pairs = a.batch * a.nheads;
+  const int64_t nchunks = (a.seqlen + kQ - 1) / kQ;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  a.n_whole = pairs;
+  a.q_split = 1;
+  if (cus > 0 && pairs > cus && pairs < 2 * int64_t(cus)) {
+    const int64_t extra = pairs - cus;
+    int64_t q = cus / extra;
+    if (q > 4) q = 4;
+    if (q > nchunks) q = nchunks;
+    if (q >= 2) {
+      a.n_whole = cus;
+      a.q_split = static_cast<int32_t>(q);
+    }
+  }
+  const dim3 grid(static_cast<unsigned>(a.n_whole + (pairs - a.n_whole) * a.q_split));
   if (a.z)
     hipLaunchKernelGGL((scan2_mfma_kernel<N, true>), grid, dim3(256), 0, stream, a);
   else

@@ -135,6 +135,32 @@ def test_empty_and_invalid_scan2():
     assert torch.equal(hl, h0)
 
 
+@pytest.mark.parametrize("batch,extra_heads,seqlen,groups", [(2, "half+eighth+1", 200, 7),
+                                                              (1, "quarter", 256, 1)])
+def test_pairs_between_one_and_two_per_cu(batch, extra_heads, seqlen, groups):
+    """More (batch row, head) pairs than CUs but fewer than two per CU: one pair per CU runs
+    whole and the others in time pieces, each starting from the state it runs alone over the
+    chunks before its own (three uneven pieces with a ragged last chunk, or four of one chunk).
+    Every head against the oracle, from an initial state."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if extra_heads == "quarter":
+        nheads = (cus + cus // 4) // batch
+    else:
+        nheads = (cus // 2 + cus // 8 + 1) // groups * groups
+    assert cus < batch * nheads < 2 * cus
+    p = wl.make_multihead(wl.MULTIHEAD, batch=batch, seqlen=seqlen, nheads=nheads,
+                          ngroups=groups, seed=seqlen + nheads)
+    h0 = 0.5 * np.random.default_rng(3).standard_normal(
+        (batch, nheads, p["B"].shape[-1], p["x"].shape[-1])).astype(np.float32)
+    g, gh, r, rh = run2(p, h0=h0)
+    e = Errors("split multi-head out", TOL["bf16"])
+    e.add(g, r)
+    e.report()
+    e = Errors("split multi-head h_last", TOL["f32"])
+    e.add(gh, rh)
+    e.report()
+
+
 def test_full_size_scan2_every_head():
     """The Mamba-2-shaped layer (batch 4, L 4096, 80 heads x 64, 128 states, bf16) in the launch
     configuration the benchmark uses, every head and channel checked."""
