@@ -496,7 +496,9 @@ def bench_multihead(args, torch, np, ops, wl, stream):
     A, D, db = (dev(p[k], torch, np) for k in ("A", "D", "dt_bias"))
     out = torch.empty_like(x)
     run = lambda: ops.scan2_fwd(x, dt, A, B, C, D=D, z=z, dt_bias=db, out=out, stream=stream)
-    _, per = timed(torch, stream, run, 20, max(3, args.steps // 4))
+    # untimed launches until the per-launch time stops falling (the clock ramp), then timed ones
+    settle = clock_settle(torch, stream, run)
+    _, per = timed(torch, stream, run, 5, max(10, args.steps))
     ms = sum(per) / len(per)
     log(f"multi-head scan {ms * 1e3:.1f} us per call")
     import oracle
@@ -524,6 +526,7 @@ def bench_multihead(args, torch, np, ops, wl, stream):
                 ngroups=w.ngroups, d_state=N, us_per_call=round(ms * 1e3, 2),
                 elements_per_s=round(w.elements / sec, 1),
                 kernel="scan2_mfma_kernel (chunked dual form, 64-step chunks, bf16 MFMA)",
+                clock_settle_launches=10 * len(settle), timed_launches=len(per),
                 roofline=dict(bound="hbm", achieved=round(nbytes / sec / 1e9, 1),
                               peak=PEAK_HBM_GBPS, unit="GB/s",
                               frac=round(nbytes / sec / 1e9 / PEAK_HBM_GBPS, 4),
