@@ -501,6 +501,14 @@ def bench_multihead(args, torch, np, ops, wl, stream):
     _, per = timed(torch, stream, run, 5, max(10, args.steps))
     ms = sum(per) / len(per)
     log(f"multi-head scan {ms * 1e3:.1f} us per call")
+    # the same layer at batch 1 (80 pairs on 256 CUs: each pair cut into time pieces)
+    x1, dt1, z1, B1, C1 = (t[:1].contiguous() for t in (x, dt, z, B, C))
+    out1 = torch.empty_like(x1)
+    run1 = lambda: ops.scan2_fwd(x1, dt1, A, B1, C1, D=D, z=z1, dt_bias=db, out=out1,
+                                 stream=stream)
+    _, per1 = timed(torch, stream, run1, 5, max(10, args.steps))
+    ms1 = sum(per1) / len(per1)
+    log(f"multi-head scan, batch 1: {ms1 * 1e3:.1f} us per call")
     import oracle
     heads = np.array([0, w.nheads - 1])
     sub = lambda a: np.ascontiguousarray(a[:, :, heads])
@@ -527,6 +535,7 @@ def bench_multihead(args, torch, np, ops, wl, stream):
                 elements_per_s=round(w.elements / sec, 1),
                 kernel="scan2_mfma_kernel (chunked dual form, 64-step chunks, bf16 MFMA)",
                 clock_settle_launches=10 * len(settle), timed_launches=len(per),
+                batch1_us_per_call=round(ms1 * 1e3, 2),
                 roofline=dict(bound="hbm", achieved=round(nbytes / sec / 1e9, 1),
                               peak=PEAK_HBM_GBPS, unit="GB/s",
                               frac=round(nbytes / sec / 1e9 / PEAK_HBM_GBPS, 4),

@@ -515,9 +515,10 @@ scan2_mfma_kernel(Scan2Args a) {
 // With more pairs than CUs but fewer than two per CU, the CUs given two whole pairs would set the
 // time while the others idle half of it.  So when the pairs number between one and two per CU,
 // one pair per CU runs whole and each remaining pair is cut into q time pieces (q = CUs / extra
-// pairs, at most 4), one workgroup each: every CU then holds one whole pair and one piece.  A
-// piece first runs the state alone (B, x and the decays; no C, no outputs) over the chunks before
-// its own, about a third of a chunk's work each.
+// pairs, at most 4), one workgroup each: every CU then holds one whole pair and one piece.  With
+// at most one pair per two CUs, every pair is cut (q = CUs / pairs, at most 4).  A piece first
+// runs the state alone (B, x and the decays; no C, no outputs) over the chunks before its own,
+// about a third of a chunk's work each.
 template <int N>
 void launch_n(const Scan2Args& a0, hipStream_t stream) {
   Scan2Args a = a0;
@@ -529,7 +530,16 @@ void launch_n(const Scan2Args& a0, hipStream_t stream) {
     cus = 0;
   a.n_whole = pairs;
   a.q_split = 1;
-  if (cus > 0 && pairs > cus && pairs < 2 * int64_t(cus)) {
+  if (cus > 0 && pairs > 0 && pairs <= cus / 2) {
+    // at most half the CUs would be busy: cut every pair into q pieces
+    int64_t q = cus / pairs;
+    if (q > 4) q = 4;
+    if (q > nchunks) q = nchunks;
+    if (q >= 2) {
+      a.n_whole = 0;
+      a.q_split = static_cast<int32_t>(q);
+    }
+  } else if (cus > 0 && pairs > cus && pairs < 2 * int64_t(cus)) {
     const int64_t extra = pairs - cus;
     int64_t q = cus / extra;
     if (q > 4) q = 4;
