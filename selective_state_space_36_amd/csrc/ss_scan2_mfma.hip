@@ -516,9 +516,9 @@ scan2_mfma_kernel(Scan2Args a) {
 // time while the others idle half of it.  So when the pairs number between one and two per CU,
 // one pair per CU runs whole and each remaining pair is cut into q time pieces (q = CUs / extra
 // pairs, at most 4), one workgroup each: every CU then holds one whole pair and one piece.  With
-// at most one pair per two CUs, every pair is cut (q = CUs / pairs, at most 4).  A piece first
-// runs the state alone (B, x and the decays; no C, no outputs) over the chunks before its own,
-// about a third of a chunk's work each.
+// at most one pair per CU, every pair is cut (below).  A piece first runs the state alone (B, x
+// and the decays; no C, no outputs) over the chunks before its own, about a third of a chunk's
+// work each.
 template <int N>
 void launch_n(const Scan2Args& a0, hipStream_t stream) {
   Scan2Args a = a0;
@@ -530,14 +530,24 @@ void launch_n(const Scan2Args& a0, hipStream_t stream) {
     cus = 0;
   a.n_whole = pairs;
   a.q_split = 1;
-  if (cus > 0 && pairs > 0 && pairs <= cus / 2) {
-    // at most half the CUs would be busy: cut every pair into q pieces
-    int64_t q = cus / pairs;
-    if (q > 4) q = 4;
-    if (q > nchunks) q = nchunks;
-    if (q >= 2) {
+  if (cus > 0 && pairs > 0 && pairs <= cus) {
+    // At most one pair per CU: cut every pair into the q pieces (1..4) that minimise the longest
+    // piece's work, (q - 1) / q r + 1 / q of a whole pair with r = 0.35 the relative cost of a
+    // state-only chunk, times 1.3 when the pieces outnumber the CUs and two share one (measured on
+    // the 80-head layer at batch 1, 2 and 3: q = 3, 3, 2); never more pieces than two per CU.
+    int64_t best_q = 1;
+    double best = 1.0;
+    for (int64_t q = 2; q <= 4 && q <= nchunks; ++q) {
+      if (pairs * q > 2 * int64_t(cus)) break;
+      const double work = (double(q - 1) / q * 0.35 + 1.0 / q) * (pairs * q > cus ? 1.3 : 1.0);
+      if (work < best) {
+        best = work;
+        best_q = q;
+      }
+    }
+    if (best_q >= 2) {
       a.n_whole = 0;
-      a.q_split = static_cast<int32_t>(q);
+      a.q_split = static_cast<int32_t>(best_q);
     }
   } else if (cus > 0 && pairs > cus && pairs < 2 * int64_t(cus)) {
     const int64_t extra = pairs - cus;
