@@ -10,6 +10,7 @@ namespace ss {
 constexpr int kScan2Threads = 256;
 constexpr int kScan2Chunk = 16;
 constexpr int kScan2PBlock = 16;  // head channels per workgroup
+constexpr int kScan2MaxPieces = 4;  // time pieces a (batch row, head) pair is cut into, at most
 
 struct Scan2Args {
   const void* x;         // (batch, seqlen, nheads, headdim) io dtype
@@ -28,9 +29,11 @@ struct Scan2Args {
   int32_t d_state;
   int32_t softplus;
   // chunked kernel only (set by its launcher): the first n_whole (batch row, head) pairs run
-  // whole, each of the others in q_split time pieces
+  // whole, each of the others in q_split time pieces, piece k over the chunks
+  // [piece_beg[k], piece_beg[k + 1])
   int64_t n_whole;
   int32_t q_split;
+  int32_t piece_beg[kScan2MaxPieces + 1];
 };
 
 hipError_t launch_scan2(const Scan2Args& a, bool bf16, hipStream_t stream);

@@ -20,8 +20,9 @@
 // wave computes some of them, applies the mask and decays, and writes the split products to LDS.
 // Per chunk the workgroup stages B, C and x in LDS as loaded (16-byte / 8-byte global loads
 // issued one chunk ahead) and reads the operands that need a transpose with the LDS transpose
-// read; each wave transposes its own z tile into LDS once the B tile is free, and writes its
-// outputs through an LDS tile as 16-byte stores.
+// read.  The outputs are formed transposed (rows: channels, columns: steps), which leaves each
+// lane 4 adjacent channels of one step, as x, z and out lie in memory: z is loaded straight into
+// that layout, and the outputs leave through an LDS tile as 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,24 +83,14 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
   lo = pack_bf16(a - lo_f(hi), b - hi_f(hi));
 }
 
-// The low 16 bits of a and of b, as (a_lo, b_lo); the high halves, as (a_hi, b_hi).
-__device__ __forceinline__ uint32_t lows(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t highs(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
 // LDS of one workgroup: 64 KB at d_state 128.  B, C and x are staged as loaded (row-major);
 // the operands that run K down a column (B^T for the state update, x for the products and the
-// epilogue) come from them by LDS transpose reads (tr_read4).  Two regions are reused within a
-// chunk: once every wave is past the C B^T tiles and the state update, the B tile holds each
-// wave's z tile (p, t); and once a wave has read its x for the epilogue, its own 16 columns of
-// the x tile hold its output tile (t, p).
+// epilogue) come from them by LDS transpose reads (tr_read4).  Once a wave has read its x for
+// the epilogue, its own 16 columns of the x tile hold its output tile (t, p).
 template <int N>
 struct alignas(16) Smem2 {
   uint16_t b[kQ][N + 16];       // B of the chunk, (s, n) (rows start 8 banks apart for the
-                                // transpose reads); later: per-wave z tiles
+                                // transpose reads)
   uint16_t c[kQ][N + 8];        // C, (t, n)
   uint16_t x[kQ][kXS];          // x, (s, p); later, in each wave's 16 columns, its output tile
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
@@ -138,7 +129,7 @@ scan2_mfma_kernel(Scan2Args a) {
   const int wv = tid >> 6, l = tid & 63, l16 = l & 15, g4 = l >> 4;
   const int64_t H = a.nheads, L = a.seqlen, G = a.ngroups;
   // Workgroups 0 .. n_whole - 1 take whole (batch row, head) pairs; the rest take the remaining
-  // pairs in q_split pieces each, piece k the chunks [k nchunks / q, (k + 1) nchunks / q), after
+  // pairs in q_split pieces each, piece k the chunks [piece_beg[k], piece_beg[k + 1]), after
   // running the state alone over the chunks before it (see launch_n).
   const int64_t nchunks = (L + kQ - 1) / kQ;
   int64_t bh, cbeg = 0, cend = nchunks;
@@ -147,10 +138,10 @@ scan2_mfma_kernel(Scan2Args a) {
   } else {
     const int64_t np = int64_t(gridDim.x) - a.n_whole;
     const int64_t pc = xcd_remap(blockIdx.x - a.n_whole, np);
-    const int64_t k = pc % a.q_split;
+    const int k = static_cast<int>(pc % a.q_split);
     bh = a.n_whole + pc / a.q_split;
-    cbeg = k * nchunks / a.q_split;
-    cend = (k + 1) * nchunks / a.q_split;
+    cbeg = a.piece_beg[k];
+    cend = a.piece_beg[k + 1];
   }
   const int64_t b = bh / H, h = bh - b * H;
   const int64_t grp = h / (H / G);
@@ -175,8 +166,9 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     xoff[r] = (4 * xq + r) * xrow + 8 * xp;
-    // z: each wave loads its own 16 channels, 4 steps x 4 channels per lane
-    zoff[r] = (4 * (l >> 2) + r) * xrow + (16 * wv + 4 * (l & 3)) * 2;
+    // z: each wave loads its own 16 channels in the layout of its output tile: for step
+    // 16 r + l16, the 4 channels 16 wv + 4 g4 .. + 3
+    zoff[r] = (16 * r + l16) * xrow + (16 * wv + 4 * g4) * 2;
   }
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
@@ -399,7 +391,9 @@ scan2_mfma_kernel(Scan2Args a) {
       *reinterpret_cast<uint2*>(&sm.mlo[t][s0]) = make_uint2(l0w, l1w);
     }
 
-    // ---- Y = diag(e^c) C S_in, with S_in split into bf16 high and low parts
+    // ---- Y = diag(e^c) C S_in, with S_in split into bf16 high and low parts.  Y is formed
+    // transposed, Y[j][r] = Y(t = 16 j + l16, p = 16 wv + 4 g4 + r): each lane then holds 4
+    // adjacent channels of one step, the layout of x, z and out in memory.
     f32x4 Y[4];
     {
       Op shi[KB], slo[KB];
@@ -420,14 +414,15 @@ scan2_mfma_kernel(Scan2Args a) {
           const uint2 c1 =
               *reinterpret_cast<const uint2*>(&sm.c[16 * j + l16][32 * kb + 16 + 4 * g4]);
           const Op ca = {{c0.x, c0.y, c1.x, c1.y}};
-          acc = mfma(ca, shi[kb], acc);
-          acc = mfma(ca, slo[kb], acc);
+          // S_in^T C^T: rows are channels, columns steps
+          acc = mfma(shi[kb], ca, acc);
+          acc = mfma(slo[kb], ca, acc);
         }
-        const float4 ev = *reinterpret_cast<const float4*>(&sm.e[16 * j + 4 * g4]);
-        acc[0] *= ev.x;
-        acc[1] *= ev.y;
-        acc[2] *= ev.z;
-        acc[3] *= ev.w;
+        const float ev = sm.e[16 * j + l16];
+        acc[0] *= ev;
+        acc[1] *= ev;
+        acc[2] *= ev;
+        acc[3] *= ev;
         Y[j] = acc;
       }
     }
@@ -437,59 +432,34 @@ scan2_mfma_kernel(Scan2Args a) {
     update_state(xop, acEnd);
     __syncthreads();  // every wave's tiles of C B^T are in LDS
 
-    // ---- Y += M X over the causal blocks, then skip, gate and store
+    // ---- Y += M X over the causal blocks (as X^T M^T), then skip, gate and store
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int kb = 0; kb <= (j >> 1); ++kb) {
         const Op mh = *reinterpret_cast<const Op*>(&sm.mhi[16 * j + l16][32 * kb + 8 * g4]);
         const Op ml = *reinterpret_cast<const Op*>(&sm.mlo[16 * j + l16][32 * kb + 8 * g4]);
-        Y[j] = mfma(mh, xop[kb], Y[j]);
-        Y[j] = mfma(ml, xop[kb], Y[j]);
+        Y[j] = mfma(xop[kb], mh, Y[j]);
+        Y[j] = mfma(xop[kb], ml, Y[j]);
       }
     }
-    // this wave's z tile, transposed to (p, t), in the B tile (free after the barrier above)
-    uint16_t(*zt)[kTP] = reinterpret_cast<uint16_t(*)[kTP]>(&sm.b[0][0]) + 16 * wv;
-    if (GATE) {
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        uint32_t r4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) r4[r] = (cc >> 1) == 0 ? zr[r].x : zr[r].y;
-        const uint2 v = (cc & 1) ? make_uint2(highs(r4[0], r4[1]), highs(r4[2], r4[3]))
-                                 : make_uint2(lows(r4[0], r4[1]), lows(r4[2], r4[3]));
-        *reinterpret_cast<uint2*>(&zt[4 * (l & 3) + cc][4 * (l >> 2)]) = v;
-      }
-      wave_lds_sync();
-    }
-    float xs[4][4], zs[4][4];
+    // skip, gate and the output tile: lane (l16, g4) owns step 16 j + l16, channels
+    // 16 wv + 4 g4 .. + 3 of the x tile, reads its x there and writes its outputs in their place
+    // (no other wave reads this wave's 16 columns)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int tb = 16 * j + 4 * g4;
-      const uint2 xv = tr_read4(&sm.x[0][0], kXS, tb, 16 * wv, l16);  // steps tb..tb+3
-      xs[j][0] = lo_f(xv.x);
-      xs[j][1] = hi_f(xv.x);
-      xs[j][2] = lo_f(xv.y);
-      xs[j][3] = hi_f(xv.y);
+      uint2* cell = reinterpret_cast<uint2*>(&sm.x[16 * j + l16][16 * wv + 4 * g4]);
+      const uint2 xv = *cell;
+      const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = fmaf(Dh, xs[r], Y[j][r]);
       if (GATE) {
-        const uint2 zv = *reinterpret_cast<const uint2*>(&zt[l16][tb]);
-        zs[j][0] = lo_f(zv.x);
-        zs[j][1] = hi_f(zv.x);
-        zs[j][2] = lo_f(zv.y);
-        zs[j][3] = hi_f(zv.y);
-      }
-    }
-    // the wave's output tile (t, 16 channels) over its own 16 columns of the x tile, read above
-    // (no other wave reads them)
+        const float zs[4] = {lo_f(zr[j].x), hi_f(zr[j].x), lo_f(zr[j].y), hi_f(zr[j].y)};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tb = 16 * j + 4 * g4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float y = fmaf(Dh, xs[j][r], Y[j][r]);
-        if (GATE) y *= silu_f(zs[j][r]);
-        sm.x[tb + r][16 * wv + l16] = BF16::from_float(y);
+        for (int r = 0; r < 4; ++r) y[r] *= silu_f(zs[r]);
       }
+      *cell = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
     }
     wave_lds_sync();
     pend_r = make_buf(og + t0 * H * kP, static_cast<uint32_t>(nv - 1) * xrow + kP * 2);
@@ -511,6 +481,39 @@ scan2_mfma_kernel(Scan2Args a) {
   }
 }
 
+// Relative cost of a chunk run for the state alone (B, x, decays and the state update) against a
+// full chunk, measured on the 80-head layer at batch 1 (three pieces per pair: 142.5 us against
+// 266 us whole).
+constexpr double kPreludeCost = 0.30;
+// Time of a chunk when two workgroups share a CU, against one alone (same layer, batch 4).
+constexpr double kSharedSlowdown = 1.385;
+
+// Boundaries of q pieces over n chunks with equal work: piece k runs P_k earlier chunks for the
+// state alone and its own l_k chunks, l_k + r P_k equal for all k, so l_{k+1} = (1 - r) l_k and
+// the pieces shrink geometrically.  Rounded to whole chunks, every piece at least one chunk.
+void piece_bounds(int64_t n, int q, int32_t* beg) {
+  double sum = 0.0, len = 1.0;
+  for (int k = 0; k < q; ++k, len *= 1.0 - kPreludeCost) sum += len;
+  double acc = 0.0;
+  len = 1.0;
+  beg[0] = 0;
+  for (int k = 1; k < q; ++k, len *= 1.0 - kPreludeCost) {
+    acc += len;
+    int64_t b = static_cast<int64_t>(double(n) * acc / sum + 0.5);
+    if (b < beg[k - 1] + 1) b = beg[k - 1] + 1;
+    if (b > n - (q - k)) b = n - (q - k);
+    beg[k] = static_cast<int32_t>(b);
+  }
+  beg[q] = static_cast<int32_t>(n);
+}
+
+// Longest piece's work, in whole-pair units, when a pair is cut into q equal-work pieces.
+double piece_work(int q) {
+  double sum = 0.0, len = 1.0;
+  for (int k = 0; k < q; ++k, len *= 1.0 - kPreludeCost) sum += len;
+  return 1.0 / sum;
+}
+
 // Each (batch row, head) pair is a sequential walk over the chunks, two of which share a CU.
 // With more pairs than CUs but fewer than two per CU, the CUs given two whole pairs would set the
 // time while the others idle half of it.  So when the pairs number between one and two per CU,
@@ -518,7 +521,7 @@ scan2_mfma_kernel(Scan2Args a) {
 // pairs, at most 4), one workgroup each: every CU then holds one whole pair and one piece.  With
 // at most one pair per CU, every pair is cut (below).  A piece first runs the state alone (B, x
 // and the decays; no C, no outputs) over the chunks before its own, about a third of a chunk's
-// work each.
+// work each, so the pieces are cut to equal work rather than equal length.
 template <int N>
 void launch_n(const Scan2Args& a0, hipStream_t stream) {
   Scan2Args a = a0;
@@ -530,34 +533,30 @@ void launch_n(const Scan2Args& a0, hipStream_t stream) {
     cus = 0;
   a.n_whole = pairs;
   a.q_split = 1;
+  int64_t q = 1;
   if (cus > 0 && pairs > 0 && pairs <= cus) {
     // At most one pair per CU: cut every pair into the q pieces (1..4) that minimise the longest
-    // piece's work, (q - 1) / q r + 1 / q of a whole pair with r = 0.35 the relative cost of a
-    // state-only chunk, times 1.3 when the pieces outnumber the CUs and two share one (measured on
-    // the 80-head layer at batch 1, 2 and 3: q = 3, 3, 2); never more pieces than two per CU.
-    int64_t best_q = 1;
+    // piece's work, slowed by kSharedSlowdown when the pieces outnumber the CUs and two share
+    // one; never more pieces than two per CU.
     double best = 1.0;
-    for (int64_t q = 2; q <= 4 && q <= nchunks; ++q) {
-      if (pairs * q > 2 * int64_t(cus)) break;
-      const double work = (double(q - 1) / q * 0.35 + 1.0 / q) * (pairs * q > cus ? 1.3 : 1.0);
+    for (int64_t qq = 2; qq <= kScan2MaxPieces && qq <= nchunks; ++qq) {
+      if (pairs * qq > 2 * int64_t(cus)) break;
+      const double work = piece_work(static_cast<int>(qq)) *
+                          (pairs * qq > cus ? kSharedSlowdown : 1.0);
       if (work < best) {
         best = work;
-        best_q = q;
+        q = qq;
       }
     }
-    if (best_q >= 2) {
-      a.n_whole = 0;
-      a.q_split = static_cast<int32_t>(best_q);
-    }
   } else if (cus > 0 && pairs > cus && pairs < 2 * int64_t(cus)) {
-    const int64_t extra = pairs - cus;
-    int64_t q = cus / extra;
-    if (q > 4) q = 4;
+    q = cus / (pairs - cus);
+    if (q > kScan2MaxPieces) q = kScan2MaxPieces;
     if (q > nchunks) q = nchunks;
-    if (q >= 2) {
-      a.n_whole = cus;
-      a.q_split = static_cast<int32_t>(q);
-    }
+  }
+  if (q >= 2 && nchunks < (int64_t(1) << 31)) {
+    a.q_split = static_cast<int32_t>(q);
+    a.n_whole = pairs <= cus ? 0 : cus;
+    piece_bounds(nchunks, static_cast<int>(q), a.piece_beg);
   }
   const dim3 grid(static_cast<unsigned>(a.n_whole + (pairs - a.n_whole) * a.q_split));
   if (a.z)
