@@ -22,7 +22,7 @@
 // issued one chunk ahead) and reads the operands that need a transpose with the LDS transpose
 // read.  The outputs are formed transposed (rows: channels, columns: steps), which leaves each
 // lane 4 adjacent channels of one step, as x, z and out lie in memory: z is loaded straight into
-// that layout, and the outputs leave through an LDS tile as 16-byte stores.
+// that layout, and the outputs leave straight from registers as 8-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,6 +60,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const b2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
   return __builtin_bit_cast(uint32_t, v);
 }
+// 8-byte store through a buffer resource (dropped past its range).
+__device__ __forceinline__ void store8(uint2 v, rsrc_t r, uint32_t off) {
+  using v2u = __attribute__((ext_vector_type(2))) unsigned int;
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v), r, off, 0, 0);
+}
 __device__ __forceinline__ float lo_f(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float hi_f(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -85,14 +90,13 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
 
 // LDS of one workgroup: 64 KB at d_state 128.  B, C and x are staged as loaded (row-major);
 // the operands that run K down a column (B^T for the state update, x for the products and the
-// epilogue) come from them by LDS transpose reads (tr_read4).  Once a wave has read its x for
-// the epilogue, its own 16 columns of the x tile hold its output tile (t, p).
+// epilogue) come from them by LDS transpose reads (tr_read4).
 template <int N>
 struct alignas(16) Smem2 {
   uint16_t b[kQ][N + 16];       // B of the chunk, (s, n) (rows start 8 banks apart for the
                                 // transpose reads)
   uint16_t c[kQ][N + 8];        // C, (t, n)
-  uint16_t x[kQ][kXS];          // x, (s, p); later, in each wave's 16 columns, its output tile
+  uint16_t x[kQ][kXS];          // x, (s, p)
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
   uint16_t mlo[kQ][kTP];        // low part
   float ac[kQ];                 // c_t, the chunk's cumulative log2 decay
@@ -166,7 +170,7 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     xoff[r] = (4 * xq + r) * xrow + 8 * xp;
-    // z: each wave loads its own 16 channels in the layout of its output tile: for step
+    // z: each wave loads its own 16 channels in the layout of its outputs: for step
     // 16 r + l16, the 4 channels 16 wv + 4 g4 .. + 3
     zoff[r] = (16 * r + l16) * xrow + (16 * wv + 4 * g4) * 2;
   }
@@ -237,16 +241,15 @@ scan2_mfma_kernel(Scan2Args a) {
     }
   };
 
-  // Output tile of the previous chunk, stored at the start of the next one: stores issued right
+  // Outputs of the previous chunk, stored at the start of the next one: stores issued right
   // after the next chunk's loads would make the wait for those loads wait for the stores too.
-  uint4 pend[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  // Each lane stores its 4 channels of each of its 4 steps (8 bytes, at z's offsets); the four
+  // waves fill the 128 bytes of a step's row.
+  uint2 pend[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
   rsrc_t pend_r = make_buf(og, 0);
   auto store_pending = [&]() {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int t = 32 * it + (l >> 1), piece = l & 1;
-      buf_store(pend[it], pend_r, t * xrow + (16 * wv + 8 * piece) * 2);
-    }
+    for (int j = 0; j < 4; ++j) store8(pend[j], pend_r, zoff[j]);
   };
 
   // S_out = e^{c_end} S_in + B^T (w o X) for the chunk staged in LDS; leaves this wave's x
@@ -443,13 +446,11 @@ scan2_mfma_kernel(Scan2Args a) {
         Y[j] = mfma(xop[kb], ml, Y[j]);
       }
     }
-    // skip, gate and the output tile: lane (l16, g4) owns step 16 j + l16, channels
-    // 16 wv + 4 g4 .. + 3 of the x tile, reads its x there and writes its outputs in their place
-    // (no other wave reads this wave's 16 columns)
+    // skip and gate: lane (l16, g4) owns step 16 j + l16, channels 16 wv + 4 g4 .. + 3, and reads
+    // its x in the x tile
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint2* cell = reinterpret_cast<uint2*>(&sm.x[16 * j + l16][16 * wv + 4 * g4]);
-      const uint2 xv = *cell;
+      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.x[16 * j + l16][16 * wv + 4 * g4]);
       const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
       float y[4];
 #pragma unroll
@@ -459,16 +460,10 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[r] *= silu_f(zs[r]);
       }
-      *cell = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+      pend[j] = make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
     }
-    wave_lds_sync();
     pend_r = make_buf(og + t0 * H * kP, static_cast<uint32_t>(nv - 1) * xrow + kP * 2);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int t = 32 * it + (l >> 1), piece = l & 1;
-      pend[it] = *reinterpret_cast<const uint4*>(&sm.x[t][16 * wv + 8 * piece]);
-    }
-    lds_reads_done();  // the next chunk's staging overwrites these rows after the barrier
+    lds_reads_done();  // the next chunk's staging overwrites the x tile after the barrier
   }
   if (cend > cbeg) store_pending();
 
