@@ -95,7 +95,9 @@ template <int N>
 struct alignas(16) Smem2 {
   uint16_t b[kQ][N + 16];       // B of the chunk, (s, n) (rows start 8 banks apart for the
                                 // transpose reads)
-  uint16_t c[kQ][N + 8];        // C, (t, n)
+  uint16_t c[kQ][N + 4];        // C, (t, n): rows 2 banks apart, so the 8-byte operand reads
+                                // of S_in^T C^T (16 rows, one per lane) are free of conflicts;
+                                // staged and read by the C B^T tiles 8 bytes at a time
   uint16_t x[kQ][kXS];          // x, (s, p)
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
   uint16_t mlo[kQ][kTP];        // low part
@@ -341,7 +343,11 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           *reinterpret_cast<uint4*>(&sm.b[4 * rq + r][8 * nb]) = br[k][r];
-          *reinterpret_cast<uint4*>(&sm.c[4 * rq + r][8 * nb]) = cr[k][r];
+          {
+            uint2* cp = reinterpret_cast<uint2*>(&sm.c[4 * rq + r][8 * nb]);
+            cp[0] = make_uint2(cr[k][r].x, cr[k][r].y);
+            cp[1] = make_uint2(cr[k][r].z, cr[k][r].w);
+          }
         }
       }
     }
@@ -372,7 +378,9 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const Op ab = *reinterpret_cast<const Op*>(&sm.b[16 * ti + l16][32 * kb + 8 * g4]);
-        const Op bc = *reinterpret_cast<const Op*>(&sm.c[16 * tj + l16][32 * kb + 8 * g4]);
+        const uint2* cq = reinterpret_cast<const uint2*>(&sm.c[16 * tj + l16][32 * kb + 8 * g4]);
+        const uint2 bc0 = cq[0], bc1 = cq[1];
+        const Op bc = {{bc0.x, bc0.y, bc1.x, bc1.y}};
         g = mfma(ab, bc, g);  // g[r] = sum_n B[s, n] C[t, n], s = 16 ti + 4 g4 + r, t = 16 tj + l16
       }
       const int t = 16 * tj + l16, s0 = 16 * ti + 4 * g4;
