@@ -577,12 +577,12 @@ __global__ void __launch_bounds__(256) reduce_bc_kernel(BwdArgs a, int64_t nchun
     const float2* src = reinterpret_cast<const float2*>(a.part_bc) + bc * a.n_cblk * blk + idx;
     float sb = 0.0f, sc = 0.0f;
     int64_t cb = 0;
-    for (; cb + 8 <= a.n_cblk; cb += 8) {  // eight loads in flight, added in order
-      float2 v[8];
+    for (; cb + 16 <= a.n_cblk; cb += 16) {  // sixteen loads in flight, added in order
+      float2 v[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = src[(cb + j) * blk];
+      for (int j = 0; j < 16; ++j) v[j] = src[(cb + j) * blk];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 16; ++j) {
         sb += v[j].x;
         sc += v[j].y;
       }
