@@ -161,10 +161,13 @@ def test_pairs_between_one_and_two_per_cu(batch, extra_heads, seqlen, groups):
     e.report()
 
 
-def test_full_size_scan2_every_head():
-    """The Mamba-2-shaped layer (batch 4, L 4096, 80 heads x 64, 128 states, bf16) in the launch
-    configuration the benchmark uses, every head and channel checked."""
-    p = wl.make_multihead(wl.MULTIHEAD)
+@pytest.mark.parametrize("batch", [4, 1, 3])
+def test_full_size_scan2_every_head(batch):
+    """The Mamba-2-shaped layer (L 4096, 80 heads x 64, 128 states, bf16), every head and channel
+    checked: batch 4 in the launch configuration the benchmark times (one whole pair per CU and
+    the other pairs in four time pieces of equal work), batch 1 and 3 with every pair cut (three
+    pieces, one per CU; two pieces, two sharing a CU)."""
+    p = wl.make_multihead(wl.MULTIHEAD, batch=batch)
     g, gh, r, rh = run2(p)
     e = Errors("multi-head out", TOL["bf16"])
     e.add(g, r)
