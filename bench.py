@@ -282,7 +282,11 @@ def bench_variants(args, torch, np, ops, pf, stream):
     res = {}
     zsteps = max(3, args.steps // 4)
     zoh_out = torch.empty_like(g["u"])
-    ms, per = timed(torch, stream, lambda: pf.step(out=zoh_out, zoh_exact=True), 20, zsteps)
+    # each kernel is timed after a clock settle of its own (the sections before it leave the
+    # chip at a different clock)
+    run_zoh = lambda: pf.step(out=zoh_out, zoh_exact=True)
+    settles = {"zoh_exact": 10 * len(clock_settle(torch, stream, run_zoh))}
+    ms, per = timed(torch, stream, run_zoh, 20, zsteps)
     res["zoh_exact"] = {"kernel_us": round(sum(per) / len(per) * 1e3, 2),
                         "elements_per_s": round(w.elements / (ms * 1e-3), 1),
                         "note": "same layer with the exact zero-order-hold input term; its "
@@ -297,6 +301,7 @@ def bench_variants(args, torch, np, ops, pf, stream):
     run_conv = lambda: ops.scan_fwd_conv(g["u"], cw, cbias, g["delta"], g["A"], g["B"], g["C"],
                                          D=g["D"], z=g["z"], delta_bias=g["delta_bias"],
                                          out=conv_out, workspace=pf.ws, stream=stream)
+    settles["conv_front_end"] = 10 * len(clock_settle(torch, stream, run_conv))
     ms, per = timed(torch, stream, run_conv, 20, zsteps)
     res["conv_front_end"] = {"kernel_us": round(sum(per) / len(per) * 1e3, 2),
                              "elements_per_s": round(w.elements / (ms * 1e-3), 1),
@@ -314,6 +319,7 @@ def bench_variants(args, torch, np, ops, pf, stream):
                                    z=g["z"], delta_bias=g["delta_bias"], workspace=ws_b,
                                    stream=stream)
     bsteps = max(3, args.steps // 10)
+    settles["backward"] = 10 * len(clock_settle(torch, stream, run_bwd))
     ms_bwd, _ = timed(torch, stream, run_bwd, 5, bsteps, per_launch=False)
     del ws_b
     ws_t, st_buf = ops.bwd_workspace(w.batch, w.seqlen, w.d_inner, w.d_state, g["u"].dtype)
@@ -324,7 +330,9 @@ def bench_variants(args, torch, np, ops, pf, stream):
     bwd_s = lambda: ops.scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dout, D=g["D"],
                                  z=g["z"], delta_bias=g["delta_bias"], workspace=ws_t,
                                  states_given=True, stream=stream)
+    settles["fwd_states"] = 10 * len(clock_settle(torch, stream, fwd_s))
     ms_fs, _ = timed(torch, stream, fwd_s, 5, bsteps, per_launch=False)
+    settles["bwd_states_given"] = 10 * len(clock_settle(torch, stream, bwd_s))
     ms_bs, _ = timed(torch, stream, bwd_s, 5, bsteps, per_launch=False)
     del ws_t, st_buf, st_out
     nb = backward_bytes(w)
@@ -359,6 +367,7 @@ def bench_variants(args, torch, np, ops, pf, stream):
             "note": "ss_scan_fwd_states (the forward also writing the chunk-end states) then "
                     "ss_scan_bwd with SS_FLAG_STATES_GIVEN (no forward pass of its own)"}}
     log(f"backward {ms_bwd * 1e3:.1f} us, training path {ms_fs * 1e3:.1f} + {ms_bs * 1e3:.1f} us")
+    res["variants_clock_settle_launches"] = settles
     return res
 
 
@@ -719,9 +728,12 @@ def main():
                 continue
             pf = Prefill(wl.WORKLOADS[idx], torch, np, ops, wl, stream)
             k = args.steps if idx != 3 else max(5, args.steps // 10)
+            # its own clock settle: the sections before leave the chip at a lower clock
+            settle_w = clock_settle(torch, stream, pf.step)
             ms, per = timed(torch, stream, pf.step, 5, k)
             others[idx] = pf
             extra.setdefault("workloads", {})[pf.w.name] = pf.line(ms, per)
+            extra["workloads"][pf.w.name]["clock_settle_launches"] = len(settle_w) * 10
             extra["workloads"][pf.w.name]["kernels"] = (
                 "summary pass + output pass (time split)" if pf.ws_bytes else "output pass")
             log(f"{pf.w.name}: {extra['workloads'][pf.w.name]['us_per_call']} us per call")
