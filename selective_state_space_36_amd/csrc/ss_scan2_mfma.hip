@@ -74,6 +74,17 @@ __device__ __forceinline__ float hi_f(uint32_t v) { return __uint_as_float(v & 0
 // lane i of each 16-lane group element i % 4 of the 8 bytes read by lanes i / 4 + 4 m of the
 // group, m = 0..3 (lane layout checked on the MI355X); so lane j reads the 4 elements of row
 // s0 + j / 4 starting at column n0 + 4 (j % 4).
+// The same from a tile whose rows hold their 8-byte units (4 bf16) XOR-permuted by `key`
+// (uniform over rows s0 .. s0 + 3): lane j reads logical columns n0 + 4 (j % 4) .. + 3 where the
+// permutation put them.
+__device__ __forceinline__ uint2 tr_read4_swz(const uint16_t* tile, int stride, int s0, int n0,
+                                              int l16, int key) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef v4s __attribute__((address_space(3)))* lds_v4s;
+  const int unit = (n0 >> 2) + (l16 & 3);
+  const uint16_t* q = tile + (s0 + (l16 >> 2)) * stride + 4 * (unit ^ key);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(q)));
+}
 __device__ __forceinline__ uint2 tr_read4(const uint16_t* tile, int stride, int s0, int n0,
                                           int l16) {
   typedef short v4s __attribute__((ext_vector_type(4)));
@@ -98,7 +109,9 @@ struct alignas(16) Smem2 {
   uint16_t c[kQ][N + 4];        // C, (t, n): rows 2 banks apart, so the 8-byte operand reads
                                 // of S_in^T C^T (16 rows, one per lane) are free of conflicts;
                                 // staged and read by the C B^T tiles 8 bytes at a time
-  uint16_t x[kQ][kXS];          // x, (s, p)
+  uint16_t x[kQ][kXS];          // x, (s, p); in row s the 8-byte units (4 channels) are
+                                // XOR-permuted by (s / 4) mod 4, so that the epilogue's 8-byte
+                                // reads of 16 rows are free of bank conflicts
   uint16_t mhi[kQ][kTP];        // masked, decayed and dt-scaled C B^T, (t, s): high part
   uint16_t mlo[kQ][kTP];        // low part
   float ac[kQ];                 // c_t, the chunk's cumulative log2 decay
@@ -263,8 +276,10 @@ scan2_mfma_kernel(Scan2Args a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       {  // x of channel p, K = s = 32 kb + 8 g4 + 0..7, down a column of the x tile
-        const uint2 k03 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4, 16 * wv, l16);
-        const uint2 k47 = tr_read4(&sm.x[0][0], kXS, 32 * kb + 8 * g4 + 4, 16 * wv, l16);
+        const uint2 k03 =
+            tr_read4_swz(&sm.x[0][0], kXS, 32 * kb + 8 * g4, 16 * wv, l16, (2 * g4) & 3);
+        const uint2 k47 =
+            tr_read4_swz(&sm.x[0][0], kXS, 32 * kb + 8 * g4 + 4, 16 * wv, l16, (2 * g4 + 1) & 3);
         xop[kb] = Op{{k03.x, k03.y, k47.x, k47.y}};
       }
       const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[32 * kb + 8 * g4]);
@@ -307,7 +322,7 @@ scan2_mfma_kernel(Scan2Args a) {
     __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<uint2*>(&sm.x[4 * xq + r][4 * xp]) = xr[r];
+      *reinterpret_cast<uint2*>(&sm.x[4 * xq + r][4 * (xp ^ (xq & 3))]) = xr[r];
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + 256 * k;
@@ -334,7 +349,7 @@ scan2_mfma_kernel(Scan2Args a) {
     // ---- stage the chunk in LDS
 #pragma unroll
     for (int r = 0; r < 4; ++r)  // x as loaded: 4 channels of a step per write
-      *reinterpret_cast<uint2*>(&sm.x[4 * xq + r][4 * xp]) = xr[r];
+      *reinterpret_cast<uint2*>(&sm.x[4 * xq + r][4 * (xp ^ (xq & 3))]) = xr[r];
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + 256 * k;
@@ -458,7 +473,8 @@ scan2_mfma_kernel(Scan2Args a) {
     // its x in the x tile
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint2 xv = *reinterpret_cast<const uint2*>(&sm.x[16 * j + l16][16 * wv + 4 * g4]);
+      const uint2 xv = *reinterpret_cast<const uint2*>(
+          &sm.x[16 * j + l16][4 * ((4 * wv + g4) ^ ((l16 >> 2) & 3))]);
       const float xs[4] = {lo_f(xv.x), hi_f(xv.x), lo_f(xv.y), hi_f(xv.y)};
       float y[4];
 #pragma unroll
